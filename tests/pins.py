@@ -1,0 +1,440 @@
+"""Checks that pin the CPU oracle to facts fixed outside it.
+
+Each ``check_*`` function raises ``AssertionError`` when the oracle disagrees
+with what the pages print, with a closed form, with a library routine, or
+with brute force.  ``test_oracle_pins.py`` runs them all on the oracle as it
+is; ``test_oracle_mutations.py`` plants plausible mistakes in the oracle and
+shows each one trips at least one check.
+
+Sources: [KG] kgptalkie.com "Day 28: PagedAttention"; [ZQ] zenaique.com
+"How does PagedAttention enable prefix sharing across requests and what data
+structure makes it cheap?".
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+from oracle import blocks as oblocks
+from oracle import paged
+from paged_kv_cache_252_amd import inputs
+from tests.helpers import oracle_args, oracle_decode, poison_tails, to_np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_workload(seed, num_seqs=3, len_lo=0, len_hi=23, hq=4, hkv=2, d=16, bs=4,
+                   dtype="f32", num_blocks=40):
+    return inputs.paged_random("rand", num_seqs, len_lo, len_hi, hq, hkv, head_dim=d,
+                               block_size=bs, dtype=dtype, num_blocks=num_blocks, seed=seed)
+
+
+# ----------------------------------------------------------------------------
+# translation: [KG] "Follow One Token Address", "Split the Cache Into Fixed Blocks"
+# ----------------------------------------------------------------------------
+
+def check_worked_address():
+    g = _golden("worked_address.json")
+    pr = g["printed"]
+    lb, off, phys, _ = paged.translate(pr["position"], g["block_table"], g["block_size"])
+    assert (lb, off, phys) == (pr["logical_block"], pr["offset"], pr["physical_block"])
+    for case in g["positions"]:
+        got = paged.translate(case["position"], g["block_table"], g["block_size"])
+        assert got == (case["logical_block"], case["offset"], case["physical_block"],
+                       case["slot"]), (case, got)
+    # the same through the batched slot mapping
+    pos = [c["position"] for c in g["positions"]] + [-1]
+    slots = paged.slot_mapping([g["block_table"]], [0] * len(pos), pos, g["block_size"])
+    assert slots.tolist() == [c["slot"] for c in g["positions"]] + [-1]
+
+
+def check_fixed_blocks_16():
+    g = _golden("fixed_blocks_16.json")
+    for case in g["positions"]:
+        got = paged.translate(case["position"], g["block_table"], g["block_size"])
+        assert got == (case["logical_block"], case["offset"], case["physical_block"],
+                       case["slot"]), (case, got)
+
+
+# ----------------------------------------------------------------------------
+# growth and tail waste: [KG] "Growth Needs Only Another Free Block"
+# ----------------------------------------------------------------------------
+
+def check_block_growth():
+    g = _golden("block_growth.json")
+    bs = g["block_size"]
+    pr = g["printed"]
+    assert paged.blocks_needed(pr["tokens"], bs) == pr["blocks"]
+    assert paged.blocks_needed(pr["tokens"], bs) * bs == pr["slots"]
+    assert paged.tail_waste(pr["tokens"], bs) == pr["unused_slots"]
+    pool = oblocks.BlockPool(16, bs)
+    seq = pool.new_sequence()
+    allocs = [pool.append(seq).allocated is not None for _ in range(pr["tokens"])]
+    assert sum(allocs) == pr["blocks"] and len(seq.table) == pr["blocks"]
+    assert pool.num_free == 16 - pr["blocks"]
+    for token in pr["tokens_needing_no_new_block"]:
+        assert seq.length + 1 == token
+        assert pool.append(seq).allocated is None
+    assert seq.length + 1 == pr["token_needing_fourth_block"]
+    first_three = list(seq.table)
+    assert pool.append(seq).allocated is not None
+    assert len(seq.table) == 4
+    assert seq.table[:3] == first_three          # the history never moves when it grows
+
+
+def check_tail_waste_bound(max_bs=64, max_len=600):
+    """Brute force: grow a request one token at a time and count empty slots."""
+    for bs in range(1, max_bs + 1):
+        capacity = 0
+        for n in range(1, max_len + 1):
+            while capacity < n:         # one more block only when the last is full
+                capacity += bs
+            waste = capacity - n
+            assert paged.blocks_needed(n, bs) * bs == capacity
+            assert paged.tail_waste(n, bs) == waste
+            assert waste <= bs - 1
+            assert (waste == bs - 1) == (n % bs == 1 % bs)
+
+
+# ----------------------------------------------------------------------------
+# in-block layout: the library contract, checked against its scalar formulas
+# ----------------------------------------------------------------------------
+
+def check_layout_contract():
+    for dtype, x in (("f32", 4), ("bf16", 8)):
+        nb, hkv, bs, d = 3, 2, 4, 16
+        n = hkv * bs * d
+        # element id = its (block, head, offset, dim) coordinates packed as an int
+        k_pool = np.zeros((nb, n), dtype=np.int64)
+        v_pool = np.zeros((nb, n), dtype=np.int64)
+        for b in range(nb):
+            for h in range(hkv):
+                for t in range(bs):
+                    for e in range(d):
+                        code = ((b * 10 + h) * 100 + t) * 1000 + e
+                        ki = (((b * hkv + h) * (d // x) + e // x) * bs + t) * x + e % x
+                        vi = ((b * hkv + h) * d + e) * bs + t
+                        k_pool.reshape(-1)[ki] = code
+                        v_pool.reshape(-1)[vi] = code
+        for b in range(nb):
+            k_rows, v_rows = paged.block_tokens(k_pool, v_pool, b, hkv, bs, d, dtype)
+            for t in range(bs):
+                for h in range(hkv):
+                    want = [((b * 10 + h) * 100 + t) * 1000 + e for e in range(d)]
+                    assert k_rows[t, h].tolist() == want
+                    assert v_rows[t, h].tolist() == want
+
+
+# ----------------------------------------------------------------------------
+# attention: closed forms, a library routine, invariances
+# ----------------------------------------------------------------------------
+
+def check_sdpa_identity_tables(seed=11):
+    """Identity placement = contiguous attention, checked against torch SDPA."""
+    rng = np.random.default_rng(seed)
+    for (hq, hkv, d, bs, L) in ((2, 2, 16, 4, 9), (8, 2, 16, 4, 23), (4, 1, 32, 16, 40),
+                                (6, 3, 8, 1, 5)):
+        nb = paged.blocks_needed(L, bs)
+        x = 4
+        k = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        q = rng.standard_normal((1, hq, d)).astype(np.float32)
+        # build a pool in the documented layout by the scalar formulas
+        kp = np.full(nb * hkv * bs * d, np.nan, dtype=np.float32)
+        vp = np.full(nb * hkv * bs * d, np.nan, dtype=np.float32)
+        for t in range(L):
+            b, o = divmod(t, bs)
+            for h in range(hkv):
+                for e in range(d):
+                    kp[(((b * hkv + h) * (d // x) + e // x) * bs + o) * x + e % x] = k[t, h, e]
+                    vp[((b * hkv + h) * d + e) * bs + o] = v[t, h, e]
+        kp = kp.reshape(nb, -1)
+        vp = vp.reshape(nb, -1)
+        scale = 1.0 / math.sqrt(d) * 1.3
+        got = paged.decode(q, kp, vp, [list(range(nb))], [L], scale, hkv, bs, d, "f32")
+        g = hq // hkv
+        qt = torch.from_numpy(q.astype(np.float64)).reshape(1, hq, 1, d)
+        kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.unsqueeze(0).contiguous(), vt.unsqueeze(0).contiguous(), scale=scale)
+        ref = ref.reshape(hq, d).numpy()
+        assert np.max(np.abs(got[0] - ref)) <= 1e-12, np.max(np.abs(got[0] - ref))
+
+
+def check_closed_forms(seed=12):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 4, 2, 8
+    # L = 1: the output is the single value row, exactly
+    k = rng.standard_normal((1, hkv, d))
+    v = rng.standard_normal((1, hkv, d))
+    q = rng.standard_normal((hq, d))
+    out = paged.attend(q, k, v, 0.7)
+    for hq_i in range(hq):
+        assert np.array_equal(out[hq_i], v[0, hq_i // 2])
+    # all value rows equal c: output c
+    L = 13
+    k = rng.standard_normal((L, hkv, d))
+    c = rng.standard_normal((hkv, d))
+    v = np.broadcast_to(c, (L, hkv, d)).copy()
+    out = paged.attend(q, k, v, 0.7)
+    for hq_i in range(hq):
+        assert np.allclose(out[hq_i], c[hq_i // 2], rtol=0, atol=1e-14)
+    # q = 0 (or all keys equal): plain mean of the value rows
+    v = rng.standard_normal((L, hkv, d))
+    out = paged.attend(np.zeros((hq, d)), k, v, 0.7)
+    for hq_i in range(hq):
+        assert np.allclose(out[hq_i], v[:, hq_i // 2].mean(axis=0), rtol=0, atol=1e-14)
+    kk = np.broadcast_to(rng.standard_normal((1, hkv, d)), (L, hkv, d)).copy()
+    out = paged.attend(q, kk, v, 0.7)
+    for hq_i in range(hq):
+        assert np.allclose(out[hq_i], v[:, hq_i // 2].mean(axis=0), rtol=0, atol=1e-14)
+    # L = 0: zeros
+    assert not paged.attend(q, np.zeros((0, hkv, d)), np.zeros((0, hkv, d)), 0.7).any()
+    # two positions with a known score gap: weights are a logistic function
+    k = np.zeros((2, 1, 1))
+    v = np.array([[[1.0]], [[0.0]]])
+    k[0, 0, 0], k[1, 0, 0] = 2.0, -1.0
+    out = paged.attend(np.array([[1.0]]), k, v, 0.5)
+    assert abs(out[0, 0] - 1.0 / (1.0 + math.exp(-1.5))) <= 1e-15
+
+
+def check_gqa_equals_repeated_mha(seed=13):
+    """Grouped heads == plain multi-head attention with each KV head repeated g times."""
+    w = _rand_workload(seed, num_seqs=3, len_lo=1, len_hi=19, hq=6, hkv=2)
+    got = oracle_decode(w)
+    g = w.group
+    kp = to_np(w.k_cache)
+    vp = to_np(w.v_cache)
+    nb = kp.shape[0]
+    d, bs, hkv = w.head_dim, w.block_size, w.num_kv_heads
+    k5 = kp.reshape(nb, hkv, d // 4, bs, 4)
+    v4 = vp.reshape(nb, hkv, d, bs)
+    k_rep = np.repeat(k5, g, axis=1).reshape(nb, -1)
+    v_rep = np.repeat(v4, g, axis=1).reshape(nb, -1)
+    mha = paged.decode(to_np(w.q), k_rep, v_rep, to_np(w.block_tables), to_np(w.context_lens),
+                       w.scale, w.num_q_heads, bs, d, "f32")
+    assert np.array_equal(got, mha)
+
+
+def check_placement_invariance(seed=14):
+    """Moving physical block locations (pool and tables together) changes nothing."""
+    for dtype in ("f32", "bf16"):
+        w = _rand_workload(seed, dtype=dtype, num_seqs=4, len_lo=0, len_hi=29)
+        base = oracle_decode(w)
+        rng = np.random.default_rng(seed + 1)
+        perm = rng.permutation(w.num_blocks)       # new location of block b is perm[b]
+        kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+        kp2 = np.empty_like(kp)
+        vp2 = np.empty_like(vp)
+        kp2[perm] = kp
+        vp2[perm] = vp
+        bt = to_np(w.block_tables)
+        bt2 = np.where(bt >= 0, perm[np.maximum(bt, 0)], -1)
+        moved = paged.decode(to_np(w.q), kp2, vp2, bt2, to_np(w.context_lens), w.scale,
+                             **oracle_args(w))
+        assert np.array_equal(base, moved)
+        # and: equal to plain attention over the contiguous history
+        for i in range(w.num_seqs):
+            L = int(w.context_lens[i])
+            kc, vc = paged.gather_kv(kp, vp, bt[i], L, **oracle_args(w))
+            ref = paged.attend(paged.to_f64(to_np(w.q)[i], dtype), paged.to_f64(kc, dtype),
+                               paged.to_f64(vc, dtype), w.scale)
+            assert np.array_equal(ref, base[i])
+
+
+def check_sharing_equals_duplication(seed=15):
+    """Tables that alias prefix blocks give the same bits as tables pointing at copies."""
+    w = inputs.shared_prefix(seed=seed, num_seqs=5, prefix_len=32, suffix_lo=1, suffix_hi=20,
+                             num_blocks=64, num_q_heads=4, num_kv_heads=2)
+    shared_out = oracle_decode(w)
+    kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+    bt = to_np(w.block_tables).copy()
+    used = set(np.unique(bt[bt >= 0]).tolist())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    prefix = list(w.shared_blocks)
+    for i in range(1, w.num_seqs):               # request 0 keeps the originals
+        for j, b in enumerate(prefix):
+            nb = free.pop()
+            kp[nb] = kp[b]
+            vp[nb] = vp[b]
+            bt[i, j] = nb
+    dup_out = paged.decode(to_np(w.q), kp, vp, bt, to_np(w.context_lens), w.scale,
+                           **oracle_args(w))
+    assert np.array_equal(shared_out, dup_out)
+
+
+def check_visibility(seed=16):
+    """Positions at or past L never affect the output (NaN poison included)."""
+    for dtype in ("f32", "bf16"):
+        w = _rand_workload(seed, dtype=dtype, num_seqs=4, len_lo=1, len_hi=22)
+        base = oracle_decode(w)
+        assert np.isfinite(base).all()
+        poison_tails(w)
+        assert np.array_equal(oracle_decode(w), base)
+        # shortening a request by one token changes its output
+        lens = w.context_lens.clone()
+        i = int(torch.argmax(lens))
+        lens[i] -= 1
+        shorter = oracle_decode(w, context_lens=lens)
+        assert not np.array_equal(shorter[i], base[i])
+
+
+def check_gather_order(seed=17):
+    """Gathered history follows logical order through the table, not physical order."""
+    w = inputs.tiny(seed=seed)
+    kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+    bt = to_np(w.block_tables)
+    kc, vc = paged.gather_kv(kp, vp, bt[0], 9, **oracle_args(w))
+    for t in range(9):
+        phys, off = [9, 2, 14][t // 4], t % 4
+        k_rows, v_rows = paged.block_tokens(kp, vp, phys, **oracle_args(w))
+        assert np.array_equal(kc[t], k_rows[off]) and np.array_equal(vc[t], v_rows[off])
+
+
+# ----------------------------------------------------------------------------
+# cache writes: scatter and copy-on-write
+# ----------------------------------------------------------------------------
+
+def check_write_scatter(seed=18):
+    for dtype in ("f32", "bf16"):
+        w = _rand_workload(seed, dtype=dtype, num_seqs=3, len_lo=1, len_hi=21)
+        inputs.add_step_tokens(w)
+        kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+        bt = to_np(w.block_tables)
+        pos = to_np(w.new_pos).copy()
+        pos[1] = -1                                # one padding token
+        slots = paged.slot_mapping(bt, to_np(w.new_seq), pos, w.block_size)
+        kn, vn = to_np(w.new_k), to_np(w.new_v)
+        k2, v2 = paged.write_kv(kp, vp, kn, vn, slots, **oracle_args(w))
+        touched = np.zeros(kp.shape[0], dtype=bool)
+        for t, s in enumerate(slots):
+            if s < 0:
+                continue
+            L = int(pos[t]) + 1
+            kc, vc = paged.gather_kv(k2, v2, bt[t], L, **oracle_args(w))
+            assert np.array_equal(kc[L - 1], kn[t]) and np.array_equal(vc[L - 1], vn[t])
+            kc0, vc0 = paged.gather_kv(kp, vp, bt[t], L - 1, **oracle_args(w))
+            assert np.array_equal(kc[:L - 1], kc0) and np.array_equal(vc[:L - 1], vc0)
+            touched[s // w.block_size] = True
+        # every other block is byte-identical (NaN bits compared as bits)
+        for b in np.nonzero(~touched)[0]:
+            assert kp[b].tobytes() == k2[b].tobytes() and vp[b].tobytes() == v2[b].tobytes()
+        # the padding token's data appears nowhere it was not written
+        assert slots[1] == -1
+
+
+def check_copy_on_write(seed=19):
+    """Fork + divergent append: only the partly filled shared block is copied,
+    the writer's history differs from the others only at its new token."""
+    bs, hkv, d = 4, 2, 16
+    nb = 24
+    pool = oblocks.BlockPool(nb, bs)
+    parent = pool.new_sequence()
+    for _ in range(10):                            # 2 full blocks + 2 tokens in a third
+        pool.append(parent)
+    kids = [pool.fork(parent) for _ in range(3)]
+    assert all(pool.refcount[b] == 4 for b in parent.table)
+    rng = np.random.default_rng(seed)
+    kp = rng.standard_normal((nb, hkv * bs * d)).astype(np.float32)
+    vp = rng.standard_normal((nb, hkv * bs * d)).astype(np.float32)
+    res = pool.append(kids[0])
+    assert res.cow == (parent.table[-1], kids[0].table[-1])
+    assert res.allocated is None
+    assert kids[0].table[:2] == parent.table[:2]       # full blocks stay shared
+    assert pool.refcount[parent.table[-1]] == 3
+    k2, v2 = paged.copy_blocks(kp, vp, [res.cow])
+    assert np.array_equal(k2[res.cow[1]], kp[res.cow[0]])
+    assert np.array_equal(v2[res.cow[1]], vp[res.cow[0]])
+    changed = [b for b in range(nb) if not np.array_equal(k2[b], kp[b])]
+    assert changed == [res.cow[1]]
+    kn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    vn = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    k3, v3 = paged.write_kv(k2, v2, kn, vn, [res.slot], hkv, bs, d, "f32")
+    for other in [parent] + kids[1:]:
+        a = paged.gather_kv(kp, vp, other.table, other.length, hkv, bs, d, "f32")
+        b = paged.gather_kv(k3, v3, other.table, other.length, hkv, bs, d, "f32")
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    mine = paged.gather_kv(k3, v3, kids[0].table, kids[0].length, hkv, bs, d, "f32")
+    before = paged.gather_kv(kp, vp, parent.table, parent.length, hkv, bs, d, "f32")
+    assert np.array_equal(mine[0][:10], before[0]) and np.array_equal(mine[0][10], kn[0])
+    # the remaining branches also copy; the last copy leaves the parent alone on the block
+    for kid in kids[1:]:
+        assert pool.append(kid).cow is not None
+    assert pool.refcount[parent.table[-1]] == 1
+    assert pool.append(parent).cow is None             # sole owner appends in place
+
+
+def check_refcount_free():
+    pool = oblocks.BlockPool(8, 4)
+    a = pool.new_sequence()
+    for _ in range(6):
+        pool.append(a)
+    b = pool.fork(a)
+    pool.free(a)                                       # finishing one request frees nothing shared
+    assert pool.num_free == 6 and all(pool.refcount[x] == 1 for x in b.table)
+    pool.free(b)
+    assert pool.num_free == 8
+    try:
+        pool.release(0)
+    except oblocks.RefcountError:
+        pass
+    else:
+        raise AssertionError("refcount underflow not caught")
+    c = pool.new_sequence()
+    for _ in range(32):
+        pool.append(c)
+    try:
+        pool.append(c)
+    except oblocks.PoolExhausted:
+        pass
+    else:
+        raise AssertionError("exhaustion not caught")
+
+
+def check_fanout_scenario(num_prompts=6, branches=4):
+    """The fan-out workload's tables and copy pairs are what the block model
+    decides for fork + one divergent append per branch (up to block ids)."""
+    w = inputs.fanout(num_prompts=num_prompts, branches=branches, prompt_lo=17, prompt_hi=60,
+                      num_blocks=256)
+    plens = w.extra["prompt_lens"]
+    bt = to_np(w.block_tables)
+    pairs = to_np(w.cow_pairs).tolist()
+    dsts = [p[1] for p in pairs]
+    assert len(set(dsts)) == len(dsts)
+    all_parent = {b for t in w.parent_tables for b in t}
+    assert not (set(dsts) & all_parent)
+    pool = oblocks.BlockPool(256, 16)
+    for p, n in enumerate(plens):
+        parent = pool.new_sequence()
+        for _ in range(n):
+            pool.append(parent)
+        kids = [pool.fork(parent) for _ in range(branches)]
+        for b, kid in enumerate(kids):
+            r = pool.append(kid)
+            i = p * branches + b
+            # same structure: shared full blocks, one copy of the partial block
+            assert r.cow is not None and r.cow[0] == parent.table[-1]
+            assert pairs[i][0] == w.parent_tables[p][-1]
+            assert bt[i, :len(kid.table) - 1].tolist() == w.parent_tables[p][:-1]
+            assert bt[i, len(kid.table) - 1] == pairs[i][1]
+            assert int(w.context_lens[i]) == kid.length == n + 1
+            assert int(w.new_pos[i]) == n
+        pool.free(parent)
+
+
+ALL_CHECKS = [
+    check_worked_address, check_fixed_blocks_16, check_block_growth, check_tail_waste_bound,
+    check_layout_contract, check_sdpa_identity_tables, check_closed_forms,
+    check_gqa_equals_repeated_mha, check_placement_invariance, check_sharing_equals_duplication,
+    check_visibility, check_gather_order, check_write_scatter, check_copy_on_write,
+    check_refcount_free, check_fanout_scenario,
+]

@@ -1,0 +1,187 @@
+"""Plausible mistakes planted in the CPU oracle must trip at least one pin.
+
+Each case monkeypatches one oracle function with a wrong variant (a dropped
+term, a wrong index, a transposed operand, an off-by-one) and runs every pin
+check; the test passes only if some check fails.  This shows the pins are
+strong enough to catch the mistake.  Nothing here touches a GPU.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import blocks as oblocks
+from oracle import paged
+from tests import pins
+
+_orig_attend = paged.attend
+_orig_gather = paged.gather_kv
+_orig_block_tokens = paged.block_tokens
+_orig_write = paged.write_kv
+
+
+def _translate_swapped(position, block_table, block_size):
+    offset, logical = divmod(int(position), int(block_size))
+    phys = int(block_table[min(logical, len(block_table) - 1)])
+    return logical, offset, phys, phys * block_size + offset
+
+
+def _translate_bad_slot(position, block_table, block_size):
+    logical, offset = divmod(int(position), int(block_size))
+    phys = int(block_table[logical])
+    return logical, offset, phys, phys * block_size + logical
+
+
+def _blocks_needed_floor(n, bs):
+    return n // bs
+
+
+def _attend_no_scale(q, keys, values, scale):
+    return _orig_attend(q, keys, values, 1.0)
+
+
+def _attend_modulo_heads(q, keys, values, scale):
+    hq, d = q.shape
+    L, hkv, _ = keys.shape
+    out = np.zeros((hq, d))
+    if L == 0:
+        return out
+    for h_q in range(hq):
+        h = h_q % hkv                              # wrong grouping
+        s = scale * (keys[:, h, :] @ q[h_q])
+        w = np.exp(s - s.max())
+        out[h_q] = (w @ values[:, h, :]) / w.sum()
+    return out
+
+
+def _attend_unnormalised(q, keys, values, scale):
+    hq, d = q.shape
+    L, hkv, _ = keys.shape
+    g = hq // hkv
+    out = np.zeros((hq, d))
+    if L == 0:
+        return out
+    for h_q in range(hq):
+        s = scale * (keys[:, h_q // g, :] @ q[h_q])
+        out[h_q] = np.exp(s - s.max()) @ values[:, h_q // g, :]
+    return out
+
+
+def _attend_drop_last(q, keys, values, scale):
+    return _orig_attend(q, keys[:-1], values[:-1], scale) if keys.shape[0] > 1 else \
+        _orig_attend(q, keys, values, scale)
+
+
+def _attend_values_as_keys(q, keys, values, scale):
+    return _orig_attend(q, keys, keys, scale)
+
+
+def _gather_physical_order(k_pool, v_pool, block_table, context_len, **kw):
+    n = paged.blocks_needed(context_len, kw["block_size"])
+    return _orig_gather(k_pool, v_pool, sorted(block_table[:n]), context_len, **kw)
+
+
+def _gather_one_extra(k_pool, v_pool, block_table, context_len, **kw):
+    bs = kw["block_size"]
+    if context_len % bs and context_len:
+        return _orig_gather(k_pool, v_pool, block_table, context_len + 1, **kw)
+    return _orig_gather(k_pool, v_pool, block_table, context_len, **kw)
+
+
+def _block_tokens_k_transposed(k_pool, v_pool, physical_block, num_kv_heads, block_size,
+                               head_dim, dtype):
+    x = 16 // paged.ELEM_BYTES[dtype]
+    k5 = np.asarray(k_pool).reshape(-1, num_kv_heads, block_size, head_dim // x, x)
+    k_rows = k5[physical_block].transpose(1, 0, 2, 3).reshape(block_size, num_kv_heads,
+                                                                head_dim)
+    _, v_rows = _orig_block_tokens(k_pool, v_pool, physical_block, num_kv_heads, block_size,
+                                   head_dim, dtype)
+    return k_rows, v_rows
+
+
+def _block_tokens_v_rowmajor(k_pool, v_pool, physical_block, num_kv_heads, block_size,
+                             head_dim, dtype):
+    k_rows, _ = _orig_block_tokens(k_pool, v_pool, physical_block, num_kv_heads, block_size,
+                                   head_dim, dtype)
+    v_rows = np.asarray(v_pool).reshape(-1, num_kv_heads, block_size, head_dim)[physical_block]
+    return k_rows, v_rows.transpose(1, 0, 2)
+
+
+def _write_wrong_block(k_pool, v_pool, k_new, v_new, slots, num_kv_heads, block_size,
+                       head_dim, dtype):
+    bad = [(-1 if s < 0 else (s % block_size) * block_size + s // block_size) for s in slots]
+    bad = [b if b < np.asarray(k_pool).shape[0] * block_size else -1 for b in bad]
+    return _orig_write(k_pool, v_pool, k_new, v_new, bad, num_kv_heads, block_size, head_dim,
+                       dtype)
+
+
+def _copy_reversed(k_pool, v_pool, pairs):
+    k = np.array(k_pool, copy=True)
+    v = np.array(v_pool, copy=True)
+    for src, dst in pairs:
+        k[int(src)] = k[int(dst)]
+        v[int(src)] = v[int(dst)]
+    return k, v
+
+
+def _append_in_place(self, seq):
+    bs = self.block_size
+    allocated = None
+    if seq.length % bs == 0:
+        allocated = self.allocate()
+        seq.table.append(allocated)
+    slot = paged.translate(seq.length, seq.table, bs)[3]
+    seq.length += 1
+    return oblocks.AppendResult(slot=slot, allocated=allocated, cow=None)
+
+
+def _free_without_refcount(self, seq):
+    for b in seq.table:
+        self.refcount[b] = 0
+        self._free.append(b)
+    seq.table = []
+    seq.length = 0
+
+
+MUTATIONS = {
+    "translate_swapped_divmod": (paged, "translate", _translate_swapped),
+    "translate_slot_uses_logical": (paged, "translate", _translate_bad_slot),
+    "blocks_needed_floor": (paged, "blocks_needed", _blocks_needed_floor),
+    "attend_drops_scale": (paged, "attend", _attend_no_scale),
+    "attend_heads_modulo": (paged, "attend", _attend_modulo_heads),
+    "attend_unnormalised": (paged, "attend", _attend_unnormalised),
+    "attend_drops_newest_token": (paged, "attend", _attend_drop_last),
+    "attend_mixes_keys": (paged, "attend", _attend_values_as_keys),
+    "gather_physical_order": (paged, "gather_kv", _gather_physical_order),
+    "gather_reads_past_length": (paged, "gather_kv", _gather_one_extra),
+    "layout_k_chunks_transposed": (paged, "block_tokens", _block_tokens_k_transposed),
+    "layout_v_row_major": (paged, "block_tokens", _block_tokens_v_rowmajor),
+    "write_wrong_block": (paged, "write_kv", _write_wrong_block),
+    "copy_reversed": (paged, "copy_blocks", _copy_reversed),
+    "append_without_cow": (oblocks.BlockPool, "append", _append_in_place),
+    "free_ignores_refcount": (oblocks.BlockPool, "free", _free_without_refcount),
+}
+
+
+def _gather_kw_wrapper(fn):
+    """gather_kv is called positionally inside the oracle; adapt the mutants."""
+    def wrapped(k_pool, v_pool, block_table, context_len, num_kv_heads, block_size, head_dim,
+                dtype):
+        return fn(k_pool, v_pool, block_table, context_len, num_kv_heads=num_kv_heads,
+                  block_size=block_size, head_dim=head_dim, dtype=dtype)
+    return wrapped
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    owner, attr, fn = MUTATIONS[name]
+    if attr == "gather_kv":
+        fn = _gather_kw_wrapper(fn)
+    monkeypatch.setattr(owner, attr, fn)
+    failed = []
+    for check in pins.ALL_CHECKS:
+        try:
+            check()
+        except AssertionError:
+            failed.append(check.__name__)
+            break
+    assert failed, f"mutation {name} passed every pin"
