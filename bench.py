@@ -1,0 +1,268 @@
+"""Benchmark of the paged decode hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout]
+
+A step is one pass of the whole hot path over one batch of synthetic
+requests: copy-on-write block copies (only the fan-out workload has any),
+the KV write of each request's newest token through its slot, and decode
+attention over every request's paged history.  Inputs are resident in HBM
+before timing starts.  Steps cycle through R replicas of the batch placed
+at disjoint physical blocks, so the 256 MB Infinity Cache cannot hold the
+working set between steps (every replica holds the same bytes, so every
+replica gives bit-identical outputs; the benchmark checks that).
+
+Prints one JSON line.  ``value`` is KV GB/s: algorithmic bytes of a step
+(distinct KV bytes read by decode + q/out/table/length bytes + the KV write
+and copy bytes) per second.  ``roofline`` is for the decode call, timed on
+its own with HIP events on the stream it runs on.  ``cpu_baseline`` times
+the CPU oracle on the same workload (first requests until ~10 s of work).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_252_amd import inputs, ops  # noqa: E402
+
+METRIC = "paged decode attn: KV GB/s (% HBM peak) + decode tokens/s, 1x MI355X"
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    "gqa": dict(make=inputs.gqa, replicas=8,
+                desc="GQA decode: 32 requests, context U[512,4096], 32 q / 8 KV heads, "
+                     "head_dim 128, block 16, bf16, blocks shuffled in a 65536-block pool"),
+    "prefix": dict(make=inputs.shared_prefix, replicas=4,
+                   desc="shared prefix: 256 requests, first 2048 tokens in the same 128 blocks, "
+                        "private suffix U[64,512], 32 q / 8 KV heads, head_dim 128, block 16, bf16"),
+    "long": dict(make=inputs.long_context, replicas=1,
+                 desc="long context: 8 requests, context U[32768,131072], 64 q / 8 KV heads, "
+                      "head_dim 128, block 16, bf16, pool sized to fit"),
+    "fanout": dict(make=inputs.fanout, replicas=1,
+                   desc="fan-out step: 128 prompts x 4 branches, prompt U[256,2048] with a "
+                        "partial last block, copy-on-write of that block per branch, one new "
+                        "token per branch, 32 q / 8 KV heads, head_dim 128, block 16, bf16"),
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def unique_kv_tokens(tables: np.ndarray, lens: np.ndarray, bs: int) -> int:
+    """Distinct cached positions decode reads: per physical block, the most
+    positions any request reads from it."""
+    best = {}
+    for t, L in zip(tables, lens):
+        L = int(L)
+        for j in range(-(-L // bs)):
+            n = min(bs, L - j * bs)
+            b = int(t[j])
+            if best.get(b, 0) < n:
+                best[b] = n
+    return sum(best.values())
+
+
+def decode_bytes(w) -> dict:
+    """Algorithmic bytes of one decode call."""
+    e = 2 if w.dtype == "bf16" else 4
+    tables = w.block_tables.cpu().numpy()
+    lens = w.context_lens.cpu().numpy()
+    per_tok = w.num_kv_heads * w.head_dim * 2 * e          # K + V of one position
+    uniq = unique_kv_tokens(tables, lens, w.block_size) * per_tok
+    logical = int(lens.sum()) * per_tok
+    qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e   # q read + out written
+    meta = 4 * sum(-(-int(L) // w.block_size) for L in lens) + 4 * w.num_seqs
+    return dict(unique=uniq + qo + meta, logical=logical + qo + meta, kv_unique=uniq,
+                kv_logical=logical)
+
+
+def step_extra_bytes(w) -> int:
+    """Algorithmic bytes of the KV write (read new K/V, write them, read slots)
+    and of the block copies (read + write whole blocks)."""
+    e = 2 if w.dtype == "bf16" else 4
+    t = w.new_k.shape[0] if w.new_k is not None else 0
+    write = 2 * 2 * t * w.num_kv_heads * w.head_dim * e + 8 * t
+    pairs = w.cow_pairs.shape[0] if w.cow_pairs is not None else 0
+    copy = pairs * (2 * 2 * w.block_elems * e + 16)
+    return write + copy
+
+
+def cpu_baseline(w, budget_s: float = 10.0) -> dict:
+    """The CPU oracle as it stands, on the first requests of the workload."""
+    from oracle import paged
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        threads = 1
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    bt = host(w.block_tables)
+    lens = host(w.context_lens)
+    used = np.unique(bt[bt >= 0])
+    if w.cow_pairs is not None:
+        used = np.union1d(used, host(w.cow_pairs)[:, 0])
+    sel = torch.as_tensor(used, device=w.k_cache.device)
+    kp, vp = host(w.k_cache[sel]), host(w.v_cache[sel])       # compact pool of used blocks
+    remap = np.full(w.num_blocks, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    bt_c = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1)
+    q = host(w.q)
+    args = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim,
+                dtype=w.dtype)
+    new_k = host(w.new_k) if w.new_k is not None else None
+    new_v = host(w.new_v) if w.new_v is not None else None
+    pairs = remap[host(w.cow_pairs)] if w.cow_pairs is not None else None
+    e = 2 if w.dtype == "bf16" else 4
+    per_tok = w.num_kv_heads * w.head_dim * 2 * e
+    done, kv_bytes = 0, 0
+    t0 = time.perf_counter()
+    while done < w.num_seqs and (time.perf_counter() - t0) < budget_s:
+        n = min(w.num_seqs - done, max(1, w.num_seqs // 8))
+        rows = slice(done, done + n)
+        k_use, v_use = kp, vp
+        if pairs is not None:
+            k_use, v_use = paged.copy_blocks(k_use, v_use, pairs[rows])
+        if new_k is not None:
+            slots = paged.slot_mapping(bt_c, np.arange(done, done + n), lens[rows] - 1,
+                                       w.block_size)
+            k_use, v_use = paged.write_kv(k_use, v_use, new_k[rows], new_v[rows], slots, **args)
+        paged.decode(q[rows], k_use, v_use, bt_c[rows], lens[rows], w.scale, **args)
+        kv_bytes += int(lens[rows].sum()) * per_tok
+        done += n
+    dt = time.perf_counter() - t0
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} of {w.num_seqs} requests ({w.name}), one pass: copy/write "
+                      f"for those requests then fp64 decode, {dt:.2f} s",
+            "tokens_per_s": done / dt, "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")
+    ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=200)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the paged decode path here runs on a single "
+              "MI355X with no collectives; run it with --gpus 1.", file=sys.stderr, flush=True)
+        return 2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = WORKLOADS[args.workload]
+    log(f"generating {args.workload}")
+    w = cfg["make"](device=dev, poison=False)
+    if w.new_k is None:
+        inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    reps = args.replicas or cfg["replicas"]
+    tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
+    slots = [ops.slot_mapping(w.block_size, t, w.new_pos, w.new_seq) for t in tables]
+    max_len = w.max_context_len
+    part = args.partition or ops.decode_partition_tokens(spec, w.num_seqs, w.num_q_heads, max_len)
+    ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(w.q) for _ in tables]
+    log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
+        f"workspace {ws_bytes} B, {reps} replicas")
+
+    def step(r: int) -> None:
+        if w.cow_pairs is not None:
+            ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
+        ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots[r])
+        ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
+                   out=outs[r], workspace=workspace, partition_tokens=part)
+
+    for i in range(args.warmup):
+        step(i % reps)
+    torch.cuda.synchronize()
+    # every replica holds the same bytes: outputs must agree bit for bit
+    for r in range(reps):
+        step(r)
+    torch.cuda.synchronize()
+    for r in range(1, reps):
+        if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
+            log("replica outputs differ")
+            return 1
+
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % reps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    # the dominant kernel: decode alone, HIP events on the stream it runs on
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.kernel_iters):
+        r = i % reps
+        ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
+                   out=outs[r], workspace=workspace, partition_tokens=part)
+    ev1.record(stream)
+    ev1.synchronize()
+    dec_us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
+
+    db = decode_bytes(w)
+    step_bytes = db["unique"] + step_extra_bytes(w)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    achieved = db["unique"] / (dec_us * 1e-6) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"], "name": args.workload, "requests": w.num_seqs,
+                   "max_context_len": max_len, "total_context_tokens": int(w.context_lens.sum()),
+                   "replicas": reps, "partition_tokens": part},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
+        "kv_gbs_logical": round((db["logical"] + step_extra_bytes(w)) / (ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_decode", "bytes_per_launch": db["unique"],
+                     "avg_launch_us": round(dec_us, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

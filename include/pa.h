@@ -1,0 +1,248 @@
+/*
+ * pa.h -- C ABI of libpagedkv: decode attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ZQ] zenaique.com, "How does PagedAttention enable prefix sharing across
+ *        requests and what data structure makes it cheap?" (answer, TL;DR,
+ *        "Most common mistake").
+ *   [KG] kgptalkie.com, "Day 28: PagedAttention".
+ *
+ * The KV cache of one attention layer lives in fixed-size physical blocks
+ * ([KG] "Split the Cache Into Fixed Blocks").  A request reaches its tokens
+ * through a block table: the token at logical position p is in logical
+ * block p / block_size at offset p % block_size, and the table names the
+ * physical block ([KG] "The Block Table Is the Map", "Follow One Token
+ * Address").  Requests that share a prefix name the same physical blocks;
+ * copy-on-write copies only a block that diverges ([ZQ] answer, "Most common
+ * mistake"; [KG] "Shared Blocks Must Not Be Changed in Place").
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions for every call
+ * ---------------------------------------------------------------------------
+ *  - Pointers named *_cache, q, out, k_new, v_new, block_tables,
+ *    context_lens, slot_mapping, block_pairs, seq_ids, positions, workspace
+ *    are DEVICE pointers (memory of the current HIP device).  Descriptor
+ *    structs and scalars are host values.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on `stream` and returns; nothing
+ *    synchronises unless PA_VALIDATE=1 is set in the environment (below).
+ *  - The caller owns all memory.  The library allocates no device memory,
+ *    keeps no pointer after a call returns and holds no global mutable state
+ *    except a thread-local error message.
+ *  - Return value: PA_OK (0) or a pa_status_t error.  On error nothing was
+ *    enqueued and pa_last_error() describes the problem.  Device-side
+ *    contract violations (a block id outside [0, num_blocks), a context
+ *    length above max_context_len, duplicate write slots, a copy destination
+ *    that is also a source) are not detected in normal runs; the kernels
+ *    clamp every such index so no access leaves the buffers, and the
+ *    results are then unspecified.  With PA_VALIDATE=1 the library copies
+ *    the index arrays to the host (a synchronising copy) and rejects such
+ *    calls with PA_ERR_VALIDATE before launching.
+ *
+ * ---------------------------------------------------------------------------
+ * Cache layout (one layer; K and V are separate buffers)
+ * ---------------------------------------------------------------------------
+ *  The pages leave the bytes of a block to the implementation ([KG] "Split
+ *  the Cache Into Fixed Blocks").  This library fixes them so that a block's
+ *  keys feed the gfx950 matrix cores straight from 16-byte loads:
+ *
+ *    x = 16 / sizeof(element)           (8 for bf16, 4 for f32)
+ *    K element (block b, kv head h, offset t, dim d) at index
+ *        (((b * Hkv + h) * (D / x) + d / x) * block_size + t) * x + d % x
+ *    V element (block b, kv head h, offset t, dim d) at index
+ *        ((b * Hkv + h) * D + d) * block_size + t
+ *
+ *  i.e. K is [num_blocks][Hkv][D/x][block_size][x] and V is
+ *  [num_blocks][Hkv][D][block_size].  A (block, head) tile is contiguous
+ *  (4 KiB for K and 4 KiB for V at block_size 16, D 128, bf16).  Both
+ *  buffers must be 16-byte aligned.
+ *
+ *  Queries, outputs and new-token K/V are plain row-major
+ *  [tokens][heads][D].  Query head hq reads KV head hq / (Hq / Hkv).
+ */
+#ifndef PAGED_KV_PA_H
+#define PAGED_KV_PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+    PA_F32 = 0,   /* IEEE binary32 */
+    PA_BF16 = 1,  /* bfloat16 */
+} pa_dtype_t;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,         /* a required pointer is NULL */
+    PA_ERR_SHAPE = 2,        /* a size is negative, zero where it must not be, or inconsistent */
+    PA_ERR_DTYPE = 3,        /* unknown dtype */
+    PA_ERR_ALIGN = 4,        /* a buffer is not 16-byte aligned */
+    PA_ERR_UNSUPPORTED = 5,  /* a combination outside the compiled set */
+    PA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than pa_decode_workspace_bytes */
+    PA_ERR_HIP = 7,          /* the HIP runtime reported an error (launch or query) */
+    PA_ERR_VALIDATE = 8,     /* PA_VALIDATE=1 found an index outside its range */
+} pa_status_t;
+
+/* Shape of one layer's paged KV cache. */
+typedef struct {
+    int64_t num_blocks;    /* physical blocks in each of the K and V buffers, >= 1 */
+    int32_t block_size;    /* token positions per block: 1..256 (16 on the fast path) */
+    int32_t num_kv_heads;  /* Hkv >= 1 */
+    int32_t head_dim;      /* D: 16, 32, 64, 128 or 256 (128 on the fast path) */
+    int32_t dtype;         /* pa_dtype_t of K, V, q, out, k_new, v_new */
+} pa_cache_desc_t;
+
+/* Version of this ABI (PA_ABI_VERSION of the library that was built). */
+int pa_abi_version(void);
+
+/* Static name of a status code. */
+const char* pa_status_string(int status);
+
+/* Detail for the last non-OK return on this thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * pa_write_kv -- scatter new tokens' keys and values into the cache.
+ *
+ * For every token t with slot_mapping[t] >= 0, writes k_new[t][h][:] and
+ * v_new[t][h][:] for every KV head h at block slot / block_size, offset
+ * slot % block_size ([KG] "Follow One Token Address": the flat slot is
+ * physical_block * block_size + offset).  A negative slot marks a padding
+ * token and is skipped.  Bytes are copied unchanged.
+ *
+ *   c            cache descriptor (host)
+ *   k_cache      [num_blocks] blocks in the K layout above (written)
+ *   v_cache      [num_blocks] blocks in the V layout above (written)
+ *   k_new, v_new [num_tokens][Hkv][D], dtype c->dtype
+ *   slot_mapping int64 [num_tokens]; valid slots are < num_blocks * block_size
+ *                and unique (a duplicate slot is a race; the winner is unspecified)
+ *   num_tokens   >= 0 (0 enqueues nothing)
+ */
+int pa_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block copies.
+ *
+ * For each pair i, copies the whole physical block block_pairs[2i] (src) to
+ * block_pairs[2i+1] (dst): every head, every slot, K and V ([ZQ] answer: a
+ * diverging request gets a fresh block; [KG] "Shared Blocks Must Not Be
+ * Changed in Place": a private copy is made before the shared part changes;
+ * [ZQ] "Most common mistake": only that block is copied).  Destinations
+ * must be distinct and no destination may be a source of the same call.
+ *
+ *   block_pairs  int64 [num_pairs][2] = {src, dst}, each in [0, num_blocks)
+ *   num_pairs    >= 0 (0 enqueues nothing)
+ */
+int pa_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                   const int64_t* block_pairs, int32_t num_pairs, void* stream);
+
+/*
+ * pa_slot_mapping -- address translation on the device.
+ *
+ * slot_mapping[t] = block_tables[s][p / block_size] * block_size + p % block_size
+ * with s = seq_ids[t] (or t when seq_ids is NULL) and p = positions[t]
+ * ([KG] "Follow One Token Address").  A negative position gives -1; so does
+ * a position past the table (p / block_size >= max_blocks_per_seq), a
+ * sequence index outside [0, num_seqs) or a negative table entry.
+ *
+ *   block_tables int32 [num_seqs][max_blocks_per_seq]
+ *   seq_ids      int32 [num_tokens] or NULL
+ *   positions    int32 [num_tokens]
+ *   slot_mapping int64 [num_tokens] (written)
+ */
+int pa_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                    const int32_t* positions, int32_t num_tokens, int64_t* slot_mapping,
+                    void* stream);
+
+/*
+ * pa_gather_kv -- the contiguous history of one request.
+ *
+ * Walks block_table in logical order and writes the first context_len
+ * tokens' keys and values as row-major [context_len][Hkv][D] ([KG] "Batching
+ * Becomes More Flexible": the kernel reads the request's table and gathers
+ * its history).  A copy, bit for bit; used to check address translation in
+ * isolation.
+ *
+ *   block_table  int32 [ceil(context_len / block_size)] (device)
+ *   k_out, v_out [context_len][Hkv][D], dtype c->dtype (written)
+ */
+int pa_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, int32_t context_len, void* k_out, void* v_out,
+                 void* stream);
+
+/*
+ * Partition length, in tokens, that pa_decode uses for split-K when
+ * partition_tokens = 0.  It depends only on these host scalars and the
+ * device's compute-unit count, never on block placement, so outputs are
+ * bit-identical whatever the physical block ids.
+ */
+int32_t pa_decode_partition_tokens(const pa_cache_desc_t* c, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes (0 when every request
+ * fits one partition): the fp32 partial results of every partition,
+ * S * Hq * ceil(max_context_len / partition) * (D + 2) floats.
+ * partition_tokens as for pa_decode (0 = automatic).
+ */
+size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_tokens);
+
+/*
+ * pa_decode -- one decode query per request against its paged history.
+ *
+ * For request i and query head hq, with h = hq / (Hq / Hkv) and
+ * L = context_lens[i]:
+ *     s_t = scale * <q[i][hq], K_i[t][h]>          for t = 0 .. L-1
+ *     out[i][hq] = sum_t softmax(s)_t * V_i[t][h]
+ * where K_i[t], V_i[t] are found through block_tables[i] as in
+ * pa_slot_mapping ([KG] "Follow One Token Address": after lookup the newest
+ * query scores the keys, applies its visibility rule and mixes the values;
+ * "The Contiguous Allocation Problem": the attention formula is unchanged by
+ * paging).  The query sees positions [0, L): the cache holds the current
+ * token's K/V (written by pa_write_kv) and nothing later.  L = 0 gives a
+ * zero output.  Positions at or past L are never read into the result, so
+ * stale or NaN bytes there do not matter.
+ *
+ * Arithmetic: fp32 accumulation; bf16 outputs are rounded to nearest even.
+ * Long histories are split into partitions of partition_tokens positions
+ * whose partial softmax states are merged in a fixed order, so results are
+ * deterministic and independent of physical block placement.
+ *
+ *   q             [num_seqs][num_q_heads][D], dtype c->dtype
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs], 0 <= L <= max_context_len and
+ *                 L <= max_blocks_per_seq * block_size
+ *   num_q_heads   a multiple of Hkv, with Hq / Hkv <= 16
+ *   max_context_len  host int >= every L (sizes the launch; no device->host sync)
+ *   scale         softmax scale (1/sqrt(D) for standard attention)
+ *   out           [num_seqs][num_q_heads][D], dtype c->dtype (written)
+ *   workspace     device scratch of >= pa_decode_workspace_bytes(...) bytes,
+ *                 16-byte aligned, any contents (may be NULL when the size
+ *                 is 0).  Calls in flight at the same time must not share a
+ *                 workspace.
+ *   partition_tokens  0 = automatic; otherwise a multiple of block_size in
+ *                 [block_size, 1024] (the fast path also needs a multiple of 16)
+ */
+int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+              const void* q, const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+              int32_t max_context_len, float scale, void* out, void* workspace,
+              size_t workspace_bytes, int32_t partition_tokens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_KV_PA_H */

@@ -1,0 +1,368 @@
+// C ABI of libpagedkv: argument checks, split-K planning, optional host-side
+// validation of device index arrays, and dispatch to the kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+constexpr int kMaxPartitionTokens = 1024;   // fast path: one table entry per lane of a wave
+constexpr int kMinAutoPartitionTokens = 256;
+constexpr int kWavesPerCu = 8;              // decode waves the plan aims to keep resident per CU
+constexpr int kMaxGridYZ = 65535;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+}  // namespace
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return PA_OK;
+}
+
+int check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return PA_OK;
+}
+
+bool validate_enabled() {
+    const char* v = std::getenv("PA_VALIDATE");
+    return v != nullptr && v[0] == '1';
+}
+
+int check_desc(const pa_cache_desc_t* c) {
+    if (c == nullptr) return fail(PA_ERR_NULL, "cache descriptor is NULL");
+    if (c->dtype != PA_F32 && c->dtype != PA_BF16) return fail(PA_ERR_DTYPE, "unknown dtype %d", c->dtype);
+    if (c->num_blocks < 1) return fail(PA_ERR_SHAPE, "num_blocks must be >= 1 (got %lld)", (long long)c->num_blocks);
+    if (c->block_size < 1 || c->block_size > 256)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d outside [1, 256]", c->block_size);
+    if (c->num_kv_heads < 1 || c->num_kv_heads > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "num_kv_heads %d outside [1, %d]", c->num_kv_heads, kMaxGridYZ);
+    switch (c->head_dim) {
+        case 16: case 32: case 64: case 128: case 256: break;
+        default: return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128, 256}", c->head_dim);
+    }
+    return PA_OK;
+}
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+namespace {
+
+int granule(const pa_cache_desc_t* c, int group) {
+    return fast_path_ok(c, group) ? 16 : c->block_size;
+}
+
+int32_t plan_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_context_len) {
+    const int group = num_q_heads / c->num_kv_heads;
+    const int g = granule(c, group);
+    const int cap = (kMaxPartitionTokens / g) * g;
+    if (max_context_len <= 0) return g;
+    const int64_t units = static_cast<int64_t>(num_seqs) * (fast_path_ok(c, group) ? c->num_kv_heads : num_q_heads);
+    const int64_t target = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
+    int64_t p = ceil_div(static_cast<int64_t>(max_context_len) * std::max<int64_t>(units, 1), target);
+    p = std::max<int64_t>(p, kMinAutoPartitionTokens);
+    p = ceil_div(p, g) * g;
+    p = std::min<int64_t>(p, cap);
+    if (p >= max_context_len) p = std::min<int64_t>(ceil_div(max_context_len, g) * g, cap);
+    return static_cast<int32_t>(std::max<int64_t>(p, g));
+}
+
+// Workspace layout: the partials acc [S][Hq][parts][D], then m and l
+// [S][Hq][parts], all fp32.
+size_t workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t max_context_len, int32_t part) {
+    const int64_t max_parts = ceil_div(std::max(max_context_len, 0), part);
+    if (max_parts <= 1) return 0;
+    return static_cast<size_t>(num_seqs) * num_q_heads * max_parts * (c->head_dim + 2) * sizeof(float);
+}
+
+// Host copies of small device arrays, for PA_VALIDATE=1.
+template <typename T>
+int fetch(std::vector<T>& host, const T* dev, size_t n, hipStream_t stream) {
+    host.resize(n);
+    if (n == 0) return PA_OK;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipMemcpy(host.data(), dev, n * sizeof(T), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "PA_VALIDATE copy failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
+int resolve_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_context_len, int32_t requested, int32_t* out) {
+    if (requested == 0) {
+        *out = plan_partition(c, num_seqs, num_q_heads, max_context_len);
+        return PA_OK;
+    }
+    const int group = num_q_heads / c->num_kv_heads;
+    const int g = granule(c, group);
+    if (requested < c->block_size || requested > kMaxPartitionTokens || requested % g != 0)
+        return fail(PA_ERR_SHAPE,
+                    "partition_tokens %d must be a multiple of %d in [%d, %d]", requested, g,
+                    c->block_size, kMaxPartitionTokens);
+    *out = requested;
+    return PA_OK;
+}
+
+int check_heads(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads) {
+    if (num_seqs < 0 || num_seqs > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "num_seqs %d outside [0, %d]", num_seqs, kMaxGridYZ);
+    if (num_q_heads < 1 || num_q_heads > kMaxGridYZ || num_q_heads % c->num_kv_heads != 0)
+        return fail(PA_ERR_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                    num_q_heads, c->num_kv_heads);
+    return PA_OK;
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+int pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_NULL: return "PA_ERR_NULL";
+        case PA_ERR_SHAPE: return "PA_ERR_SHAPE";
+        case PA_ERR_DTYPE: return "PA_ERR_DTYPE";
+        case PA_ERR_ALIGN: return "PA_ERR_ALIGN";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+        case PA_ERR_VALIDATE: return "PA_ERR_VALIDATE";
+        default: return "PA_ERR_UNKNOWN";
+    }
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int pa_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                const void* v_new, const int64_t* slot_mapping, int32_t num_tokens,
+                void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if (num_tokens < 0) return fail(PA_ERR_SHAPE, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping)
+        return fail(PA_ERR_NULL, "pa_write_kv: a required pointer is NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+        return fail(PA_ERR_ALIGN, "pa_write_kv: caches and new K/V must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int64_t> slots;
+        if ((st = fetch(slots, slot_mapping, num_tokens, s))) return st;
+        const int64_t limit = c->num_blocks * c->block_size;
+        std::unordered_set<int64_t> seen;
+        for (int32_t t = 0; t < num_tokens; ++t) {
+            const int64_t v = slots[t];
+            if (v < 0) continue;
+            if (v >= limit) return fail(PA_ERR_VALIDATE, "slot_mapping[%d] = %lld >= %lld", t, (long long)v, (long long)limit);
+            if (!seen.insert(v).second) return fail(PA_ERR_VALIDATE, "slot %lld written twice", (long long)v);
+        }
+    }
+    if ((st = launch_write_kv(c, k_cache, v_cache, k_new, v_new, slot_mapping, num_tokens, s))) return st;
+    return ok();
+}
+
+int pa_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                   const int64_t* block_pairs, int32_t num_pairs, void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if (num_pairs < 0) return fail(PA_ERR_SHAPE, "num_pairs %d < 0", num_pairs);
+    if (num_pairs == 0) return ok();
+    if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_NULL, "pa_copy_blocks: a required pointer is NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_ALIGN, "pa_copy_blocks: caches must be 16-byte aligned");
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int64_t> pairs;
+        if ((st = fetch(pairs, block_pairs, 2 * static_cast<size_t>(num_pairs), s))) return st;
+        std::unordered_set<int64_t> dsts, srcs;
+        for (int32_t i = 0; i < num_pairs; ++i) {
+            const int64_t a = pairs[2 * i], b = pairs[2 * i + 1];
+            if (a < 0 || a >= c->num_blocks || b < 0 || b >= c->num_blocks)
+                return fail(PA_ERR_VALIDATE, "pair %d = (%lld, %lld) outside [0, %lld)", i, (long long)a, (long long)b, (long long)c->num_blocks);
+            if (!dsts.insert(b).second) return fail(PA_ERR_VALIDATE, "block %lld is the destination of two pairs", (long long)b);
+            srcs.insert(a);
+        }
+        for (int64_t b : dsts)
+            if (srcs.count(b)) return fail(PA_ERR_VALIDATE, "block %lld is both a source and a destination", (long long)b);
+    }
+    if ((st = launch_copy_blocks(c, k_cache, v_cache, block_pairs, num_pairs, s))) return st;
+    return ok();
+}
+
+int pa_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,
+                    int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                    const int32_t* positions, int32_t num_tokens, int64_t* slot_mapping,
+                    void* stream) {
+    if (block_size < 1) return fail(PA_ERR_SHAPE, "block_size %d < 1", block_size);
+    if (num_seqs < 0 || max_blocks_per_seq < 1 || num_tokens < 0)
+        return fail(PA_ERR_SHAPE, "pa_slot_mapping: need num_seqs >= 0, max_blocks_per_seq >= 1, num_tokens >= 0");
+    if (num_tokens == 0) return ok();
+    if (!positions || !slot_mapping || (num_seqs > 0 && !block_tables))
+        return fail(PA_ERR_NULL, "pa_slot_mapping: a required pointer is NULL");
+    int st = launch_slot_mapping(block_size, block_tables, num_seqs, max_blocks_per_seq, seq_ids,
+                                 positions, num_tokens, slot_mapping, as_stream(stream));
+    return st ? st : ok();
+}
+
+int pa_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, int32_t context_len, void* k_out, void* v_out,
+                 void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if (context_len < 0) return fail(PA_ERR_SHAPE, "context_len %d < 0", context_len);
+    if (context_len == 0) return ok();
+    if (!k_cache || !v_cache || !block_table || !k_out || !v_out)
+        return fail(PA_ERR_NULL, "pa_gather_kv: a required pointer is NULL");
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int32_t> table;
+        const size_t n = static_cast<size_t>((context_len + c->block_size - 1) / c->block_size);
+        if ((st = fetch(table, block_table, n, s))) return st;
+        for (size_t i = 0; i < n; ++i)
+            if (table[i] < 0 || table[i] >= c->num_blocks)
+                return fail(PA_ERR_VALIDATE, "block_table[%zu] = %d outside [0, %lld)", i, table[i], (long long)c->num_blocks);
+    }
+    if ((st = launch_gather_kv(c, k_cache, v_cache, block_table, context_len, k_out, v_out, s))) return st;
+    return ok();
+}
+
+int32_t pa_decode_partition_tokens(const pa_cache_desc_t* c, int32_t num_seqs,
+                                   int32_t num_q_heads, int32_t max_context_len) {
+    if (check_desc(c) || check_heads(c, num_seqs, num_q_heads)) return -1;
+    return plan_partition(c, num_seqs, num_q_heads, max_context_len);
+}
+
+size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
+                                 int32_t num_q_heads, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+    if (check_desc(c) || check_heads(c, num_seqs, num_q_heads)) return 0;
+    int32_t part = 0;
+    if (resolve_partition(c, num_seqs, num_q_heads, max_context_len, partition_tokens, &part)) return 0;
+    return workspace_bytes(c, num_seqs, num_q_heads, max_context_len, part);
+}
+
+int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+              const void* q, const int32_t* block_tables, const int32_t* context_lens,
+              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+              int32_t max_context_len, float scale, void* out, void* workspace,
+              size_t workspace_bytes_given, int32_t partition_tokens, void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d < 0", max_context_len);
+    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+        return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
+    if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+    if (num_seqs == 0) return ok();
+    if (!k_cache || !v_cache || !q || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "pa_decode: a required pointer is NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
+        return fail(PA_ERR_ALIGN, "pa_decode: caches, q and out must be 16-byte aligned");
+    int32_t part = 0;
+    if ((st = resolve_partition(c, num_seqs, num_q_heads, max_context_len, partition_tokens, &part))) return st;
+    const size_t need = workspace_bytes(c, num_seqs, num_q_heads, max_context_len, part);
+    if (need > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got NULL", need);
+        if (workspace_bytes_given < need)
+            return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got %zu", need, workspace_bytes_given);
+        if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int32_t> lens, tables;
+        if ((st = fetch(lens, context_lens, num_seqs, s))) return st;
+        if ((st = fetch(tables, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, s))) return st;
+        for (int32_t i = 0; i < num_seqs; ++i) {
+            const int32_t L = lens[i];
+            if (L < 0 || L > max_context_len)
+                return fail(PA_ERR_VALIDATE, "context_lens[%d] = %d outside [0, %d]", i, L, max_context_len);
+            const int32_t nb = (L + c->block_size - 1) / c->block_size;
+            for (int32_t j = 0; j < nb; ++j) {
+                const int32_t b = tables[static_cast<size_t>(i) * max_blocks_per_seq + j];
+                if (b < 0 || b >= c->num_blocks)
+                    return fail(PA_ERR_VALIDATE, "block_tables[%d][%d] = %d outside [0, %lld)", i, j, b, (long long)c->num_blocks);
+            }
+        }
+    }
+    const int64_t parts64 = std::max<int64_t>(1, ceil_div(max_context_len, part));
+    if (parts64 > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "max_context_len %d needs %lld partitions of %d tokens (> %d)",
+                    max_context_len, (long long)parts64, part, kMaxGridYZ);
+    const int32_t max_parts = static_cast<int32_t>(parts64);
+    DecodeArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.q = q;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = c->num_blocks;
+    a.block_size = c->block_size;
+    a.num_kv_heads = c->num_kv_heads;
+    a.head_dim = c->head_dim;
+    a.dtype = c->dtype;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / c->num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.len_clamp = max_context_len;
+    a.part_tokens = part;
+    a.max_parts = max_parts;
+    a.scale = scale;
+    a.out = out;
+    const size_t slots = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
+    float* ws = need ? static_cast<float*>(workspace) : nullptr;
+    a.ws_acc = ws;
+    a.ws_m = need ? ws + slots * c->head_dim : nullptr;
+    a.ws_l = need ? ws + slots * (c->head_dim + 1) : nullptr;
+    a.stream = s;
+    if ((st = launch_decode(a))) return st;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,184 @@
+// Cache-side kernels: KV-write scatter, copy-on-write block copy, address
+// translation (slot mapping) and the history gather used to test it.
+//
+// All of them move bits unchanged (no floating-point conversion), so a NaN
+// payload or a signed zero arrives exactly as it left.  Every index read
+// from device memory is range-checked before use; an out-of-range index
+// skips the element (or yields slot -1), so a contract violation cannot
+// reach outside the buffers.
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// ---- write: [KG] "Follow One Token Address" read backwards -----------------
+// One workgroup per new token.  K rows go out as 16-byte chunks of x
+// consecutive dims (the K layout keeps them contiguous); V is dim-major, so
+// each element is stored on its own.
+template <typename E>
+__global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
+                                                       E* __restrict__ v_cache,
+                                                       const E* __restrict__ k_new,
+                                                       const E* __restrict__ v_new,
+                                                       const int64_t* __restrict__ slots,
+                                                       int64_t num_slots, int block_size,
+                                                       int num_kv_heads, int head_dim) {
+    constexpr int X = 16 / sizeof(E);
+    const int t = blockIdx.x;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) return;
+    const int64_t b = slot / block_size;
+    const int o = static_cast<int>(slot - b * block_size);
+    const int chunks = head_dim / X;
+    const int64_t tile = static_cast<int64_t>(head_dim) * block_size;
+    const int64_t row = static_cast<int64_t>(t) * num_kv_heads * head_dim;
+
+    // K: (head, chunk) pairs, 16 bytes each.
+    for (int i = threadIdx.x; i < num_kv_heads * chunks; i += blockDim.x) {
+        const int h = i / chunks;
+        const int c = i - h * chunks;
+        const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
+        E* dst = k_cache + (b * num_kv_heads + h) * tile + (static_cast<int64_t>(c) * block_size + o) * X;
+        *reinterpret_cast<uint4*>(dst) = v;
+    }
+    // V: (head, dim) elements.
+    for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
+        const int h = i / head_dim;
+        const int d = i - h * head_dim;
+        v_cache[(b * num_kv_heads + h) * tile + static_cast<int64_t>(d) * block_size + o] =
+            v_new[row + i];
+    }
+}
+
+// ---- copy: [ZQ] answer, [KG] "Shared Blocks Must Not Be Changed in Place" --
+// grid.x is the pair, grid.y covers one block's bytes in 4 KiB pieces (256
+// lanes x 16 bytes); K and V are copied by the same lanes.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache,
+                                                          uint4* __restrict__ v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t num_blocks,
+                                                          int64_t vecs_per_block) {
+    const int64_t src = pairs[2 * static_cast<int64_t>(blockIdx.x)];
+    const int64_t dst = pairs[2 * static_cast<int64_t>(blockIdx.x) + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+    const int64_t i = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
+    if (i >= vecs_per_block) return;
+    const uint4 kv = k_cache[src * vecs_per_block + i];
+    const uint4 vv = v_cache[src * vecs_per_block + i];
+    k_cache[dst * vecs_per_block + i] = kv;
+    v_cache[dst * vecs_per_block + i] = vv;
+}
+
+// ---- translate: [KG] "Follow One Token Address" ----------------------------
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    int block_size, const int32_t* __restrict__ block_tables, int num_seqs,
+    int max_blocks_per_seq, const int32_t* __restrict__ seq_ids,
+    const int32_t* __restrict__ positions, int num_tokens, int64_t* __restrict__ slots) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= num_tokens) return;
+    const int s = seq_ids ? seq_ids[t] : t;
+    const int p = positions[t];
+    int64_t slot = -1;
+    if (p >= 0 && s >= 0 && s < num_seqs) {
+        const int logical = p / block_size;
+        if (logical < max_blocks_per_seq) {
+            const int phys = block_tables[static_cast<int64_t>(s) * max_blocks_per_seq + logical];
+            if (phys >= 0) slot = static_cast<int64_t>(phys) * block_size + (p - logical * block_size);
+        }
+    }
+    slots[t] = slot;
+}
+
+// ---- gather: [KG] "Batching Becomes More Flexible" -------------------------
+// One thread per (token, head, dim) element of the contiguous output.
+template <typename E>
+__global__ __launch_bounds__(256) void gather_kv_kernel(const E* __restrict__ k_cache,
+                                                        const E* __restrict__ v_cache,
+                                                        const int32_t* __restrict__ table,
+                                                        int64_t num_blocks, int block_size,
+                                                        int num_kv_heads, int head_dim,
+                                                        int64_t total, E* __restrict__ k_out,
+                                                        E* __restrict__ v_out) {
+    constexpr int X = 16 / sizeof(E);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int d = static_cast<int>(i % head_dim);
+    const int64_t th = i / head_dim;
+    const int h = static_cast<int>(th % num_kv_heads);
+    const int t = static_cast<int>(th / num_kv_heads);
+    const int lb = t / block_size;
+    const int o = t - lb * block_size;
+    int phys = table[lb];
+    if (phys < 0 || phys >= num_blocks) phys = 0;
+    const int64_t tile = (static_cast<int64_t>(phys) * num_kv_heads + h) * head_dim * block_size;
+    k_out[i] = k_cache[tile + (static_cast<int64_t>(d / X) * block_size + o) * X + d % X];
+    v_out[i] = v_cache[tile + static_cast<int64_t>(d) * block_size + o];
+}
+
+}  // namespace
+
+int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                    const void* v_new, const int64_t* slots, int32_t num_tokens,
+                    hipStream_t stream) {
+    if (num_tokens == 0) return PA_OK;
+    const int64_t num_slots = c->num_blocks * c->block_size;
+    if (c->dtype == PA_BF16) {
+        hipLaunchKernelGGL(write_kv_kernel<uint16_t>, dim3(num_tokens), dim3(256), 0, stream,
+                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                           slots, num_slots, c->block_size, c->num_kv_heads, c->head_dim);
+    } else {
+        hipLaunchKernelGGL(write_kv_kernel<uint32_t>, dim3(num_tokens), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                           static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                           slots, num_slots, c->block_size, c->num_kv_heads, c->head_dim);
+    }
+    return check_launch("write_kv");
+}
+
+int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                       const int64_t* pairs, int32_t num_pairs, hipStream_t stream) {
+    if (num_pairs == 0) return PA_OK;
+    const int64_t bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim *
+                          elem_bytes(c->dtype);
+    const int64_t vecs = bytes / 16;
+    const int64_t gy = (vecs + 255) / 256;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, static_cast<unsigned>(gy)), dim3(256),
+                       0, stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                       pairs, c->num_blocks, vecs);
+    return check_launch("copy_blocks");
+}
+
+int launch_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                        const int32_t* positions, int32_t num_tokens, int64_t* slots,
+                        hipStream_t stream) {
+    if (num_tokens == 0) return PA_OK;
+    hipLaunchKernelGGL(slot_mapping_kernel, dim3((num_tokens + 255) / 256), dim3(256), 0, stream,
+                       block_size, block_tables, num_seqs, max_blocks_per_seq, seq_ids, positions,
+                       num_tokens, slots);
+    return check_launch("slot_mapping");
+}
+
+int launch_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t context_len, void* k_out, void* v_out,
+                     hipStream_t stream) {
+    if (context_len == 0) return PA_OK;
+    const int64_t total = static_cast<int64_t>(context_len) * c->num_kv_heads * c->head_dim;
+    const unsigned grid = static_cast<unsigned>((total + 255) / 256);
+    if (c->dtype == PA_BF16) {
+        hipLaunchKernelGGL(gather_kv_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+                           block_table, c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim,
+                           total, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
+    } else {
+        hipLaunchKernelGGL(gather_kv_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
+                           static_cast<const uint32_t*>(k_cache), static_cast<const uint32_t*>(v_cache),
+                           block_table, c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim,
+                           total, static_cast<uint32_t*>(k_out), static_cast<uint32_t*>(v_out));
+    }
+    return check_launch("gather_kv");
+}
+
+}  // namespace pa

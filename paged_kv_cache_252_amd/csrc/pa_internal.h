@@ -1,0 +1,93 @@
+// Internal declarations shared by the libpagedkv translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "pa.h"
+
+namespace pa {
+
+// ---- error reporting ------------------------------------------------------
+
+// Records a printf-style message for pa_last_error() and returns `status`.
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Clears the thread's last error and returns PA_OK.
+int ok();
+
+// Maps the runtime's last launch error (if any) to PA_ERR_HIP.
+int check_launch(const char* what);
+
+// True when PA_VALIDATE=1 is set: index arrays are checked on the host.
+bool validate_enabled();
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int elem_bytes(int dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+// Checks the descriptor itself: dtype, sizes, supported head_dim.
+int check_desc(const pa_cache_desc_t* c);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---- decode planning --------------------------------------------------------
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// The fast MFMA kernel handles this shape.
+inline bool fast_path_ok(const pa_cache_desc_t* c, int group) {
+    return c->dtype == PA_BF16 && c->head_dim == 128 && c->block_size == 16 && group >= 1 &&
+           group <= 16;
+}
+
+// ---- kernel launchers (defined in the .hip files) --------------------------
+
+struct DecodeArgs {
+    const void* k_cache;
+    const void* v_cache;
+    const void* q;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    int64_t num_blocks;
+    int32_t block_size;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t group;
+    int32_t max_blocks_per_seq;
+    int32_t len_clamp;       // min(max_context_len, max_blocks_per_seq * block_size)
+    int32_t part_tokens;
+    int32_t max_parts;
+    float scale;
+    void* out;
+    float* ws_acc;           // [S][Hq][max_parts][D]
+    float* ws_m;             // [S][Hq][max_parts]  (log2 domain running max)
+    float* ws_l;             // [S][Hq][max_parts]
+    hipStream_t stream;
+};
+
+int launch_decode(const DecodeArgs& a);
+
+int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                    const void* v_new, const int64_t* slots, int32_t num_tokens,
+                    hipStream_t stream);
+
+int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                       const int64_t* pairs, int32_t num_pairs, hipStream_t stream);
+
+int launch_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, const int32_t* seq_ids,
+                        const int32_t* positions, int32_t num_tokens, int64_t* slots,
+                        hipStream_t stream);
+
+int launch_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+                     const int32_t* block_table, int32_t context_len, void* k_out, void* v_out,
+                     hipStream_t stream);
+
+}  // namespace pa
