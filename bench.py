@@ -185,6 +185,8 @@ def main() -> int:
     ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(w.q) for _ in tables]
+    # no block is shared between requests in this batch: let decode stream K/V
+    stream_kv = w.shared_blocks is None
     log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
         f"workspace {ws_bytes} B, {reps} replicas")
 
@@ -193,7 +195,7 @@ def main() -> int:
             ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
         ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots[r])
         ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
-                   out=outs[r], workspace=workspace, partition_tokens=part)
+                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv)
 
     for i in range(args.warmup):
         step(i % reps)
@@ -224,7 +226,7 @@ def main() -> int:
     for i in range(args.kernel_iters):
         r = i % reps
         ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
-                   out=outs[r], workspace=workspace, partition_tokens=part)
+                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv)
     ev1.record(stream)
     ev1.synchronize()
     dec_us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
@@ -248,7 +250,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg["desc"], "name": args.workload, "requests": w.num_seqs,
                    "max_context_len": max_len, "total_context_tokens": int(w.context_lens.sum()),
-                   "replicas": reps, "partition_tokens": part},
+                   "replicas": reps, "partition_tokens": part, "stream_kv": stream_kv,
+                   "kv_layout": "one buffer [block][K|V], block_stride 2 blocks"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
         "kv_gbs_logical": round((db["logical"] + step_extra_bytes(w)) / (ms * 1e-3) / 1e9, 2),

@@ -21,8 +21,13 @@ namespace {
 thread_local std::string g_last_error;
 
 constexpr int kMaxPartitionTokens = 1024;   // fast path: one table entry per lane of a wave
-constexpr int kMinAutoPartitionTokens = 256;
-constexpr int kWavesPerCu = 8;              // decode waves the plan aims to keep resident per CU
+constexpr int kMinAutoPartitionTokens = 64;
+// Partition plan: the longest partitions (fewest partials to merge, least
+// per-wave set-up) that still give about this many waves per CU when every
+// request is as long as the longest.  Measured on MI355X: 1024-token
+// partitions beat 256-512 on the GQA, long-context and shared-prefix
+// workloads, where even at 1024 there are >= 2 waves per CU.
+constexpr int kWavesPerCu = 2;
 constexpr int kMaxGridYZ = 65535;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -65,6 +70,14 @@ int check_desc(const pa_cache_desc_t* c) {
     switch (c->head_dim) {
         case 16: case 32: case 64: case 128: case 256: break;
         default: return fail(PA_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128, 256}", c->head_dim);
+    }
+    if (c->block_stride != 0) {
+        if (c->block_stride < block_elems(c))
+            return fail(PA_ERR_SHAPE, "block_stride %lld is smaller than one block (%lld elements)",
+                        (long long)c->block_stride, (long long)block_elems(c));
+        if ((c->block_stride * elem_bytes(c->dtype)) % 16 != 0)
+            return fail(PA_ERR_ALIGN, "block_stride %lld elements is not a multiple of 16 bytes",
+                        (long long)c->block_stride);
     }
     return PA_OK;
 }
@@ -289,7 +302,8 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
               const void* q, const int32_t* block_tables, const int32_t* context_lens,
               int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
               int32_t max_context_len, float scale, void* out, void* workspace,
-              size_t workspace_bytes_given, int32_t partition_tokens, void* stream) {
+              size_t workspace_bytes_given, int32_t partition_tokens, uint32_t flags,
+              void* stream) {
     int st = check_desc(c);
     if (st) return st;
     if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
@@ -299,6 +313,7 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
         return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
                     max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
     if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+    if (flags & ~PA_DECODE_STREAM_KV) return fail(PA_ERR_UNSUPPORTED, "unknown decode flags 0x%x", flags);
     if (num_seqs == 0) return ok();
     if (!k_cache || !v_cache || !q || !block_tables || !context_lens || !out)
         return fail(PA_ERR_NULL, "pa_decode: a required pointer is NULL");
@@ -342,6 +357,7 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.num_blocks = c->num_blocks;
+    a.block_stride = block_stride(c);
     a.block_size = c->block_size;
     a.num_kv_heads = c->num_kv_heads;
     a.head_dim = c->head_dim;
@@ -354,6 +370,7 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
     a.part_tokens = part;
     a.max_parts = max_parts;
     a.scale = scale;
+    a.flags = flags;
     a.out = out;
     const size_t slots = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
     float* ws = need ? static_cast<float*>(workspace) : nullptr;

@@ -22,8 +22,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
                                                        const E* __restrict__ k_new,
                                                        const E* __restrict__ v_new,
                                                        const int64_t* __restrict__ slots,
-                                                       int64_t num_slots, int block_size,
-                                                       int num_kv_heads, int head_dim) {
+                                                       int64_t num_slots, int64_t blk_stride,
+                                                       int block_size, int num_kv_heads,
+                                                       int head_dim) {
     constexpr int X = 16 / sizeof(E);
     const int t = blockIdx.x;
     const int64_t slot = slots[t];
@@ -39,14 +40,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
         const int h = i / chunks;
         const int c = i - h * chunks;
         const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
-        E* dst = k_cache + (b * num_kv_heads + h) * tile + (static_cast<int64_t>(c) * block_size + o) * X;
+        E* dst = k_cache + b * blk_stride + h * tile + (static_cast<int64_t>(c) * block_size + o) * X;
         *reinterpret_cast<uint4*>(dst) = v;
     }
     // V: (head, dim) elements.
     for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
         const int h = i / head_dim;
         const int d = i - h * head_dim;
-        v_cache[(b * num_kv_heads + h) * tile + static_cast<int64_t>(d) * block_size + o] =
+        v_cache[b * blk_stride + h * tile + static_cast<int64_t>(d) * block_size + o] =
             v_new[row + i];
     }
 }
@@ -58,16 +59,17 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
                                                           uint4* __restrict__ v_cache,
                                                           const int64_t* __restrict__ pairs,
                                                           int64_t num_blocks,
-                                                          int64_t vecs_per_block) {
+                                                          int64_t vecs_per_block,
+                                                          int64_t vecs_stride) {
     const int64_t src = pairs[2 * static_cast<int64_t>(blockIdx.x)];
     const int64_t dst = pairs[2 * static_cast<int64_t>(blockIdx.x) + 1];
     if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
     const int64_t i = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
     if (i >= vecs_per_block) return;
-    const uint4 kv = k_cache[src * vecs_per_block + i];
-    const uint4 vv = v_cache[src * vecs_per_block + i];
-    k_cache[dst * vecs_per_block + i] = kv;
-    v_cache[dst * vecs_per_block + i] = vv;
+    const uint4 kv = k_cache[src * vecs_stride + i];
+    const uint4 vv = v_cache[src * vecs_stride + i];
+    k_cache[dst * vecs_stride + i] = kv;
+    v_cache[dst * vecs_stride + i] = vv;
 }
 
 // ---- translate: [KG] "Follow One Token Address" ----------------------------
@@ -96,8 +98,9 @@ template <typename E>
 __global__ __launch_bounds__(256) void gather_kv_kernel(const E* __restrict__ k_cache,
                                                         const E* __restrict__ v_cache,
                                                         const int32_t* __restrict__ table,
-                                                        int64_t num_blocks, int block_size,
-                                                        int num_kv_heads, int head_dim,
+                                                        int64_t num_blocks, int64_t blk_stride,
+                                                        int block_size, int num_kv_heads,
+                                                        int head_dim,
                                                         int64_t total, E* __restrict__ k_out,
                                                         E* __restrict__ v_out) {
     constexpr int X = 16 / sizeof(E);
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const E* __restrict__ k_
     const int o = t - lb * block_size;
     int phys = table[lb];
     if (phys < 0 || phys >= num_blocks) phys = 0;
-    const int64_t tile = (static_cast<int64_t>(phys) * num_kv_heads + h) * head_dim * block_size;
+    const int64_t tile = static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * head_dim * block_size;
     k_out[i] = k_cache[tile + (static_cast<int64_t>(d / X) * block_size + o) * X + d % X];
     v_out[i] = v_cache[tile + static_cast<int64_t>(d) * block_size + o];
 }
@@ -127,12 +130,14 @@ int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, cons
         hipLaunchKernelGGL(write_kv_kernel<uint16_t>, dim3(num_tokens), dim3(256), 0, stream,
                            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                            static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                           slots, num_slots, c->block_size, c->num_kv_heads, c->head_dim);
+                           slots, num_slots, block_stride(c), c->block_size, c->num_kv_heads,
+                           c->head_dim);
     } else {
         hipLaunchKernelGGL(write_kv_kernel<uint32_t>, dim3(num_tokens), dim3(256), 0, stream,
                            static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
                            static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
-                           slots, num_slots, c->block_size, c->num_kv_heads, c->head_dim);
+                           slots, num_slots, block_stride(c), c->block_size, c->num_kv_heads,
+                           c->head_dim);
     }
     return check_launch("write_kv");
 }
@@ -140,13 +145,12 @@ int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, cons
 int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
                        const int64_t* pairs, int32_t num_pairs, hipStream_t stream) {
     if (num_pairs == 0) return PA_OK;
-    const int64_t bytes = static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim *
-                          elem_bytes(c->dtype);
-    const int64_t vecs = bytes / 16;
+    const int64_t vecs = block_elems(c) * elem_bytes(c->dtype) / 16;
+    const int64_t vstride = block_stride(c) * elem_bytes(c->dtype) / 16;
     const int64_t gy = (vecs + 255) / 256;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, static_cast<unsigned>(gy)), dim3(256),
                        0, stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
-                       pairs, c->num_blocks, vecs);
+                       pairs, c->num_blocks, vecs, vstride);
     return check_launch("copy_blocks");
 }
 
@@ -170,12 +174,14 @@ int launch_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* 
     if (c->dtype == PA_BF16) {
         hipLaunchKernelGGL(gather_kv_kernel<uint16_t>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
-                           block_table, c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim,
+                           block_table, c->num_blocks, block_stride(c), c->block_size,
+                           c->num_kv_heads, c->head_dim,
                            total, static_cast<uint16_t*>(k_out), static_cast<uint16_t*>(v_out));
     } else {
         hipLaunchKernelGGL(gather_kv_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream,
                            static_cast<const uint32_t*>(k_cache), static_cast<const uint32_t*>(v_cache),
-                           block_table, c->num_blocks, c->block_size, c->num_kv_heads, c->head_dim,
+                           block_table, c->num_blocks, block_stride(c), c->block_size,
+                           c->num_kv_heads, c->head_dim,
                            total, static_cast<uint32_t*>(k_out), static_cast<uint32_t*>(v_out));
     }
     return check_launch("gather_kv");

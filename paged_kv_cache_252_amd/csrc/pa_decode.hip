@@ -78,7 +78,7 @@ __device__ __forceinline__ int clamp_block(int e, int64_t num_blocks) {
 // ============================================================================
 
 #ifndef PA_FAST_NBUF
-#define PA_FAST_NBUF 3           // tiles in the load ring of the fast path
+#define PA_FAST_NBUF 2           // tiles in the load ring of the fast path
 #endif
 
 
@@ -91,14 +91,22 @@ struct Tile {
     s16x4 v[8];    // V: dim 16*j + l%16, tokens 4*(l/16)..+3 -> A operand of PV j
 };
 
+// NT: non-temporal loads (streaming hint), for batches without shared blocks.
+template <bool NT, typename V>
+__device__ __forceinline__ V load16(const V* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
 __device__ __forceinline__ void load_tile(Tile& t, const __bf16* __restrict__ k_tile,
                                           const __bf16* __restrict__ v_tile, int lane) {
     const bf16x8* kp = reinterpret_cast<const bf16x8*>(k_tile) + lane;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) t.k[s] = kp[64 * s];
+    for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + 64 * s);
     const s16x4* vp = reinterpret_cast<const s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t.v[j] = vp[64 * j];
+    for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 64 * j);
 }
 
 struct SoftmaxState {
@@ -179,11 +187,11 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
-template <int NBUF>
+template <int NBUF, bool NT>
 __global__ __launch_bounds__(64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int64_t num_blocks, int num_kv_heads,
+    const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
     int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
     int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l) {
@@ -238,7 +246,6 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
 
     const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
     const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
-    const int64_t blk_stride = static_cast<int64_t>(num_kv_heads) * FTILE;
 
     SoftmaxState st;
     st.m = -INFINITY;
@@ -261,7 +268,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) {
         const int64_t o = tile_off(u);
-        load_tile(buf[u], k_head + o, v_head + o, lane);
+        load_tile<NT>(buf[u], k_head + o, v_head + o, lane);
     }
     for (int j0 = 0; j0 < nblk; j0 += NBUF) {
 #pragma unroll
@@ -269,7 +276,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
             const int j = j0 + u;
             {
                 const int64_t o = tile_off(j + NBUF - 1);
-                load_tile(buf[(u + NBUF - 1) % NBUF], k_head + o, v_head + o, lane);
+                load_tile<NT>(buf[(u + NBUF - 1) % NBUF], k_head + o, v_head + o, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (j < nblk)
@@ -311,7 +318,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_generic_kernel(
     const T* __restrict__ k_cache, const T* __restrict__ v_cache, const T* __restrict__ q,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int64_t num_blocks, int block_size, int num_kv_heads, int num_q_heads, int group,
+    int64_t num_blocks, int64_t blk_stride, int block_size, int num_q_heads, int group,
     int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts, float scale_log2,
     T* __restrict__ out, float* __restrict__ ws_acc, float* __restrict__ ws_m,
     float* __restrict__ ws_l) {
@@ -350,7 +357,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
         const int lb = t / block_size;
         const int o = t - lb * block_size;
         const int phys = clamp_block(table[lb], num_blocks);
-        const int64_t base = (static_cast<int64_t>(phys) * num_kv_heads + h) * tile;
+        const int64_t base = static_cast<int64_t>(phys) * blk_stride + h * tile;
         float kd[DPL], vd[DPL];
         float dot = 0.f;
 #pragma unroll
@@ -474,7 +481,7 @@ int launch_generic(const DecodeArgs& a) {
     hipLaunchKernelGGL((decode_generic_kernel<T, D>), grid, dim3(64), 0, a.stream,
                        static_cast<const T*>(a.k_cache), static_cast<const T*>(a.v_cache),
                        static_cast<const T*>(a.q), a.block_tables, a.context_lens, a.num_blocks,
-                       a.block_size, a.num_kv_heads, a.num_q_heads, a.group,
+                       a.block_stride, a.block_size, a.num_q_heads, a.group,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
                        static_cast<T*>(a.out), a.ws_acc, a.ws_m, a.ws_l);
     int st = check_launch("decode (generic)");
@@ -497,13 +504,14 @@ int launch_generic_d(const DecodeArgs& a) {
     }
 }
 
+template <bool NT>
 int launch_fast(const DecodeArgs& a) {
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL(decode_fast_kernel<PA_FAST_NBUF>, grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
-                       a.num_blocks, a.num_kv_heads, a.num_q_heads, a.group,
+                       a.num_blocks, a.block_stride, a.num_q_heads, a.group,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
                        static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l);
     int st = check_launch("decode (fast)");
@@ -517,8 +525,9 @@ int launch_fast(const DecodeArgs& a) {
 }  // namespace
 
 int launch_decode(const DecodeArgs& a) {
-    pa_cache_desc_t c{a.num_blocks, a.block_size, a.num_kv_heads, a.head_dim, a.dtype};
-    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0) return launch_fast(a);
+    pa_cache_desc_t c{a.num_blocks, a.block_size, a.num_kv_heads, a.head_dim, a.dtype, a.block_stride};
+    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0)
+        return (a.flags & PA_DECODE_STREAM_KV) ? launch_fast<true>(a) : launch_fast<false>(a);
     if (a.dtype == PA_BF16) return launch_generic_d<uint16_t>(a);
     return launch_generic_d<float>(a);
 }

@@ -33,6 +33,16 @@ int check_desc(const pa_cache_desc_t* c);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Elements of one block's K (or V) data: Hkv * block_size * head_dim.
+inline int64_t block_elems(const pa_cache_desc_t* c) {
+    return static_cast<int64_t>(c->num_kv_heads) * c->block_size * c->head_dim;
+}
+
+// Elements from one block to the next (the descriptor's stride, or dense).
+inline int64_t block_stride(const pa_cache_desc_t* c) {
+    return c->block_stride ? c->block_stride : block_elems(c);
+}
+
 // ---- decode planning --------------------------------------------------------
 
 // Compute units of the current device (cached per device).
@@ -53,6 +63,7 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     int64_t num_blocks;
+    int64_t block_stride;    // elements between consecutive blocks of k_cache / v_cache
     int32_t block_size;
     int32_t num_kv_heads;
     int32_t head_dim;
@@ -65,6 +76,7 @@ struct DecodeArgs {
     int32_t part_tokens;
     int32_t max_parts;
     float scale;
+    uint32_t flags;
     void* out;
     float* ws_acc;           // [S][Hq][max_parts][D]
     float* ws_m;             // [S][Hq][max_parts]  (log2 domain running max)

@@ -20,6 +20,10 @@ Recipe (all workloads):
 * Blocks that no table references are filled with quiet NaN when
   ``poison=True`` (so reading one shows up in the output) and zeros
   otherwise.  Table entries past a request's last block are -1.
+* K and V live in one buffer ``[num_blocks, 2, Hkv * block_size * head_dim]``
+  (the library's recommended allocation); ``k_cache`` and ``v_cache`` are
+  its ``[:, 0]`` and ``[:, 1]`` views.  ``separate_pools`` converts a
+  workload to two dense buffers instead.
 
 Named presets follow the five workload descriptions of the paged decode
 benchmark: a tiny fp32 example built around the worked block table
@@ -54,8 +58,8 @@ class Workload:
     context_lens: torch.Tensor      # int32 [S]
     block_tables: torch.Tensor      # int32 [S][max_blocks]; -1 past the last block
     q: torch.Tensor                 # [S][Hq][D]
-    k_cache: torch.Tensor           # [num_blocks][Hkv * block_size * head_dim]
-    v_cache: torch.Tensor           # [num_blocks][Hkv * block_size * head_dim]
+    k_cache: torch.Tensor           # [num_blocks][Hkv * block_size * head_dim] (view)
+    v_cache: torch.Tensor           # [num_blocks][Hkv * block_size * head_dim] (view)
     # the token each request writes this step (fan-out step and benchmark step)
     new_k: torch.Tensor | None = None        # [T][Hkv][D]
     new_v: torch.Tensor | None = None        # [T][Hkv][D]
@@ -108,16 +112,12 @@ def _values(gen: torch.Generator, shape, dtype: str, device) -> torch.Tensor:
     return x.to(TORCH_DTYPE[dtype])
 
 
-def _fill_pool(num_blocks: int, block_elems: int, blocks: np.ndarray, gen, dtype: str, device,
-               poison: bool, chunk: int = 4096):
-    """Pool with N(0,1) values in ``blocks`` (in the given order) and NaN/0 elsewhere."""
-    fill = float("nan") if poison else 0.0
-    pool = torch.full((num_blocks, block_elems), fill, dtype=TORCH_DTYPE[dtype], device=device)
-    ids = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device=device)
+def _fill_pool(pool: torch.Tensor, blocks: np.ndarray, gen, dtype: str, chunk: int = 4096):
+    """N(0,1) values into ``pool`` rows ``blocks`` (in the given order)."""
+    ids = torch.as_tensor(np.asarray(blocks, dtype=np.int64), device=pool.device)
     for lo in range(0, len(blocks), chunk):
         sel = ids[lo:lo + chunk]
-        pool[sel] = _values(gen, (sel.numel(), block_elems), dtype, device)
-    return pool
+        pool[sel] = _values(gen, (sel.numel(), pool.shape[1]), dtype, pool.device)
 
 
 def _finish(name, dtype, bs, hq, hkv, d, num_blocks, lens, tables, max_blocks, seed, device,
@@ -128,8 +128,11 @@ def _finish(name, dtype, bs, hq, hkv, d, num_blocks, lens, tables, max_blocks, s
     s = len(lens)
     q = _values(gen, (s, hq, d), dtype, dev)
     elems = hkv * bs * d
-    k_cache = _fill_pool(num_blocks, elems, value_blocks, gen, dtype, dev, poison)
-    v_cache = _fill_pool(num_blocks, elems, value_blocks, gen, dtype, dev, poison)
+    buf = torch.full((num_blocks, 2, elems), float("nan") if poison else 0.0,
+                     dtype=TORCH_DTYPE[dtype], device=dev)
+    k_cache, v_cache = buf[:, 0], buf[:, 1]
+    _fill_pool(k_cache, value_blocks, gen, dtype)
+    _fill_pool(v_cache, value_blocks, gen, dtype)
     return Workload(
         name=name, dtype=dtype, block_size=bs, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
         num_blocks=num_blocks, scale=(1.0 / math.sqrt(d)) if scale is None else scale,
@@ -291,6 +294,13 @@ def fanout(seed: int = 4, device="cpu", poison: bool = True, num_prompts: int = 
     w.parent_tables = parent_tables
     w.extra["prompt_lens"] = plens
     w.extra["branches"] = branches
+    return w
+
+
+def separate_pools(w: Workload) -> Workload:
+    """Move the caches into two dense buffers (block stride = one block)."""
+    w.k_cache = w.k_cache.contiguous()
+    w.v_cache = w.v_cache.contiguous()
     return w
 
 

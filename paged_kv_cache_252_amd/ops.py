@@ -7,8 +7,11 @@ with the library's message on a non-zero status.  All computation happens in
 the HIP kernels; if ``libpagedkv.so`` is missing, loading fails loudly (there
 is no CPU fallback).
 
-Cache tensors are ``[num_blocks, Hkv * block_size * head_dim]`` (any shape
-whose first dimension is the block), laid out as ``include/pa.h`` describes.
+Cache tensors are 2-D ``[num_blocks, Hkv * block_size * head_dim]`` views
+with unit stride inside a block and ``block_stride`` elements between blocks
+(``include/pa.h`` gives the layout).  ``kv_pool`` allocates the recommended
+form: one buffer ``[num_blocks, 2, block]`` whose ``[:, 0]`` and ``[:, 1]``
+views are the K and V caches.
 """
 
 from __future__ import annotations
@@ -25,6 +28,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pa.h")
 
 PA_F32, PA_BF16 = 0, 1
+PA_DECODE_STREAM_KV = 1
 _DTYPES = {"f32": (PA_F32, torch.float32), "bf16": (PA_BF16, torch.bfloat16)}
 
 
@@ -41,7 +45,7 @@ class PagedKVError(RuntimeError):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int64), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("block_stride", ctypes.c_int64)]
 
 
 @dataclass(frozen=True)
@@ -53,6 +57,7 @@ class CacheSpec:
     num_kv_heads: int
     head_dim: int
     dtype: str = "bf16"
+    block_stride: int = 0          # elements between blocks; 0 = dense
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -62,14 +67,37 @@ class CacheSpec:
     def block_elems(self) -> int:
         return self.num_kv_heads * self.block_size * self.head_dim
 
+    @property
+    def stride(self) -> int:
+        return self.block_stride or self.block_elems
+
     def desc(self) -> CacheDesc:
         return CacheDesc(self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim,
-                         _DTYPES[self.dtype][0])
+                         _DTYPES[self.dtype][0], self.block_stride)
 
     @staticmethod
     def of(w) -> "CacheSpec":
-        """The spec of a workload from ``inputs`` (anything with the same fields)."""
-        return CacheSpec(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
+        """The spec of a workload from ``inputs`` (anything with the same fields),
+        with the block stride read off its cache tensors."""
+        stride = int(w.k_cache.stride(0))
+        elems = w.num_kv_heads * w.block_size * w.head_dim
+        return CacheSpec(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype,
+                         0 if stride == elems else stride)
+
+
+def kv_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+            dtype: str = "bf16", device="cuda", fill=None):
+    """The recommended cache allocation: one buffer [num_blocks, 2, block] with
+    K and V of a block adjacent.  Returns (spec, k_cache, v_cache) where the
+    caches are [num_blocks, block] views into it."""
+    elems = num_kv_heads * block_size * head_dim
+    tdt = _DTYPES[dtype][1]
+    if fill is None:
+        buf = torch.empty((num_blocks, 2, elems), dtype=tdt, device=device)
+    else:
+        buf = torch.full((num_blocks, 2, elems), fill, dtype=tdt, device=device)
+    spec = CacheSpec(num_blocks, block_size, num_kv_heads, head_dim, dtype, 2 * elems)
+    return spec, buf[:, 0], buf[:, 1]
 
 
 _lib = None
@@ -87,7 +115,8 @@ _SIGNATURES = {
     "pa_decode_workspace_bytes": (ctypes.c_size_t,
                                   [ctypes.POINTER(CacheDesc), _I32, _I32, _I32, _I32]),
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _I32, _I32,
-                                 _I32, _I32, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32, _P]),
+                                 _I32, _I32, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
+                                 ctypes.c_uint32, _P]),
 }
 
 
@@ -140,26 +169,28 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device=None):
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, device=None, contiguous=True):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_contiguous():
+    if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _cache_pair(spec: CacheSpec, k_cache, v_cache):
-    _need(k_cache, "k_cache", spec.torch_dtype)
-    _need(v_cache, "v_cache", spec.torch_dtype, k_cache.device)
-    want = spec.num_blocks * spec.block_elems
-    if k_cache.numel() != want or v_cache.numel() != want:
-        raise ValueError(f"caches must hold num_blocks * Hkv * block_size * head_dim = {want} "
-                         "elements")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, spec.torch_dtype, k_cache.device, contiguous=False)
+        if t.dim() != 2 or tuple(t.shape) != (spec.num_blocks, spec.block_elems):
+            raise ValueError(f"{name} must be [num_blocks, Hkv * block_size * head_dim] = "
+                             f"{(spec.num_blocks, spec.block_elems)}, got {tuple(t.shape)}")
+        if t.stride(1) != 1 or (spec.num_blocks > 1 and t.stride(0) != spec.stride):
+            raise ValueError(f"{name} strides {t.stride()} do not match block_stride "
+                             f"{spec.stride}")
     return k_cache.device
 
 
@@ -254,12 +285,13 @@ def decode_workspace(spec: CacheSpec, num_seqs: int, num_q_heads: int, max_conte
 
 def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
            max_context_len: int, scale: float, out=None, workspace=None,
-           partition_tokens: int = 0):
+           partition_tokens: int = 0, stream_kv: bool = False):
     """``pa_decode``: attention of one query per request over its paged history.
 
     ``q`` is [num_seqs, Hq, head_dim]; returns ``out`` of the same shape and
     dtype.  ``workspace`` (>= ``decode_workspace_bytes``) is allocated here
-    when not given.
+    when not given.  ``stream_kv`` sets ``PA_DECODE_STREAM_KV``: a cache hint
+    for batches in which no block is read by two requests.
     """
     dev = _cache_pair(spec, k_cache, v_cache)
     _need(q, "q", spec.torch_dtype, dev)
@@ -285,5 +317,6 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
                                         _ptr(block_tables), _ptr(context_lens), s, hq,
                                         block_tables.shape[1], max_context_len, float(scale),
                                         _ptr(out), _ptr(workspace), ws_bytes,
-                                        partition_tokens, _stream(dev)))
+                                        partition_tokens,
+                                        PA_DECODE_STREAM_KV if stream_kv else 0, _stream(dev)))
     return out

@@ -29,7 +29,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ops.abi_version() == 1
+    assert ops.abi_version() == 2
     assert ops.status_string(0) == "PA_OK"
     assert ops.status_string(5) == "PA_ERR_UNSUPPORTED"
     assert ops.status_string(8) == "PA_ERR_VALIDATE"
@@ -37,16 +37,18 @@ def test_version_and_status_strings(lib):
 
 
 def _desc(**kw):
-    base = dict(num_blocks=64, block_size=16, num_kv_heads=8, head_dim=128, dtype=1)
+    base = dict(num_blocks=64, block_size=16, num_kv_heads=8, head_dim=128, dtype=1,
+                block_stride=0)
     base.update(kw)
     return ops.CacheDesc(**base)
 
 
 def _decode(lib, d, num_seqs=2, num_q_heads=32, max_blocks=4, max_len=64, ptr=1 << 20,
-            part=16, scale=0.1):
+            part=16, scale=0.1, flags=0):
     p = ctypes.c_void_p(ptr)
     return lib.pa_decode(ctypes.byref(d) if d is not None else None, p, p, p, p, p, num_seqs,
-                         num_q_heads, max_blocks, max_len, scale, p, p, 1 << 30, part, None)
+                         num_q_heads, max_blocks, max_len, scale, p, p, 1 << 30, part, flags,
+                         None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -56,6 +58,8 @@ def _decode(lib, d, num_seqs=2, num_q_heads=32, max_blocks=4, max_len=64, ptr=1 
     (dict(block_size=512), 5),
     (dict(head_dim=96), 5),
     (dict(num_kv_heads=0), 2),
+    (dict(block_stride=1000), 2),                 # smaller than one block (16384)
+    (dict(block_stride=16384 + 4), 4),            # not a multiple of 16 bytes
 ])
 def test_bad_descriptor_rejected(lib, kw, status):
     assert _decode(lib, _desc(**kw)) == status
@@ -71,9 +75,10 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, _desc(), part=24) == 2                      # not a multiple of 16
     assert _decode(lib, _desc(), part=2048) == 2                    # above 1024
     assert _decode(lib, _desc(), ptr=(1 << 20) + 8) == 4            # misaligned buffers
+    assert _decode(lib, _desc(), flags=2) == 5                      # unknown flag bit
     d = _desc()
     assert lib.pa_decode(ctypes.byref(d), None, None, None, None, None, 2, 32, 4, 64, 0.1, None,
-                         None, 0, 16, None) == 1
+                         None, 0, 16, 0, None) == 1
     assert "NULL" in ops.last_error()
     assert _decode(lib, _desc(), num_seqs=0) == 0                   # nothing to do
     assert ops.last_error() == ""
@@ -86,7 +91,7 @@ def test_workspace_size_rules(lib):
     # 4 partitions of 16 over 64 tokens: S * Hq * parts * (D + 2) floats
     assert lib.pa_decode_workspace_bytes(ctypes.byref(d), 4, 32, 64, 16) == 4 * 32 * 4 * 130 * 4
     p = ctypes.c_void_p(1 << 20)
-    st = lib.pa_decode(ctypes.byref(d), p, p, p, p, p, 4, 32, 4, 64, 0.1, p, p, 100, 16, None)
+    st = lib.pa_decode(ctypes.byref(d), p, p, p, p, p, 4, 32, 4, 64, 0.1, p, p, 100, 16, 0, None)
     assert st == 6 and "workspace" in ops.last_error()
 
 

@@ -178,6 +178,34 @@ def test_fast_path_groups_and_partitions(group, part):
     ref = oracle_decode(w)
     out = run_decode(w, partition_tokens=part)
     assert_close(w, out, ref, f"g={group} part={part}")
+    streamed = run_decode(w, partition_tokens=part, stream_kv=True)
+    assert same_bits(out, streamed)              # a cache hint: the same bits
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_separate_dense_pools(dtype):
+    """K and V in two dense buffers (block stride 0) instead of one combined buffer."""
+    say(f"separate dense K/V pools {dtype}")
+    w = inputs.paged_random("sep", 5, 1, 400, 8, 2, head_dim=128, block_size=16, dtype=dtype,
+                            num_blocks=200, seed=90, device=DEV)
+    poison_tails(w)
+    ref = oracle_decode(w)
+    combined = run_decode(w, partition_tokens=64).clone()
+    inputs.separate_pools(w)
+    assert ops.CacheSpec.of(w).block_stride == 0
+    out = run_decode(w, partition_tokens=64)
+    assert_close(w, out, ref, "separate pools")
+    assert same_bits(out, combined)
+    # cache ops on dense pools too
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    kr, vr = paged.write_kv(to_np(w.k_cache), to_np(w.v_cache), to_np(w.new_k), to_np(w.new_v),
+                            slots.cpu().numpy(), **oracle_args(w))
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    torch.cuda.synchronize()
+    assert to_np(w.k_cache).tobytes() == kr.tobytes()
+    assert to_np(w.v_cache).tobytes() == vr.tobytes()
 
 
 @pytest.mark.parametrize("dtype,d,bs,hq,hkv", [
@@ -232,12 +260,14 @@ def test_placement_invariance_bitwise():
     bt = w.block_tables.long()
     bt2 = torch.where(bt >= 0, perm[bt.clamp(min=0)], bt).to(torch.int32)
     spec = ops.CacheSpec.of(w)
+    spec2 = ops.CacheSpec(w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim, w.dtype)
     for part in (0, 64, 512):
-        a = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
-                       w.max_context_len, w.scale, partition_tokens=part)
-        b = ops.decode(spec, w.q, k2, v2, bt2, w.context_lens, w.max_context_len, w.scale,
-                       partition_tokens=part)
-        assert same_bits(a, b)
+        for stream_kv in (False, True):
+            a = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                           w.max_context_len, w.scale, partition_tokens=part, stream_kv=stream_kv)
+            b = ops.decode(spec2, w.q, k2, v2, bt2, w.context_lens, w.max_context_len, w.scale,
+                           partition_tokens=part)
+            assert same_bits(a, b)
     assert same_bits(base, run_decode(w))         # and repeatable
 
 
