@@ -152,6 +152,42 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
             "tokens_per_s": done / dt, "seconds": dt}
 
 
+def measured_traffic(workload: str, part: int, stream_kv: bool):
+    """HBM bytes per decode call from the committed counter summary, or None when
+    there is none for this workload or the decode source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if (digest != rec["source_sha256"] or rec["partition_tokens"] != part
+            or rec["stream_kv"] != stream_kv):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def copy_probe(dev, mib: int) -> float:
+    """Read+write GB/s of a plain device-to-device copy of ``mib`` MiB."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    e1.synchronize()
+    gbs = 2 * 3 * (mib << 20) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +198,9 @@ def main() -> int:
     ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=200)
+    ap.add_argument("--copy-probe-mib", type=int, default=1024,
+                    help="size of a plain device-to-device copy timed first, as context and "
+                         "as the known-size reference for traffic counters (0 = skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -171,6 +210,7 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    copy_gbs = copy_probe(dev, args.copy_probe_mib) if args.copy_probe_mib > 0 else None
     cfg = WORKLOADS[args.workload]
     log(f"generating {args.workload}")
     w = cfg["make"](device=dev, poison=False)
@@ -255,8 +295,10 @@ def main() -> int:
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
         "kv_gbs_logical": round((db["logical"] + step_extra_bytes(w)) / (ms * 1e-3) / 1e9, 2),
+        "copy_probe_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.workload, part, stream_kv),
                      "kernel": "pa_decode", "bytes_per_launch": db["unique"],
                      "avg_launch_us": round(dec_us, 3)},
     }
