@@ -4,8 +4,8 @@
 
 A step is one pass of the whole hot path over one batch of synthetic
 requests: copy-on-write block copies (only the fan-out workload has any),
-the KV write of each request's newest token through its slot, and decode
-attention over every request's paged history.  Inputs are resident in HBM
+then ``pa_decode_append``, which writes each request's newest token at its
+slot and runs decode attention over every request's paged history.  Inputs are resident in HBM
 before timing starts.  Steps cycle through R replicas of the batch placed
 at disjoint physical blocks, so the 256 MB Infinity Cache cannot hold the
 working set between steps (every replica holds the same bytes, so every
@@ -219,7 +219,9 @@ def main() -> int:
     spec = ops.CacheSpec.of(w)
     reps = args.replicas or cfg["replicas"]
     tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
-    slots = [ops.slot_mapping(w.block_size, t, w.new_pos, w.new_seq) for t in tables]
+    # every request appends one token at its last position, L-1
+    assert torch.equal(w.new_pos, w.context_lens - 1) and torch.equal(
+        w.new_seq, torch.arange(w.num_seqs, dtype=torch.int32, device=dev))
     max_len = w.max_context_len
     part = args.partition or ops.decode_partition_tokens(spec, w.num_seqs, w.num_q_heads, max_len)
     ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
@@ -231,11 +233,13 @@ def main() -> int:
         f"workspace {ws_bytes} B, {reps} replicas")
 
     def step(r: int) -> None:
+        # copy-on-write copies, then one call that appends each request's new
+        # token at position L-1 and attends (pa_decode_append)
         if w.cow_pairs is not None:
             ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
-        ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots[r])
-        ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
-                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv)
+        ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, tables[r],
+                          w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
+                          partition_tokens=part, stream_kv=stream_kv)
 
     for i in range(args.warmup):
         step(i % reps)

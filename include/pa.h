@@ -260,6 +260,36 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
               size_t workspace_bytes, int32_t partition_tokens, uint32_t flags,
               void* stream);
 
+/*
+ * pa_decode_append -- one decode step: append each request's newest token,
+ * then attend.
+ *
+ * Same result as pa_write_kv of k_new[i] / v_new[i] at the slot of position
+ * context_lens[i] - 1 of request i (translated through block_tables as in
+ * pa_slot_mapping), followed by pa_decode with the same arguments: the new
+ * token is the query's own position, the last one it sees ([KG] "Follow One
+ * Token Address": the newest query attends to the history including itself;
+ * "Growth Needs Only Another Free Block": the engine has already given the
+ * request a block with room for it).  Requests with L = 0 append nothing.
+ * On the fast path one kernel does both: the wave of each request's last
+ * partition stores the token and uses it directly, so no separate write
+ * launch or read-back is needed.
+ *
+ * The block that receives the token must be private to the request (a
+ * shared block is first copied with pa_copy_blocks, [ZQ] answer; [KG]
+ * "Shared Blocks Must Not Be Changed in Place").
+ *
+ *   k_cache, v_cache  written at the appended slots
+ *   k_new, v_new      [num_seqs][Hkv][D], dtype c->dtype, 16-byte aligned
+ *   other arguments   as for pa_decode
+ */
+int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const void* q, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                     uint32_t flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

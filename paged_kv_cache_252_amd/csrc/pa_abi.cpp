@@ -169,6 +169,98 @@ int check_heads(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads)
 
 using namespace pa;
 
+static int decode_impl(const char* fn, const pa_cache_desc_t* c, const void* k_cache,
+                       const void* v_cache, const void* k_new, const void* v_new, const void* q,
+                       const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                       int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                       float scale, void* out, void* workspace, size_t workspace_bytes_given,
+                       int32_t partition_tokens, uint32_t flags, void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d < 0", max_context_len);
+    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+        return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
+    if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+    if (flags & ~PA_DECODE_STREAM_KV) return fail(PA_ERR_UNSUPPORTED, "unknown decode flags 0x%x", flags);
+    if (num_seqs == 0) return ok();
+    if (!k_cache || !v_cache || !q || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "%s: a required pointer is NULL", fn);
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
+        return fail(PA_ERR_ALIGN, "%s: caches, q and out must be 16-byte aligned", fn);
+    if (k_new != nullptr || v_new != nullptr) {
+        if (!k_new || !v_new) return fail(PA_ERR_NULL, "%s: k_new and v_new are both required", fn);
+        if (!aligned16(k_new) || !aligned16(v_new))
+            return fail(PA_ERR_ALIGN, "%s: k_new and v_new must be 16-byte aligned", fn);
+    }
+    int32_t part = 0;
+    if ((st = resolve_partition(c, num_seqs, num_q_heads, max_context_len, partition_tokens, &part))) return st;
+    const size_t need = workspace_bytes(c, num_seqs, num_q_heads, max_context_len, part);
+    if (need > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got NULL", need);
+        if (workspace_bytes_given < need)
+            return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got %zu", need, workspace_bytes_given);
+        if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int32_t> lens, tables;
+        if ((st = fetch(lens, context_lens, num_seqs, s))) return st;
+        if ((st = fetch(tables, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, s))) return st;
+        for (int32_t i = 0; i < num_seqs; ++i) {
+            const int32_t L = lens[i];
+            if (L < 0 || L > max_context_len)
+                return fail(PA_ERR_VALIDATE, "context_lens[%d] = %d outside [0, %d]", i, L, max_context_len);
+            const int32_t nb = (L + c->block_size - 1) / c->block_size;
+            for (int32_t j = 0; j < nb; ++j) {
+                const int32_t b = tables[static_cast<size_t>(i) * max_blocks_per_seq + j];
+                if (b < 0 || b >= c->num_blocks)
+                    return fail(PA_ERR_VALIDATE, "block_tables[%d][%d] = %d outside [0, %lld)", i, j, b, (long long)c->num_blocks);
+            }
+        }
+    }
+    const int64_t parts64 = std::max<int64_t>(1, ceil_div(max_context_len, part));
+    if (parts64 > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "max_context_len %d needs %lld partitions of %d tokens (> %d)",
+                    max_context_len, (long long)parts64, part, kMaxGridYZ);
+    const int32_t max_parts = static_cast<int32_t>(parts64);
+    DecodeArgs a;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.q = q;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = c->num_blocks;
+    a.block_stride = block_stride(c);
+    a.block_size = c->block_size;
+    a.num_kv_heads = c->num_kv_heads;
+    a.head_dim = c->head_dim;
+    a.dtype = c->dtype;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.group = num_q_heads / c->num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.len_clamp = max_context_len;
+    a.part_tokens = part;
+    a.max_parts = max_parts;
+    a.scale = scale;
+    a.flags = flags;
+    a.out = out;
+    const size_t slots = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
+    float* ws = need ? static_cast<float*>(workspace) : nullptr;
+    a.ws_acc = ws;
+    a.ws_m = need ? ws + slots * c->head_dim : nullptr;
+    a.ws_l = need ? ws + slots * (c->head_dim + 1) : nullptr;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.stream = s;
+    if ((st = launch_decode(a))) return st;
+    return ok();
+}
+
+
 extern "C" {
 
 int pa_abi_version(void) { return PA_ABI_VERSION; }
@@ -302,84 +394,23 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
               const void* q, const int32_t* block_tables, const int32_t* context_lens,
               int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
               int32_t max_context_len, float scale, void* out, void* workspace,
-              size_t workspace_bytes_given, int32_t partition_tokens, uint32_t flags,
-              void* stream) {
-    int st = check_desc(c);
-    if (st) return st;
-    if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
-    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
-    if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d < 0", max_context_len);
-    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
-        return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
-                    max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
-    if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-    if (flags & ~PA_DECODE_STREAM_KV) return fail(PA_ERR_UNSUPPORTED, "unknown decode flags 0x%x", flags);
-    if (num_seqs == 0) return ok();
-    if (!k_cache || !v_cache || !q || !block_tables || !context_lens || !out)
-        return fail(PA_ERR_NULL, "pa_decode: a required pointer is NULL");
-    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
-        return fail(PA_ERR_ALIGN, "pa_decode: caches, q and out must be 16-byte aligned");
-    int32_t part = 0;
-    if ((st = resolve_partition(c, num_seqs, num_q_heads, max_context_len, partition_tokens, &part))) return st;
-    const size_t need = workspace_bytes(c, num_seqs, num_q_heads, max_context_len, part);
-    if (need > 0) {
-        if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got NULL", need);
-        if (workspace_bytes_given < need)
-            return fail(PA_ERR_WORKSPACE, "pa_decode needs %zu bytes of workspace, got %zu", need, workspace_bytes_given);
-        if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    }
-    hipStream_t s = as_stream(stream);
-    if (validate_enabled()) {
-        std::vector<int32_t> lens, tables;
-        if ((st = fetch(lens, context_lens, num_seqs, s))) return st;
-        if ((st = fetch(tables, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, s))) return st;
-        for (int32_t i = 0; i < num_seqs; ++i) {
-            const int32_t L = lens[i];
-            if (L < 0 || L > max_context_len)
-                return fail(PA_ERR_VALIDATE, "context_lens[%d] = %d outside [0, %d]", i, L, max_context_len);
-            const int32_t nb = (L + c->block_size - 1) / c->block_size;
-            for (int32_t j = 0; j < nb; ++j) {
-                const int32_t b = tables[static_cast<size_t>(i) * max_blocks_per_seq + j];
-                if (b < 0 || b >= c->num_blocks)
-                    return fail(PA_ERR_VALIDATE, "block_tables[%d][%d] = %d outside [0, %lld)", i, j, b, (long long)c->num_blocks);
-            }
-        }
-    }
-    const int64_t parts64 = std::max<int64_t>(1, ceil_div(max_context_len, part));
-    if (parts64 > kMaxGridYZ)
-        return fail(PA_ERR_SHAPE, "max_context_len %d needs %lld partitions of %d tokens (> %d)",
-                    max_context_len, (long long)parts64, part, kMaxGridYZ);
-    const int32_t max_parts = static_cast<int32_t>(parts64);
-    DecodeArgs a;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.q = q;
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.num_blocks = c->num_blocks;
-    a.block_stride = block_stride(c);
-    a.block_size = c->block_size;
-    a.num_kv_heads = c->num_kv_heads;
-    a.head_dim = c->head_dim;
-    a.dtype = c->dtype;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.group = num_q_heads / c->num_kv_heads;
-    a.max_blocks_per_seq = max_blocks_per_seq;
-    a.len_clamp = max_context_len;
-    a.part_tokens = part;
-    a.max_parts = max_parts;
-    a.scale = scale;
-    a.flags = flags;
-    a.out = out;
-    const size_t slots = static_cast<size_t>(num_seqs) * num_q_heads * max_parts;
-    float* ws = need ? static_cast<float*>(workspace) : nullptr;
-    a.ws_acc = ws;
-    a.ws_m = need ? ws + slots * c->head_dim : nullptr;
-    a.ws_l = need ? ws + slots * (c->head_dim + 1) : nullptr;
-    a.stream = s;
-    if ((st = launch_decode(a))) return st;
-    return ok();
+              size_t workspace_bytes, int32_t partition_tokens, uint32_t flags, void* stream) {
+    return decode_impl("pa_decode", c, k_cache, v_cache, nullptr, nullptr, q, block_tables,
+                       context_lens, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
+                       scale, out, workspace, workspace_bytes, partition_tokens, flags, stream);
+}
+
+int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const void* q, const int32_t* block_tables,
+                     const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, float scale, void* out,
+                     void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                     uint32_t flags, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PA_ERR_NULL, "pa_decode_append: k_new and v_new are required");
+    return decode_impl("pa_decode_append", c, k_cache, v_cache, k_new, v_new, q, block_tables,
+                       context_lens, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
+                       scale, out, workspace, workspace_bytes, partition_tokens, flags, stream);
 }
 
 }  // extern "C"

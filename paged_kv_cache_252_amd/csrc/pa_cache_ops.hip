@@ -52,6 +52,46 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
     }
 }
 
+// ---- append: the same scatter for one token per request at position L-1, with
+// the slot translated here from the request's table -----------------------------
+template <typename E>
+__global__ __launch_bounds__(256) void append_kv_kernel(E* __restrict__ k_cache,
+                                                        E* __restrict__ v_cache,
+                                                        const E* __restrict__ k_new,
+                                                        const E* __restrict__ v_new,
+                                                        const int32_t* __restrict__ block_tables,
+                                                        const int32_t* __restrict__ context_lens,
+                                                        int max_blocks_per_seq, int len_clamp,
+                                                        int64_t num_blocks, int64_t blk_stride,
+                                                        int block_size, int num_kv_heads,
+                                                        int head_dim) {
+    constexpr int X = 16 / sizeof(E);
+    const int t = blockIdx.x;
+    int L = context_lens[t];
+    L = L > len_clamp ? len_clamp : L;
+    if (L <= 0) return;
+    const int lb = (L - 1) / block_size;
+    const int o = (L - 1) - lb * block_size;
+    const int phys = block_tables[static_cast<int64_t>(t) * max_blocks_per_seq + lb];
+    if (phys < 0 || phys >= num_blocks) return;
+    const int64_t b = phys;
+    const int chunks = head_dim / X;
+    const int64_t tile = static_cast<int64_t>(head_dim) * block_size;
+    const int64_t row = static_cast<int64_t>(t) * num_kv_heads * head_dim;
+    for (int i = threadIdx.x; i < num_kv_heads * chunks; i += blockDim.x) {
+        const int h = i / chunks;
+        const int c = i - h * chunks;
+        const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
+        E* dst = k_cache + b * blk_stride + h * tile + (static_cast<int64_t>(c) * block_size + o) * X;
+        *reinterpret_cast<uint4*>(dst) = v;
+    }
+    for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
+        const int h = i / head_dim;
+        const int d = i - h * head_dim;
+        v_cache[b * blk_stride + h * tile + static_cast<int64_t>(d) * block_size + o] = v_new[row + i];
+    }
+}
+
 // ---- copy: [ZQ] answer, [KG] "Shared Blocks Must Not Be Changed in Place" --
 // grid.x is the pair, grid.y covers one block's bytes in 4 KiB pieces (256
 // lanes x 16 bytes); K and V are copied by the same lanes.
@@ -140,6 +180,27 @@ int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, cons
                            c->head_dim);
     }
     return check_launch("write_kv");
+}
+
+int launch_append_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t len_clamp,
+                     hipStream_t stream) {
+    if (num_seqs == 0) return PA_OK;
+    if (c->dtype == PA_BF16) {
+        hipLaunchKernelGGL(append_kv_kernel<uint16_t>, dim3(num_seqs), dim3(256), 0, stream,
+                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+                           static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                           block_tables, context_lens, max_blocks_per_seq, len_clamp, c->num_blocks,
+                           block_stride(c), c->block_size, c->num_kv_heads, c->head_dim);
+    } else {
+        hipLaunchKernelGGL(append_kv_kernel<uint32_t>, dim3(num_seqs), dim3(256), 0, stream,
+                           static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
+                           static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
+                           block_tables, context_lens, max_blocks_per_seq, len_clamp, c->num_blocks,
+                           block_stride(c), c->block_size, c->num_kv_heads, c->head_dim);
+    }
+    return check_launch("append_kv");
 }
 
 int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,

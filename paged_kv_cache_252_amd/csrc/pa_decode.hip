@@ -187,14 +187,18 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
-template <int NBUF, bool NT>
+// APPEND: the call also appends each request's newest token (position L-1):
+// the wave of the request's last partition stores k_new/v_new into the cache
+// and uses them in place of whatever its load of that slot returned.
+template <int NBUF, bool NT, bool APPEND>
 __global__ __launch_bounds__(64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
     int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
     int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_m, float* __restrict__ ws_l) {
+    float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int num_kv_heads) {
     // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
     // dealt to the XCDs round-robin, so each XCD sees every partition index
     // and the same heads for all requests (a shared prefix's head slice then
@@ -231,6 +235,38 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
     if (lane < nblk)
         my_phys = clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
                               num_blocks);
+
+    // Appending: the last partition holds position L-1 at offset o of its
+    // last block.  The four lanes of row o hold that token's 16 key chunks
+    // (the same chunk order as the K tile); the 16 lanes of quad o/4 hold its
+    // 128 value dims (dim 16*j + row).  They also store them to the cache.
+    const bool append_here = APPEND && part == nparts - 1;
+    const int o_new = (L - 1) % FBS;
+    bf16x8 fk[4];
+    short fv[8];
+    if constexpr (APPEND) {
+        if (append_here) {
+            const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * FD;
+            const bf16x8* kn = reinterpret_cast<const bf16x8*>(k_new + nrow);
+            const short* vn = reinterpret_cast<const short*>(v_new + nrow);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) fk[s4] = kn[4 * s4 + quad];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) fv[j] = vn[16 * j + row];
+            const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, nblk - 1)) *
+                                     blk_stride + static_cast<int64_t>(h) * FTILE;
+            if (row == o_new) {
+                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * FBS + o_new] = fk[s4];
+            }
+            if (quad == o_new / 4) {
+                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + toff);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * FBS + o_new] = fv[j];
+            }
+        }
+    }
 
     // Query rows of this KV head as the B operand (rows >= group are zero).
     bf16x8 qv[4];
@@ -279,6 +315,18 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
                 load_tile<NT>(buf[(u + NBUF - 1) % NBUF], k_head + o, v_head + o, lane);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if constexpr (APPEND) {
+                if (append_here && j == nblk - 1) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        if (row == o_new) buf[u].k[s4] = fk[s4];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
+                }
+            }
             if (j < nblk)
                 consume_tile(st, buf[u], qv, scale_log2, lane, j == nblk - 1 ? last_valid : FBS);
             __builtin_amdgcn_sched_barrier(0);
@@ -411,10 +459,11 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
 // ============================================================================
 
 // One 256-lane workgroup per (request, query head).  Lane (c, g) owns dims
-// 4c..4c+3 and the partitions p = g, g + G, g + 2G, ... (G = 256 / (D/4)),
-// so the loads of all partitions are in flight at once; the G partial sums
-// are then added in increasing g.  Every sum has a fixed shape, so the
-// result is deterministic and independent of block placement.
+// 4c..4c+3 and the partitions p = g, g + G, g + 2G, ... (G = 256 / (D/4)).
+// Each lane folds its partitions into a running (max, sum, acc) as they
+// arrive -- one round trip to memory when there are at most G partitions --
+// and the G group states are then combined in increasing g.  Every sum has a
+// fixed shape, so the result is deterministic and independent of placement.
 constexpr int kMergeThreads = 256;
 
 template <typename T, int D>
@@ -424,8 +473,8 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
     const float* __restrict__ ws_l, T* __restrict__ out) {
     constexpr int C = D / 4;                   // float4 chunks per row
     constexpr int G = kMergeThreads / C;       // partition groups
-    __shared__ float s_max[kMergeThreads / 64];
     __shared__ f32x4 s_num[G][C];
+    __shared__ float s_m[G];
     __shared__ float s_den[G];
 
     const int hq = blockIdx.x;
@@ -437,36 +486,39 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
     if (nparts <= 1) return;   // written directly by the partition kernel
     const int64_t base = (static_cast<int64_t>(seq) * num_q_heads + hq) * max_parts;
 
-    float mx = -INFINITY;
-    for (int p = tid; p < nparts; p += kMergeThreads) mx = fmaxf(mx, ws_m[base + p]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if ((tid & 63) == 0) s_max[tid >> 6] = mx;
-    __syncthreads();
-    float M = s_max[0];
-#pragma unroll
-    for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, s_max[w]);
-
     const int c = tid % C;
     const int g = tid / C;
+    float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
 #pragma unroll 4
     for (int p = g; p < nparts; p += G) {
-        const float w = fast_exp2(ws_m[base + p] - M);
-        num += w * reinterpret_cast<const f32x4*>(ws_acc + (base + p) * D)[c];
-        den += w * ws_l[base + p];
+        const float mp = ws_m[base + p];
+        const float lp = ws_l[base + p];
+        const f32x4 ap = reinterpret_cast<const f32x4*>(ws_acc + (base + p) * D)[c];
+        const float Mn = fmaxf(M, mp);
+        const float a = fast_exp2(M - Mn);     // 0 on the first partition (M = -inf)
+        const float w = fast_exp2(mp - Mn);
+        num = num * a + ap * w;
+        den = den * a + lp * w;
+        M = Mn;
     }
     s_num[g][c] = num;
-    if (c == 0) s_den[g] = den;
+    if (c == 0) {
+        s_m[g] = M;
+        s_den[g] = den;
+    }
     __syncthreads();
     if (g != 0) return;
-    f32x4 tot = s_num[0][c];
-    float dtot = s_den[0];
+    float Mt = s_m[0];
 #pragma unroll
-    for (int k = 1; k < G; ++k) {
-        tot += s_num[k][c];
-        dtot += s_den[k];
+    for (int k = 1; k < G; ++k) Mt = fmaxf(Mt, s_m[k]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float dtot = 0.f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+        const float w = fast_exp2(s_m[k] - Mt);   // groups without partitions: 0 * 0
+        tot += s_num[k][c] * w;
+        dtot += s_den[k] * w;
     }
     const float inv = 1.f / dtot;
     T* o = out + (static_cast<int64_t>(seq) * num_q_heads + hq) * D + 4 * c;
@@ -504,16 +556,18 @@ int launch_generic_d(const DecodeArgs& a) {
     }
 }
 
-template <bool NT>
+template <bool NT, bool APPEND>
 int launch_fast(const DecodeArgs& a) {
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT>), grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_q_heads, a.group,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
-                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l);
+                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                       a.num_kv_heads);
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
     hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads),
@@ -526,8 +580,17 @@ int launch_fast(const DecodeArgs& a) {
 
 int launch_decode(const DecodeArgs& a) {
     pa_cache_desc_t c{a.num_blocks, a.block_size, a.num_kv_heads, a.head_dim, a.dtype, a.block_stride};
-    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0)
-        return (a.flags & PA_DECODE_STREAM_KV) ? launch_fast<true>(a) : launch_fast<false>(a);
+    const bool nt = (a.flags & PA_DECODE_STREAM_KV) != 0;
+    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0) {
+        if (a.k_new) return nt ? launch_fast<true, true>(a) : launch_fast<false, true>(a);
+        return nt ? launch_fast<true, false>(a) : launch_fast<false, false>(a);
+    }
+    if (a.k_new) {   // generic path: append with its own kernel, then decode
+        int st = launch_append_kv(&c, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache),
+                                  a.k_new, a.v_new, a.block_tables, a.context_lens, a.num_seqs,
+                                  a.max_blocks_per_seq, a.len_clamp, a.stream);
+        if (st != PA_OK) return st;
+    }
     if (a.dtype == PA_BF16) return launch_generic_d<uint16_t>(a);
     return launch_generic_d<float>(a);
 }

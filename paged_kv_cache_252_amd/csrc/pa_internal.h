@@ -81,6 +81,8 @@ struct DecodeArgs {
     float* ws_acc;           // [S][Hq][max_parts][D]
     float* ws_m;             // [S][Hq][max_parts]  (log2 domain running max)
     float* ws_l;             // [S][Hq][max_parts]
+    const void* k_new;       // non-null: append each request's token at position L-1
+    const void* v_new;
     hipStream_t stream;
 };
 
@@ -97,6 +99,11 @@ int launch_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t
                         int32_t max_blocks_per_seq, const int32_t* seq_ids,
                         const int32_t* positions, int32_t num_tokens, int64_t* slots,
                         hipStream_t stream);
+
+int launch_append_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                     const void* v_new, const int32_t* block_tables, const int32_t* context_lens,
+                     int32_t num_seqs, int32_t max_blocks_per_seq, int32_t len_clamp,
+                     hipStream_t stream);
 
 int launch_gather_kv(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
                      const int32_t* block_table, int32_t context_len, void* k_out, void* v_out,

@@ -117,6 +117,9 @@ _SIGNATURES = {
     "pa_decode": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _I32, _I32,
                                  _I32, _I32, ctypes.c_float, _P, _P, ctypes.c_size_t, _I32,
                                  ctypes.c_uint32, _P]),
+    "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P,
+                                        _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
+                                        ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
 }
 
 
@@ -283,16 +286,8 @@ def decode_workspace(spec: CacheSpec, num_seqs: int, num_q_heads: int, max_conte
     return None if need == 0 else torch.empty(need, dtype=torch.uint8, device=device)
 
 
-def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
-           max_context_len: int, scale: float, out=None, workspace=None,
-           partition_tokens: int = 0, stream_kv: bool = False):
-    """``pa_decode``: attention of one query per request over its paged history.
-
-    ``q`` is [num_seqs, Hq, head_dim]; returns ``out`` of the same shape and
-    dtype.  ``workspace`` (>= ``decode_workspace_bytes``) is allocated here
-    when not given.  ``stream_kv`` sets ``PA_DECODE_STREAM_KV``: a cache hint
-    for batches in which no block is read by two requests.
-    """
+def _decode_args(spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out,
+                 workspace, partition_tokens):
     dev = _cache_pair(spec, k_cache, v_cache)
     _need(q, "q", spec.torch_dtype, dev)
     _need(block_tables, "block_tables", torch.int32, dev)
@@ -312,6 +307,22 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if workspace is not None:
         _need(workspace, "workspace", workspace.dtype, dev)
+    return dev, s, hq, out, workspace, ws_bytes
+
+
+def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
+           max_context_len: int, scale: float, out=None, workspace=None,
+           partition_tokens: int = 0, stream_kv: bool = False):
+    """``pa_decode``: attention of one query per request over its paged history.
+
+    ``q`` is [num_seqs, Hq, head_dim]; returns ``out`` of the same shape and
+    dtype.  ``workspace`` (>= ``decode_workspace_bytes``) is allocated here
+    when not given.  ``stream_kv`` sets ``PA_DECODE_STREAM_KV``: a cache hint
+    for batches in which no block is read by two requests.
+    """
+    dev, s, hq, out, workspace, ws_bytes = _decode_args(
+        spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, workspace,
+        partition_tokens)
     d = spec.desc()
     _check("pa_decode", lib().pa_decode(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q),
                                         _ptr(block_tables), _ptr(context_lens), s, hq,
@@ -319,4 +330,28 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
                                         _ptr(out), _ptr(workspace), ws_bytes,
                                         partition_tokens,
                                         PA_DECODE_STREAM_KV if stream_kv else 0, _stream(dev)))
+    return out
+
+
+def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tables,
+                  context_lens, max_context_len: int, scale: float, out=None, workspace=None,
+                  partition_tokens: int = 0, stream_kv: bool = False):
+    """``pa_decode_append``: append each request's token at position L-1, then decode.
+
+    ``k_new``/``v_new`` are [num_seqs, Hkv, head_dim]; the caches are written.
+    """
+    dev, s, hq, out, workspace, ws_bytes = _decode_args(
+        spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, workspace,
+        partition_tokens)
+    _need(k_new, "k_new", spec.torch_dtype, dev)
+    _need(v_new, "v_new", spec.torch_dtype, dev)
+    per = s * spec.num_kv_heads * spec.head_dim
+    if k_new.numel() != per or v_new.numel() != per:
+        raise ValueError("k_new/v_new must be [num_seqs, Hkv, head_dim]")
+    d = spec.desc()
+    _check("pa_decode_append", lib().pa_decode_append(
+        ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q),
+        _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1], max_context_len,
+        float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
+        PA_DECODE_STREAM_KV if stream_kv else 0, _stream(dev)))
     return out

@@ -322,6 +322,53 @@ def test_fanout_step_end_to_end():
                           to_np(w.k_cache)[w.shared_blocks].view(np.uint16))
 
 
+@pytest.mark.parametrize("shape", ["fast", "fast_g8", "generic_f32", "generic_bf16_d64"])
+@pytest.mark.parametrize("part", [0, 32])
+@pytest.mark.parametrize("stream_kv", [False, True])
+def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
+    """The fused step (append token at L-1, then attend) gives the same cache
+    bytes and the same output bits as pa_write_kv followed by pa_decode, and
+    matches the oracle."""
+    say(f"decode_append {shape} part={part} stream={stream_kv}")
+    lens = [1, 15, 16, 17, 33, 100, 255, 256, 257, 0]
+    kw = dict(fast=dict(hq=8, hkv=2, d=128, bs=16, dtype="bf16"),
+              fast_g8=dict(hq=16, hkv=2, d=128, bs=16, dtype="bf16"),
+              generic_f32=dict(hq=4, hkv=2, d=32, bs=16, dtype="f32"),
+              generic_bf16_d64=dict(hq=4, hkv=2, d=64, bs=8, dtype="bf16"))[shape]
+    if part % kw["bs"]:
+        pytest.skip("partition must be a multiple of the block size")
+    w = inputs.paged_random("ap", len(lens), 0, 300, kw["hq"], kw["hkv"], head_dim=kw["d"],
+                            block_size=kw["bs"], dtype=kw["dtype"], num_blocks=260, seed=95,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    # reference on the GPU: separate calls
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                     w.max_context_len, w.scale, partition_tokens=part, stream_kv=stream_kv)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    # fused, from the same starting cache
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                              w.context_lens, w.max_context_len, w.scale, partition_tokens=part,
+                              stream_kv=stream_kv)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+    assert same_bits(fused, sep)
+    # and the oracle: write, then decode
+    want_slots = paged.slot_mapping(to_np(w.block_tables), to_np(w.new_seq), to_np(w.new_pos),
+                                    w.block_size)
+    kr, vr = paged.write_kv(to_np(k0), to_np(v0), to_np(w.new_k), to_np(w.new_v), want_slots,
+                            **oracle_args(w))
+    ref = paged.decode(to_np(w.q), kr, vr, to_np(w.block_tables), to_np(w.context_lens),
+                       w.scale, **oracle_args(w))
+    assert_close(w, fused, ref, "decode_append")
+
+
 def test_shared_workspace_across_calls():
     """One workspace, starting with garbage, reused by calls of different sizes
     and partition counts: every result matches the oracle."""
