@@ -197,6 +197,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-group", action="store_true",
+                    help="decode shared-prefix batches one request per wave")
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device-to-device copy timed first, as context and "
@@ -227,8 +229,10 @@ def main() -> int:
     ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(w.q) for _ in tables]
-    # no block is shared between requests in this batch: let decode stream K/V
+    # no block is shared between requests in this batch: let decode stream K/V;
+    # otherwise sharers are consecutive requests: decode them together
     stream_kv = w.shared_blocks is None
+    group_shared = w.shared_blocks is not None and not args.no_group
     log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
         f"workspace {ws_bytes} B, {reps} replicas")
 
@@ -239,7 +243,7 @@ def main() -> int:
             ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
         ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, tables[r],
                           w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
-                          partition_tokens=part, stream_kv=stream_kv)
+                          partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared)
 
     for i in range(args.warmup):
         step(i % reps)
@@ -270,7 +274,8 @@ def main() -> int:
     for i in range(args.kernel_iters):
         r = i % reps
         ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
-                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv)
+                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv,
+                   group_shared=group_shared)
     ev1.record(stream)
     ev1.synchronize()
     dec_us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
@@ -295,6 +300,7 @@ def main() -> int:
         "config": {"workload": cfg["desc"], "name": args.workload, "requests": w.num_seqs,
                    "max_context_len": max_len, "total_context_tokens": int(w.context_lens.sum()),
                    "replicas": reps, "partition_tokens": part, "stream_kv": stream_kv,
+                   "group_shared": group_shared,
                    "kv_layout": "one buffer [block][K|V], block_stride 2 blocks"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),

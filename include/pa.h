@@ -109,6 +109,13 @@ typedef struct {
 } pa_cache_desc_t;
 
 /* pa_decode flags */
+#define PA_DECODE_GROUP_SHARED 2u  /* consecutive requests may share leading blocks (a common
+                                      prompt or prefix): the fast path then processes up to
+                                      16 / (Hq/Hkv) consecutive requests per wave and reads a
+                                      block they all name only once.  Results equal the
+                                      ungrouped ones up to rounding (the per-request
+                                      partitions are unchanged; the tile order inside a
+                                      partition differs where members diverge). */
 #define PA_DECODE_STREAM_KV 1u  /* no physical block is read by more than one request of
                                    the call: read K/V with non-temporal loads, which keeps
                                    them from displacing other cache contents (measured:
@@ -251,7 +258,8 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *                 workspace.
  *   partition_tokens  0 = automatic; otherwise a multiple of block_size in
  *                 [block_size, 1024] (the fast path also needs a multiple of 16)
- *   flags         0 or PA_DECODE_STREAM_KV (a cache hint; results are the same)
+ *   flags         0 or an OR of PA_DECODE_STREAM_KV (a cache hint; results are the
+ *                 same) and PA_DECODE_GROUP_SHARED
  */
 int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
               const void* q, const int32_t* block_tables, const int32_t* context_lens,

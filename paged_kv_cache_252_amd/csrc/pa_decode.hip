@@ -85,6 +85,7 @@ __device__ __forceinline__ int clamp_block(int e, int64_t num_blocks) {
 constexpr int FD = 128;          // head_dim
 constexpr int FBS = 16;          // block_size
 constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile
+constexpr int FG = 16;           // query rows of the score MFMA
 
 struct Tile {
     bf16x8 k[4];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
@@ -359,6 +360,303 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
 }
 
 // ============================================================================
+// Grouped path: several requests per wave, shared blocks read once
+// ============================================================================
+//
+// The score MFMA has 16 query rows but a KV head has only g query heads, so
+// the fast path leaves 16 - g rows empty.  Here the rows hold up to
+// R = 16 / g consecutive requests (row = member * g + head in group).  For
+// each block position of the partition, if every member that has tokens in
+// that block names the same physical block with the same number of visible
+// tokens (a shared prefix, [ZQ] answer; [KG] "Prefix Sharing Is a Natural
+// Extension"), the tile is loaded once and scored against all members'
+// queries together.  Otherwise each member's tile is processed on its own
+// with the other members' rows masked out.  Rows keep separate online-softmax
+// states, so the arithmetic per row is the same as one request per wave; only
+// the partition's tile sequence differs.
+
+// consume_tile for rows with their own visibility.  row_valid: tokens of this
+// tile visible to this lane's row; v_valid: tokens whose V may be read (the
+// rest are zeroed); rows that have seen nothing yet stay at m = -inf.
+__device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
+                                                  const bf16x8 (&qv)[4], float scale_log2,
+                                                  int lane, int row_valid, int v_valid,
+                                                  bool masked) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
+    const int tok_base = 4 * (lane >> 4);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
+    if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok_base + i >= v_valid) t.v[j][i] = 0;
+    }
+    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const float m_new = fmaxf(st.m, mx);
+    const bool dead = m_new == -INFINITY;   // nothing visible to this row yet
+    const float alpha = dead ? 1.f : fast_exp2(st.m - m_new);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - m_new);
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    st.m = m_new;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+    const unsigned p01 = pack_bf16x2(p[0], p[1]);
+    const unsigned p23 = pack_bf16x2(p[2], p[3]);
+    s16x4 pb;
+    pb[0] = static_cast<short>(p01 & 0xffff);
+    pb[1] = static_cast<short>(p01 >> 16);
+    pb[2] = static_cast<short>(p23 & 0xffff);
+    pb[3] = static_cast<short>(p23 >> 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
+}
+
+// A task is one tile to consume: block position j of the partition, for all
+// members (r = kShared) or for member r alone.
+constexpr int kShared = -1;
+
+template <int MAXR, bool NT>
+__global__ __launch_bounds__(64) void decode_grouped_kernel(
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
+    int num_seqs, int num_q_heads, int group, int members, int max_blocks_per_seq,
+    int len_clamp, int part_tokens, int max_parts, float scale_log2, __bf16* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l) {
+    const int h = blockIdx.x;
+    const int grp = blockIdx.y;
+    // z = r_wave * max_parts + part: the waves that do the work of grouped
+    // partitions (r_wave 0) are dispatched before the ones that only work in
+    // per-member partitions and otherwise exit at once.
+    const int r_wave = blockIdx.z / max_parts;   // this wave's member in per-member mode
+    const int part = blockIdx.z - r_wave * max_parts;
+    const int lane = threadIdx.x;
+    const int row = lane & 15;
+    const int quad = lane >> 4;
+
+    const int seq0 = grp * members;
+    const int nmem = min(members, num_seqs - seq0);
+    const int my_mem = row / group;
+    const bool row_ok = my_mem < nmem;
+    const int my_seq = seq0 + (row_ok ? my_mem : 0);
+    const int hq = h * group + row % group;
+    auto clampL = [&](int L) { return L < 0 ? 0 : (L > len_clamp ? len_clamp : L); };
+
+    // Lane r < nmem holds member r's length; each lane also holds its row's.
+    const int Lr = lane < nmem ? clampL(context_lens[seq0 + lane]) : 0;
+    const int my_L = row_ok ? clampL(context_lens[my_seq]) : 0;
+    int Lmax = 0;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r)
+        if (r < nmem) Lmax = max(Lmax, __builtin_amdgcn_readlane(Lr, r));
+
+    const int tok0 = part * part_tokens;
+    auto write_zero_row = [&]() {
+        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+    };
+    if (tok0 >= Lmax) {
+        if (part == 0 && r_wave == 0 && row_ok && my_L == 0) write_zero_row();
+        return;
+    }
+    const int tok1 = min(Lmax, tok0 + part_tokens);
+    const int blk0 = tok0 / FBS;
+    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64
+
+    // Lane j: each member's physical block at position j (-1 where the member
+    // has no tokens), then whether position j is shared.
+    int phys[MAXR];
+    int p_sh = 0, v_sh = 0;
+    bool sh = true, full = true;
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r) {
+        phys[r] = -1;
+        if (r < nmem) {
+            const int Lm = __builtin_amdgcn_readlane(Lr, r);
+            const int valid = min(max(Lm - (tok0 + FBS * lane), 0), FBS);
+            if (lane < nblk && valid > 0) {
+                phys[r] = clamp_block(
+                    block_tables[static_cast<int64_t>(seq0 + r) * max_blocks_per_seq + blk0 + lane],
+                    num_blocks);
+                if (v_sh == 0) {
+                    p_sh = phys[r];
+                    v_sh = valid;
+                } else if (phys[r] != p_sh || valid != v_sh) {
+                    sh = false;
+                }
+            }
+            if (valid < FBS) full = false;
+        }
+    }
+    const uint64_t shared_mask = __ballot(sh && lane < nblk);
+    const uint64_t full_mask = __ballot(full && sh && lane < nblk);
+
+    // Grouped if walking all members' tiles in one wave costs at most 1.5x the
+    // longest member's own tile count; otherwise each member gets its own wave
+    // (all R waves of the group reach the same decision).
+    int tasks_here = 0, longest = 0;
+    if (lane < nblk) {
+        if (sh) {
+            tasks_here = 1;
+        } else {
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r) tasks_here += phys[r] >= 0 ? 1 : 0;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tasks_here += __shfl_xor(tasks_here, off);
+#pragma unroll
+    for (int r = 0; r < MAXR; ++r)
+        if (r < nmem) longest = max(longest, static_cast<int>(__popcll(__ballot(phys[r] >= 0))));
+    const bool grouped = 2 * tasks_here <= 3 * longest;
+    if (grouped ? r_wave != 0 : r_wave >= nmem) return;
+    const bool mine = row_ok && (grouped || my_mem == r_wave);
+
+    auto is_shared = [&](int j) { return ((shared_mask >> j) & 1ull) != 0; };
+    auto valid_of = [&](int r, int j) {
+        return min(max(__builtin_amdgcn_readlane(Lr, r) - (tok0 + FBS * j), 0), FBS);
+    };
+    // first task at position j (j < nblk): shared, or the first member with tokens
+    // there; in per-member mode this wave's member (MAXR: it has no tokens at j)
+    auto first_task = [&](int j) {
+        if (!grouped) return valid_of(r_wave, j) > 0 ? r_wave : MAXR;
+        if (is_shared(j)) return kShared;
+        int rr = MAXR;
+#pragma unroll
+        for (int r = MAXR - 1; r >= 0; --r)
+            if (r < nmem && valid_of(r, j) > 0) rr = r;
+        return rr;
+    };
+    struct Cursor { int j, r; };
+    auto advance = [&](Cursor c) {
+        if (!grouped) {
+            const int j = c.j + 1;
+            return (j < nblk && valid_of(r_wave, j) > 0) ? Cursor{j, r_wave} : Cursor{nblk, 0};
+        }
+        if (c.r != kShared) {
+            int rr = MAXR;
+#pragma unroll
+            for (int r = MAXR - 1; r >= 0; --r)
+                if (r > c.r && r < nmem && valid_of(r, c.j) > 0) rr = r;
+            if (rr < MAXR) return Cursor{c.j, rr};
+        }
+        const int j = c.j + 1;
+        return Cursor{j, j < nblk ? first_task(j) : 0};
+    };
+    auto task_phys = [&](Cursor c) {
+        if (c.r == kShared) return __builtin_amdgcn_readlane(p_sh, c.j);
+        int ph = 0;
+#pragma unroll
+        for (int r = 0; r < MAXR; ++r)
+            if (r == c.r) ph = __builtin_amdgcn_readlane(phys[r], c.j);
+        return ph;
+    };
+
+    // Query rows: member my_mem's query head hq (rows of absent members are zero).
+    bf16x8 qv[4];
+    {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            q + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            bf16x8 v = qp[4 * s4 + quad];
+            qv[s4] = row_ok ? v : bf16x8{};
+        }
+    }
+
+    SoftmaxState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
+    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
+    auto load_task = [&](Tile& t, Cursor c) {
+        const int64_t o = static_cast<int64_t>(task_phys(c)) * blk_stride;
+        load_tile<NT>(t, k_head + o, v_head + o, lane);
+    };
+    auto consume_task = [&](Tile& t, Cursor c) {
+        const int my_valid = min(max(my_L - (tok0 + FBS * c.j), 0), FBS);
+        int row_valid, v_valid;
+        bool masked;
+        if (c.r == kShared) {
+            row_valid = my_valid;
+            v_valid = __builtin_amdgcn_readlane(v_sh, c.j);
+            masked = ((full_mask >> c.j) & 1ull) == 0;
+        } else {
+            row_valid = (row_ok && my_mem == c.r) ? my_valid : 0;
+            v_valid = valid_of(c.r, c.j);
+            masked = true;
+        }
+        consume_tile_rows(st, t, qv, scale_log2, lane, row_valid, v_valid, masked);
+    };
+
+    // Two tiles in flight, as on the fast path; past the last task the
+    // prefetch repeats the current tile (still in cache).
+    Tile ta, tb;
+    Cursor cu{0, first_task(0)};
+    if (cu.r == MAXR) cu.j = nblk;   // per-member mode, member without tokens here
+    Cursor cl = cu;
+    if (cu.j < nblk) {
+        load_task(ta, cl);
+        cl = advance(cl);
+    }
+    while (cu.j < nblk) {
+        load_task(tb, cl.j < nblk ? cl : cu);
+        if (cl.j < nblk) cl = advance(cl);
+        __builtin_amdgcn_sched_barrier(0);
+        consume_task(ta, cu);
+        cu = advance(cu);
+        __builtin_amdgcn_sched_barrier(0);
+        if (cu.j >= nblk) break;
+        load_task(ta, cl.j < nblk ? cl : cu);
+        if (cl.j < nblk) cl = advance(cl);
+        __builtin_amdgcn_sched_barrier(0);
+        consume_task(tb, cu);
+        cu = advance(cu);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    const float lsum = sum_across_rows(st.l);
+    if (!mine) return;
+    if (tok0 >= my_L) {                       // this row has no tokens in this partition
+        if (part == 0 && my_L == 0) write_zero_row();
+        return;
+    }
+    const int my_nparts = (my_L + part_tokens - 1) / part_tokens;
+    if (my_nparts == 1) {
+        const float inv = 1.f / lsum;
+        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
+                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
+        return;
+    }
+    const int64_t pidx = (static_cast<int64_t>(my_seq) * num_q_heads + hq) * max_parts + part;
+    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
+    if (quad == 0) {
+        ws_m[pidx] = st.m;
+        ws_l[pidx] = lsum;
+    }
+}
+
+// ============================================================================
 // Generic path
 // ============================================================================
 
@@ -576,11 +874,50 @@ int launch_fast(const DecodeArgs& a) {
     return check_launch("decode reduce");
 }
 
+template <int MAXR, bool NT>
+int launch_grouped(const DecodeArgs& a, int members) {
+    const int groups = (a.num_seqs + members - 1) / members;
+    dim3 grid(a.num_kv_heads, groups, a.max_parts * members);
+    const float sl2 = a.scale * kLog2e;
+    hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT>), grid, dim3(64), 0, a.stream,
+                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
+                       static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
+                       a.num_blocks, a.block_stride, a.num_seqs, a.num_q_heads, a.group, members,
+                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
+                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l);
+    int st = check_launch("decode (grouped)");
+    if (st != PA_OK || a.max_parts <= 1) return st;
+    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads),
+                       0, a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
+                       a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
+    return check_launch("decode reduce");
+}
+
+template <bool NT>
+int launch_grouped_r(const DecodeArgs& a) {
+    const int members = FG / a.group;   // requests per wave
+    if (members <= 2) return launch_grouped<2, NT>(a, members);
+    if (members <= 4) return launch_grouped<4, NT>(a, members);
+    if (members <= 8) return launch_grouped<8, NT>(a, members);
+    return launch_grouped<16, NT>(a, members);
+}
+
 }  // namespace
 
 int launch_decode(const DecodeArgs& a) {
     pa_cache_desc_t c{a.num_blocks, a.block_size, a.num_kv_heads, a.head_dim, a.dtype, a.block_stride};
     const bool nt = (a.flags & PA_DECODE_STREAM_KV) != 0;
+    const int64_t grouped_z = static_cast<int64_t>(a.max_parts) * (FG / a.group);
+    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0 && (a.flags & PA_DECODE_GROUP_SHARED) &&
+        a.group <= FG / 2 && grouped_z <= 65535) {
+        if (a.k_new) {   // append first, then the grouped decode reads the token back
+            int st = launch_append_kv(&c, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache),
+                                      a.k_new, a.v_new, a.block_tables, a.context_lens, a.num_seqs,
+                                      a.max_blocks_per_seq, a.len_clamp, a.stream);
+            if (st != PA_OK) return st;
+        }
+        return nt ? launch_grouped_r<true>(a) : launch_grouped_r<false>(a);
+    }
     if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0) {
         if (a.k_new) return nt ? launch_fast<true, true>(a) : launch_fast<false, true>(a);
         return nt ? launch_fast<true, false>(a) : launch_fast<false, false>(a);

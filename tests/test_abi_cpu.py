@@ -75,7 +75,7 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, _desc(), part=24) == 2                      # not a multiple of 16
     assert _decode(lib, _desc(), part=2048) == 2                    # above 1024
     assert _decode(lib, _desc(), ptr=(1 << 20) + 8) == 4            # misaligned buffers
-    assert _decode(lib, _desc(), flags=2) == 5                      # unknown flag bit
+    assert _decode(lib, _desc(), flags=4) == 5                      # unknown flag bit
     d = _desc()
     assert lib.pa_decode(ctypes.byref(d), None, None, None, None, None, 2, 32, 4, 64, 0.1, None,
                          None, 0, 16, 0, None) == 1

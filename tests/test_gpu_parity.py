@@ -369,6 +369,63 @@ def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
     assert_close(w, fused, ref, "decode_append")
 
 
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("part", [0, 16, 64])
+def test_grouped_decode_bit_identical(group, part):
+    """PA_DECODE_GROUP_SHARED gives the same bits as one request per wave, on a
+    batch mixing shared prefixes, private suffixes, unshared requests, L = 0
+    and a last group that is not full."""
+    say(f"grouped decode g={group} part={part}")
+    hkv = 2
+    w = inputs.shared_prefix(num_seqs=11, prefix_len=64, suffix_lo=1, suffix_hi=90,
+                             num_blocks=300, num_q_heads=hkv * group, num_kv_heads=hkv,
+                             device=DEV)
+    # make request 3 independent of the prefix and give request 5 no history
+    used = set(w.referenced_blocks().tolist())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    for j in range(4):
+        nb = free.pop()
+        w.k_cache[nb] = w.k_cache[int(w.shared_blocks[j])]
+        w.v_cache[nb] = w.v_cache[int(w.shared_blocks[j])]
+        w.block_tables[3, j] = nb
+    w.context_lens[5] = 0
+    poison_tails(w)
+    ref = oracle_decode(w)
+    spec = ops.CacheSpec.of(w)
+    base = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                      w.max_context_len, w.scale, partition_tokens=part)
+    for stream_kv in (False, True):
+        grouped = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                             w.max_context_len, w.scale, partition_tokens=part,
+                             stream_kv=stream_kv, group_shared=True)
+        assert same_bits(grouped, base)
+    assert_close(w, grouped, ref, f"grouped g={group}")
+
+
+def test_grouped_fanout_step():
+    """Fan-out branches decoded four per wave: copy, grouped append+decode."""
+    say("grouped fan-out step")
+    w = inputs.fanout(num_prompts=9, branches=4, prompt_lo=20, prompt_hi=300, num_blocks=500,
+                      device=DEV)
+    spec = ops.CacheSpec.of(w)
+    kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+    k1, v1 = paged.copy_blocks(kp, vp, to_np(w.cow_pairs))
+    want_slots = paged.slot_mapping(to_np(w.block_tables), to_np(w.new_seq), to_np(w.new_pos),
+                                    w.block_size)
+    k2, v2 = paged.write_kv(k1, v1, to_np(w.new_k), to_np(w.new_v), want_slots, **oracle_args(w))
+    ref = paged.decode(to_np(w.q), k2, v2, to_np(w.block_tables), to_np(w.context_lens),
+                       w.scale, **oracle_args(w))
+    ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
+    out = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                            w.context_lens, w.max_context_len, w.scale, group_shared=True)
+    torch.cuda.synchronize()
+    assert to_np(w.k_cache).tobytes() == k2.tobytes() and to_np(w.v_cache).tobytes() == v2.tobytes()
+    assert_close(w, out, ref, "grouped fan-out")
+    plain = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                       w.max_context_len, w.scale)
+    assert same_bits(out, plain)
+
+
 def test_shared_workspace_across_calls():
     """One workspace, starting with garbage, reused by calls of different sizes
     and partition counts: every result matches the oracle."""
