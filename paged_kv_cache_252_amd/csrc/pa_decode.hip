@@ -86,6 +86,8 @@ constexpr int FD = 128;          // head_dim
 constexpr int FBS = 16;          // block_size
 constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile
 constexpr int FG = 16;           // query rows of the score MFMA
+constexpr int kMaxWgParts = 8;   // partitions merged inside one workgroup
+constexpr size_t kMaxWgLds = 32768;
 
 struct Tile {
     bf16x8 k[4];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
@@ -135,6 +137,11 @@ __device__ __forceinline__ float sum_across_rows(float x) {
     const unsigned w = __float_as_uint(y);
     auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ f32x4 fma4(f32x4 a, float w, f32x4 c) {
+    return f32x4{__builtin_fmaf(a[0], w, c[0]), __builtin_fmaf(a[1], w, c[1]),
+                 __builtin_fmaf(a[2], w, c[2]), __builtin_fmaf(a[3], w, c[3])};
 }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
@@ -191,8 +198,12 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
 // APPEND: the call also appends each request's newest token (position L-1):
 // the wave of the request's last partition stores k_new/v_new into the cache
 // and uses them in place of whatever its load of that slot returned.
-template <int NBUF, bool NT, bool APPEND>
-__global__ __launch_bounds__(64) void decode_fast_kernel(
+// WGM: the partitions of one (request, KV head) are the waves of one
+// workgroup (wave w = partition w, at most kMaxWgParts of them) and are
+// merged through LDS after a workgroup barrier, instead of by the merge
+// kernel.  Waves without a partition wait at the barrier.
+template <int NBUF, bool NT, bool APPEND, bool WGM>
+__global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -206,8 +217,8 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
     // stays in one XCD's L2).
     const int h = blockIdx.x;
     const int seq = blockIdx.y;
-    const int part = blockIdx.z;
-    const int lane = threadIdx.x;
+    const int part = WGM ? static_cast<int>(threadIdx.x >> 6) : static_cast<int>(blockIdx.z);
+    const int lane = threadIdx.x & 63;
     const int row = lane & 15;
     const int quad = lane >> 4;
 
@@ -216,21 +227,33 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
     const int tok0 = part * part_tokens;
     const int hq = h * group + row;
     const bool row_ok = row < group;
+    auto out_row = [&]() {
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+    };
 
-    if (tok0 >= L) {
+    if (!WGM && tok0 >= L) {
         if (L == 0 && part == 0 && row_ok) {   // empty history: zero output
-            uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+            uint2* o = out_row();
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
         }
         return;
     }
+    const bool active = tok0 < L;
     const int tok1 = min(L, tok0 + part_tokens);
     const int nparts = (L + part_tokens - 1) / part_tokens;
     const int blk0 = tok0 / FBS;
     const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64
     const int last_valid = tok1 - (tok0 + (nblk - 1) * FBS);
 
+    SoftmaxState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+
+    if (active) {
     // Block-table entries of this partition: one per lane, read back with readlane.
     int my_phys = 0;
     if (lane < nblk)
@@ -284,12 +307,6 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
     const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
     const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
 
-    SoftmaxState st;
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     // A ring of NBUF tiles: while block j is consumed, blocks j+1 .. j+NBUF-1
     // are in flight.  Loads are unconditional (past the end they repeat the
     // last block, which is then still in cache), so every path through the
@@ -335,12 +352,63 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(
     }
 
     // The four lanes of a query row each summed a quarter of the tokens.
-    const float lsum = sum_across_rows(st.l);
+    lsum = sum_across_rows(st.l);
+    }   // active
+
+    if constexpr (WGM) {
+        // LDS: [partition][row < group][acc 128 | m | l | pad 2]
+        extern __shared__ float wg_part[];
+        constexpr int RS = FD + 4;
+        if (active && nparts > 1 && row_ok) {
+            float* dst = wg_part + (part * group + row) * RS;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<f32x4*>(dst + 16 * jj + 4 * quad) = st.acc[jj];
+            if (quad == 0) {
+                dst[FD] = st.m;
+                dst[FD + 1] = lsum;
+            }
+        }
+        __syncthreads();
+        if (part != 0 || !row_ok) return;
+        uint2* o = out_row();
+        if (L == 0) {                          // empty history: zero output
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+            return;
+        }
+        if (nparts > 1) {
+            // merge partitions 0..nparts-1 in order (the merge kernel's formula:
+            // global max first, then fused multiply-adds in partition order);
+            // lane: row, dims 32*quad..+31
+            float M = wg_part[row * RS + FD];
+            for (int p = 1; p < nparts; ++p) M = fmaxf(M, wg_part[(p * group + row) * RS + FD]);
+            float den = 0.f;
+            f32x4 num[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int p = 0; p < nparts; ++p) {
+                const float* src = wg_part + (p * group + row) * RS;
+                const float w = fast_exp2(src[FD] - M);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    num[k] = fma4(*reinterpret_cast<const f32x4*>(src + 32 * quad + 4 * k), w, num[k]);
+                den = __builtin_fmaf(src[FD + 1], w, den);
+            }
+            const float inv = 1.f / den;
+            uint2* ob = o + 8 * quad;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                ob[k] = make_uint2(pack_bf16x2(num[k][0] * inv, num[k][1] * inv),
+                                   pack_bf16x2(num[k][2] * inv, num[k][3] * inv));
+            return;
+        }
+        // a single partition: wave 0 holds the whole result (falls through)
+    }
 
     if (nparts == 1) {
         if (!row_ok) return;
         const float inv = 1.f / lsum;
-        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+        uint2* o = out_row();
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
             o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
@@ -786,18 +854,25 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
 
     const int c = tid % C;
     const int g = tid / C;
+    // group g's first partition is taken as is; later ones are folded in with
+    // a running max (only when there are more than G partitions)
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    if (g < nparts) {
+        M = ws_m[base + g];
+        den = ws_l[base + g];
+        num = reinterpret_cast<const f32x4*>(ws_acc + (base + g) * D)[c];
+    }
 #pragma unroll 4
-    for (int p = g; p < nparts; p += G) {
+    for (int p = g + G; p < nparts; p += G) {
         const float mp = ws_m[base + p];
         const float lp = ws_l[base + p];
         const f32x4 ap = reinterpret_cast<const f32x4*>(ws_acc + (base + p) * D)[c];
         const float Mn = fmaxf(M, mp);
-        const float a = fast_exp2(M - Mn);     // 0 on the first partition (M = -inf)
+        const float a = fast_exp2(M - Mn);
         const float w = fast_exp2(mp - Mn);
-        num = num * a + ap * w;
-        den = den * a + lp * w;
+        num = fma4(ap, w, num * a);
+        den = __builtin_fmaf(lp, w, den * a);
         M = Mn;
     }
     s_num[g][c] = num;
@@ -807,16 +882,18 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
     }
     __syncthreads();
     if (g != 0) return;
+    // global max first, then fused multiply-adds in group order (with at most
+    // G partitions: in partition order -- the same formula as the in-workgroup
+    // merge of the decode kernel)
+    const int ng = nparts < G ? nparts : G;
     float Mt = s_m[0];
-#pragma unroll
-    for (int k = 1; k < G; ++k) Mt = fmaxf(Mt, s_m[k]);
+    for (int k = 1; k < ng; ++k) Mt = fmaxf(Mt, s_m[k]);
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
     float dtot = 0.f;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-        const float w = fast_exp2(s_m[k] - Mt);   // groups without partitions: 0 * 0
-        tot += s_num[k][c] * w;
-        dtot += s_den[k] * w;
+    for (int k = 0; k < ng; ++k) {
+        const float w = fast_exp2(s_m[k] - Mt);
+        tot = fma4(s_num[k][c], w, tot);
+        dtot = __builtin_fmaf(s_den[k], w, dtot);
     }
     const float inv = 1.f / dtot;
     T* o = out + (static_cast<int64_t>(seq) * num_q_heads + hq) * D + 4 * c;
@@ -856,9 +933,23 @@ int launch_generic_d(const DecodeArgs& a) {
 
 template <bool NT, bool APPEND>
 int launch_fast(const DecodeArgs& a) {
-    dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND>), grid, dim3(64), 0, a.stream,
+    const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (FD + 4) * sizeof(float);
+    if (a.max_parts >= 2 && a.max_parts <= kMaxWgParts && wg_lds <= kMaxWgLds) {
+        // partitions of a request are the waves of one workgroup, merged in LDS
+        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true>),
+                           dim3(a.num_kv_heads, a.num_seqs, 1), dim3(64 * a.max_parts), wg_lds,
+                           a.stream, static_cast<const __bf16*>(a.k_cache),
+                           static_cast<const __bf16*>(a.v_cache), static_cast<const __bf16*>(a.q),
+                           a.block_tables, a.context_lens, a.num_blocks, a.block_stride,
+                           a.num_q_heads, a.group, a.max_blocks_per_seq, a.len_clamp, a.part_tokens,
+                           a.max_parts, sl2, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                           static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                           a.num_kv_heads);
+        return check_launch("decode (fast, workgroup merge)");
+    }
+    dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
+    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_q_heads, a.group,
