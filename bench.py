@@ -199,6 +199,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-group", action="store_true",
                     help="decode shared-prefix batches one request per wave")
+    ap.add_argument("--stream-kv", choices=("auto", "on", "off"), default="auto",
+                    help="non-temporal K/V loads: auto = on, except for shared blocks "
+                         "decoded one request per wave (--no-group), whose repeat reads "
+                         "must hit the caches")
     ap.add_argument("--kernel-iters", type=int, default=200)
     ap.add_argument("--copy-probe-mib", type=int, default=1024,
                     help="size of a plain device-to-device copy timed first, as context and "
@@ -229,10 +233,11 @@ def main() -> int:
     ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(w.q) for _ in tables]
-    # no block is shared between requests in this batch: let decode stream K/V;
-    # otherwise sharers are consecutive requests: decode them together
-    stream_kv = w.shared_blocks is None
+    # sharers are consecutive requests: decode them together (each shared
+    # block is then read once per group) and stream K/V
     group_shared = w.shared_blocks is not None and not args.no_group
+    stream_kv = {"on": True, "off": False}.get(args.stream_kv,
+                                                w.shared_blocks is None or group_shared)
     log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
         f"workspace {ws_bytes} B, {reps} replicas")
 

@@ -116,12 +116,14 @@ typedef struct {
                                       ungrouped ones up to rounding (the per-request
                                       partitions are unchanged; the tile order inside a
                                       partition differs where members diverge). */
-#define PA_DECODE_STREAM_KV 1u  /* no physical block is read by more than one request of
-                                   the call: read K/V with non-temporal loads, which keeps
-                                   them from displacing other cache contents (measured:
-                                   +6..13% on unshared batches; leave it off when
-                                   requests share prefix blocks, whose repeat reads then
-                                   hit the caches) */
+#define PA_DECODE_STREAM_KV 1u  /* read K/V with non-temporal loads, which keeps them from
+                                   displacing other cache contents.  A cache hint only:
+                                   results are identical.  Measured on MI355X: +6..13% when
+                                   no block is read by two waves of the call (unshared
+                                   batches, or shared blocks decoded with
+                                   PA_DECODE_GROUP_SHARED, which reads each once per group);
+                                   -10% for a prefix shared by many requests decoded one
+                                   request per wave, whose repeat reads must hit the caches */
 
 /* Version of this ABI (PA_ABI_VERSION of the library that was built). */
 int pa_abi_version(void);
