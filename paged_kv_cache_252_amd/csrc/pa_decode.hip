@@ -494,14 +494,19 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
 // members (r = kShared) or for member r alone.
 constexpr int kShared = -1;
 
-template <int MAXR, bool NT>
+// APPEND: as on the fast path, each member's newest token (position L-1) is
+// stored by the wave that handles the member's last block and substituted
+// into that tile; the token is staged in LDS because one wave may append for
+// several members.
+template <int MAXR, bool NT, bool APPEND>
 __global__ __launch_bounds__(64) void decode_grouped_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
     int num_seqs, int num_q_heads, int group, int members, int max_blocks_per_seq,
     int len_clamp, int part_tokens, int max_parts, float scale_log2, __bf16* __restrict__ out,
-    float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l) {
+    float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new, int num_kv_heads) {
     const int h = blockIdx.x;
     const int grp = blockIdx.y;
     // z = r_wave * max_parts + part: the waves that do the work of grouped
@@ -542,6 +547,30 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
     const int tok1 = min(Lmax, tok0 + part_tokens);
     const int blk0 = tok0 / FBS;
     const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64
+
+    // Appending: the token of each member this wave handles whose newest
+    // position lies in this partition goes to the cache and to LDS, from
+    // which it replaces that slot of the loaded tile.  A token is 256 B of K
+    // and 256 B of V; a quarter-wave moves one member (16 B of K and 8 dims
+    // of V per lane), four members a round.  The token loads go out here,
+    // ahead of the block-table reads, so that they have landed when the
+    // stores need them.
+    constexpr int kRounds = APPEND ? (MAXR + 3) / 4 : 1;
+    bf16x8 nk[kRounds], nv[kRounds];
+    bool nload[kRounds];
+    if constexpr (APPEND) {
+#pragma unroll
+        for (int it = 0; it < kRounds; ++it) {
+            const int r = 4 * it + quad;
+            const int Lm = __shfl(Lr, r);
+            nload[it] = r < nmem && Lm > 0 && Lm - 1 >= tok0 && Lm - 1 < tok1;
+            if (nload[it]) {
+                const int64_t nrow = (static_cast<int64_t>(seq0 + r) * num_kv_heads + h) * FD;
+                nk[it] = reinterpret_cast<const bf16x8*>(k_new + nrow)[row];
+                nv[it] = reinterpret_cast<const bf16x8*>(v_new + nrow)[row];
+            }
+        }
+    }
 
     // Lane j: each member's physical block at position j (-1 where the member
     // has no tokens), then whether position j is shared.
@@ -632,6 +661,61 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
         return ph;
     };
 
+    __shared__ bf16x8 fresh_k[APPEND ? MAXR : 1][FD / 8];   // K chunk c at [r][c]
+    __shared__ bf16x8 fresh_v[APPEND ? MAXR : 1][FD / 8];   // dims 8c..8c+7 at [r][c]
+    auto substitute = [&](Tile& t, int r) {   // the newest slot of member r's tile
+        const int om = (__builtin_amdgcn_readlane(Lr, r) - 1) % FBS;
+        if (row == om) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = fresh_k[r][4 * s4 + quad];
+        }
+        const short* fv = reinterpret_cast<const short*>(&fresh_v[r][0]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (quad * 4 + e == om) t.v[jj][e] = fv[16 * jj + row];
+    };
+    // Lane j: the members whose newest token lies at position j (a bit each);
+    // the tokens go to LDS now and to the cache once the tiles are consumed
+    // (stores issued ahead of the tile loads would hold up the loop's waits).
+    auto appends_here = [&](int r, int& Lm) {
+        if (r >= nmem || (!grouped && r != r_wave)) return false;
+        Lm = __builtin_amdgcn_readlane(Lr, r);
+        return Lm > 0 && Lm - 1 >= tok0 && Lm - 1 < tok1;
+    };
+    int newest_mask = 0;
+    if constexpr (APPEND) {
+#pragma unroll
+        for (int r = 0; r < MAXR; ++r) {
+            int Lm;
+            if (!appends_here(r, Lm)) continue;
+            if (lane == (Lm - 1) / FBS - blk0) newest_mask |= 1 << r;
+            if (quad == r % 4) {   // the quarter-wave that loaded member r's token
+                fresh_k[r][row] = nk[r / 4];
+                fresh_v[r][row] = nv[r / 4];
+            }
+        }
+    }
+    auto store_new_tokens = [&]() {
+#pragma unroll
+        for (int r = 0; r < MAXR; ++r) {
+            int Lm;
+            if (!appends_here(r, Lm)) continue;
+            if (quad != r % 4) continue;
+            const int jl = (Lm - 1) / FBS - blk0;
+            const int om = (Lm - 1) % FBS;
+            const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(phys[r], jl)) *
+                                     blk_stride + static_cast<int64_t>(h) * FTILE;
+            reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff)[row * FBS + om] = fresh_k[r][row];
+            // V: sixteen consecutive dims per store, 512 B of the tile apart
+            const short* fv = reinterpret_cast<const short*>(&fresh_v[r][0]);
+            short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + toff);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vd[(16 * e + row) * FBS + om] = fv[16 * e + row];
+        }
+    };
+
     // Query rows: member my_mem's query head hq (rows of absent members are zero).
     bf16x8 qv[4];
     {
@@ -664,10 +748,17 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
             row_valid = my_valid;
             v_valid = __builtin_amdgcn_readlane(v_sh, c.j);
             masked = ((full_mask >> c.j) & 1ull) == 0;
+            if constexpr (APPEND) {   // a position held by one member only counts as shared
+                const int nm = __builtin_amdgcn_readlane(newest_mask, c.j);
+                if (nm != 0) substitute(t, __builtin_ctz(nm));
+            }
         } else {
             row_valid = (row_ok && my_mem == c.r) ? my_valid : 0;
             v_valid = valid_of(c.r, c.j);
             masked = true;
+            if constexpr (APPEND) {
+                if ((__builtin_amdgcn_readlane(newest_mask, c.j) >> c.r) & 1) substitute(t, c.r);
+            }
         }
         consume_tile_rows(st, t, qv, scale_log2, lane, row_valid, v_valid, masked);
     };
@@ -697,6 +788,7 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
         cu = advance(cu);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (APPEND) store_new_tokens();
 
     const float lsum = sum_across_rows(st.l);
     if (!mine) return;
@@ -965,17 +1057,19 @@ int launch_fast(const DecodeArgs& a) {
     return check_launch("decode reduce");
 }
 
-template <int MAXR, bool NT>
+template <int MAXR, bool NT, bool APPEND>
 int launch_grouped(const DecodeArgs& a, int members) {
     const int groups = (a.num_seqs + members - 1) / members;
     dim3 grid(a.num_kv_heads, groups, a.max_parts * members);
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT>), grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT, APPEND>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_seqs, a.num_q_heads, a.group, members,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
-                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l);
+                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                       a.num_kv_heads);
     int st = check_launch("decode (grouped)");
     if (st != PA_OK || a.max_parts <= 1) return st;
     hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads),
@@ -984,13 +1078,13 @@ int launch_grouped(const DecodeArgs& a, int members) {
     return check_launch("decode reduce");
 }
 
-template <bool NT>
+template <bool NT, bool APPEND>
 int launch_grouped_r(const DecodeArgs& a) {
     const int members = FG / a.group;   // requests per wave
-    if (members <= 2) return launch_grouped<2, NT>(a, members);
-    if (members <= 4) return launch_grouped<4, NT>(a, members);
-    if (members <= 8) return launch_grouped<8, NT>(a, members);
-    return launch_grouped<16, NT>(a, members);
+    if (members <= 2) return launch_grouped<2, NT, APPEND>(a, members);
+    if (members <= 4) return launch_grouped<4, NT, APPEND>(a, members);
+    if (members <= 8) return launch_grouped<8, NT, APPEND>(a, members);
+    return launch_grouped<16, NT, APPEND>(a, members);
 }
 
 }  // namespace
@@ -1001,13 +1095,8 @@ int launch_decode(const DecodeArgs& a) {
     const int64_t grouped_z = static_cast<int64_t>(a.max_parts) * (FG / a.group);
     if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0 && (a.flags & PA_DECODE_GROUP_SHARED) &&
         a.group <= FG / 2 && grouped_z <= 65535) {
-        if (a.k_new) {   // append first, then the grouped decode reads the token back
-            int st = launch_append_kv(&c, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache),
-                                      a.k_new, a.v_new, a.block_tables, a.context_lens, a.num_seqs,
-                                      a.max_blocks_per_seq, a.len_clamp, a.stream);
-            if (st != PA_OK) return st;
-        }
-        return nt ? launch_grouped_r<true>(a) : launch_grouped_r<false>(a);
+        if (a.k_new) return nt ? launch_grouped_r<true, true>(a) : launch_grouped_r<false, true>(a);
+        return nt ? launch_grouped_r<true, false>(a) : launch_grouped_r<false, false>(a);
     }
     if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0) {
         if (a.k_new) return nt ? launch_fast<true, true>(a) : launch_fast<false, true>(a);

@@ -322,7 +322,8 @@ def test_fanout_step_end_to_end():
                           to_np(w.k_cache)[w.shared_blocks].view(np.uint16))
 
 
-@pytest.mark.parametrize("shape", ["fast", "fast_g8", "generic_f32", "generic_bf16_d64"])
+@pytest.mark.parametrize("shape", ["fast", "fast_g8", "generic_f32", "generic_bf16_d64",
+                                   "grouped", "grouped_g8"])
 @pytest.mark.parametrize("part", [0, 32])
 @pytest.mark.parametrize("stream_kv", [False, True])
 def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
@@ -333,6 +334,8 @@ def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
     lens = [1, 15, 16, 17, 33, 100, 255, 256, 257, 0]
     kw = dict(fast=dict(hq=8, hkv=2, d=128, bs=16, dtype="bf16"),
               fast_g8=dict(hq=16, hkv=2, d=128, bs=16, dtype="bf16"),
+              grouped=dict(hq=8, hkv=2, d=128, bs=16, dtype="bf16"),
+              grouped_g8=dict(hq=16, hkv=2, d=128, bs=16, dtype="bf16"),
               generic_f32=dict(hq=4, hkv=2, d=32, bs=16, dtype="f32"),
               generic_bf16_d64=dict(hq=4, hkv=2, d=64, bs=8, dtype="bf16"))[shape]
     if part % kw["bs"]:
@@ -355,7 +358,7 @@ def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
     w.v_cache.copy_(v0)
     fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
                               w.context_lens, w.max_context_len, w.scale, partition_tokens=part,
-                              stream_kv=stream_kv)
+                              stream_kv=stream_kv, group_shared=shape.startswith("grouped"))
     torch.cuda.synchronize()
     assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
     assert same_bits(fused, sep)
@@ -400,6 +403,39 @@ def test_grouped_decode_bit_identical(group, part):
                              stream_kv=stream_kv, group_shared=True)
         assert same_bits(grouped, base)
     assert_close(w, grouped, ref, f"grouped g={group}")
+
+
+@pytest.mark.parametrize("group", [1, 4])
+@pytest.mark.parametrize("part", [0, 16, 64])
+def test_grouped_prefix_append(group, part):
+    """Grouped decode with the append folded in: the same cache bytes and output
+    bits as pa_write_kv then one-request-per-wave decode, over shared prefixes,
+    private suffixes (some of one token) and several partitions."""
+    say(f"grouped prefix append g={group} part={part}")
+    hkv = 2
+    w = inputs.shared_prefix(num_seqs=11, prefix_len=64, suffix_lo=1, suffix_hi=90,
+                             num_blocks=300, num_q_heads=hkv * group, num_kv_heads=hkv,
+                             device=DEV)
+    w.context_lens[2] = 65   # newest token alone in its block
+    poison_tails(w)
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                     w.max_context_len, w.scale, partition_tokens=part)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    for stream_kv in (False, True):
+        w.k_cache.copy_(k0)
+        w.v_cache.copy_(v0)
+        fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v,
+                                  w.block_tables, w.context_lens, w.max_context_len, w.scale,
+                                  partition_tokens=part, stream_kv=stream_kv, group_shared=True)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+        assert same_bits(fused, sep)
+    assert_close(w, fused, oracle_decode(w), f"grouped append g={group}")
 
 
 def test_grouped_fanout_step():
