@@ -697,16 +697,24 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
             }
         }
     }
-    auto store_new_tokens = [&]() {
+    auto store_new_tokens = [&]() {   // quarter-wave q stores member 4*it + q
 #pragma unroll
-        for (int r = 0; r < MAXR; ++r) {
-            int Lm;
-            if (!appends_here(r, Lm)) continue;
-            if (quad != r % 4) continue;
-            const int jl = (Lm - 1) / FBS - blk0;
-            const int om = (Lm - 1) % FBS;
-            const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(phys[r], jl)) *
-                                     blk_stride + static_cast<int64_t>(h) * FTILE;
+        for (int it = 0; it < kRounds; ++it) {
+            bool act = false;
+            int om = 0;
+            int64_t toff = 0;
+#pragma unroll
+            for (int q4 = 0; q4 < 4 && 4 * it + q4 < MAXR; ++q4) {
+                int Lm;
+                if (!appends_here(4 * it + q4, Lm) || quad != q4) continue;
+                const int jl = (Lm - 1) / FBS - blk0;
+                act = true;
+                om = (Lm - 1) % FBS;
+                toff = static_cast<int64_t>(__builtin_amdgcn_readlane(phys[4 * it + q4], jl)) * blk_stride +
+                       static_cast<int64_t>(h) * FTILE;
+            }
+            if (!act) continue;
+            const int r = 4 * it + quad;
             reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff)[row * FBS + om] = fresh_k[r][row];
             // V: sixteen consecutive dims per store, 512 B of the tile apart
             const short* fv = reinterpret_cast<const short*>(&fresh_v[r][0]);
