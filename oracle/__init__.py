@@ -34,4 +34,4 @@ example to pin against (the pages print no attention numbers); those are
 pinned only through the invariants and the library cross-check.
 """
 
-from . import blocks, paged  # noqa: F401
+from . import blocks, paged, prefix_cache  # noqa: F401

@@ -127,8 +127,11 @@ class BlockPool:
         return Sequence(table=list(seq.table), length=seq.length)
 
     def free(self, seq: Sequence) -> None:
-        """The request finishes: drop one reference to each of its blocks."""
-        for b in seq.table:
+        """The request finishes: drop one reference to each of its blocks.
+
+        The pages fix no order; blocks are released last to first, so the
+        free list hands back a request's tail before its head."""
+        for b in reversed(seq.table):
             self.release(b)
         seq.table = []
         seq.length = 0

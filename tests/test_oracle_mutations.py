@@ -11,6 +11,7 @@ import pytest
 
 from oracle import blocks as oblocks
 from oracle import paged
+from oracle import prefix_cache as opc
 from tests import pins
 
 _orig_attend = paged.attend
@@ -142,6 +143,73 @@ def _free_without_refcount(self, seq):
     seq.length = 0
 
 
+_orig_fnv = opc.fnv1a64
+_orig_register = opc.PrefixCachePool._register
+_orig_pc_append = opc.PrefixCachePool.append
+
+
+def _fnv_plain(data):                      # FNV-1 order: multiply, then xor
+    h = opc.FNV64_OFFSET
+    for byte in data:
+        h = (h * opc.FNV64_PRIME) & opc.MASK64
+        h ^= byte
+    return h
+
+
+def _key_without_parent(parent, tokens):
+    return _orig_fnv(b"".join(int(t).to_bytes(4, "little", signed=True) for t in tokens))
+
+
+def _lookup_unverified(self, parent, tokens):
+    h = opc.block_hash(parent, tokens)
+    return h, self.by_hash.get(h)
+
+
+def _release_evicts_early(self, block):
+    if self.refcount[block] <= 0:
+        raise oblocks.RefcountError("underflow")
+    self.refcount[block] -= 1
+    if block in self.key:
+        self.evictable[block] = None          # even while still in use
+    elif self.refcount[block] == 0:
+        self._free.append(block)
+
+
+def _allocate_newest_first(self):
+    if self._free:
+        b = self._free.pop()
+    elif self.evictable:
+        b, _ = self.evictable.popitem(last=True)
+        del self.by_hash[self.key.pop(b)[0]]
+    else:
+        raise oblocks.PoolExhausted("no free block")
+    self.refcount[b] = 1
+    return b
+
+
+def _pc_free_head_first(self, seq):
+    for b in seq.table:
+        self.release(b)
+    seq.table, seq.length, seq.tokens = [], 0, []
+
+
+def _pc_append_no_registration(self, seq, token):
+    res = oblocks.BlockPool.append(self, seq)
+    seq.tokens.append(int(token))
+    return res
+
+
+def _admit_registers_partial(self, tokens):
+    seq, hits = _orig_admit(self, tokens)
+    bs = self.block_size
+    if len(tokens) % bs:
+        _orig_register(self, seq.table[-1], seq.parent_hash, list(tokens[-(len(tokens) % bs):]))
+    return seq, hits
+
+
+_orig_admit = opc.PrefixCachePool.admit
+
+
 MUTATIONS = {
     "translate_swapped_divmod": (paged, "translate", _translate_swapped),
     "translate_slot_uses_logical": (paged, "translate", _translate_bad_slot),
@@ -159,6 +227,14 @@ MUTATIONS = {
     "copy_reversed": (paged, "copy_blocks", _copy_reversed),
     "append_without_cow": (oblocks.BlockPool, "append", _append_in_place),
     "free_ignores_refcount": (oblocks.BlockPool, "free", _free_without_refcount),
+    "fnv_multiply_before_xor": (opc, "fnv1a64", _fnv_plain),
+    "key_ignores_parent": (opc, "block_hash", _key_without_parent),
+    "lookup_trusts_hash": (opc.PrefixCachePool, "_lookup", _lookup_unverified),
+    "cached_block_evictable_in_use": (opc.PrefixCachePool, "release", _release_evicts_early),
+    "evict_newest_first": (opc.PrefixCachePool, "allocate", _allocate_newest_first),
+    "free_head_first": (opc.PrefixCachePool, "free", _pc_free_head_first),
+    "decode_blocks_not_registered": (opc.PrefixCachePool, "append", _pc_append_no_registration),
+    "partial_block_registered": (opc.PrefixCachePool, "admit", _admit_registers_partial),
 }
 
 
