@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
     PA_F32 = 0,   /* IEEE binary32 */
@@ -95,6 +95,8 @@ typedef enum {
     PA_ERR_WORKSPACE = 6,    /* workspace missing or smaller than pa_decode_workspace_bytes */
     PA_ERR_HIP = 7,          /* the HIP runtime reported an error (launch or query) */
     PA_ERR_VALIDATE = 8,     /* PA_VALIDATE=1 found an index outside its range */
+    PA_ERR_NO_SPACE = 9,     /* block manager: not enough free blocks (nothing was changed) */
+    PA_ERR_NOT_FOUND = 10,   /* block manager: unknown sequence id */
 } pa_status_t;
 
 /* Shape of one layer's paged KV cache. */
@@ -112,10 +114,10 @@ typedef struct {
 #define PA_DECODE_GROUP_SHARED 2u  /* consecutive requests may share leading blocks (a common
                                       prompt or prefix): the fast path then processes up to
                                       16 / (Hq/Hkv) consecutive requests per wave and reads a
-                                      block they all name only once.  Results equal the
-                                      ungrouped ones up to rounding (the per-request
-                                      partitions are unchanged; the tile order inside a
-                                      partition differs where members diverge). */
+                                      block they all name only once.  The output bits equal
+                                      the ungrouped ones: every request still sees its
+                                      tiles in logical order with the same partitions and
+                                      the same arithmetic. */
 #define PA_DECODE_STREAM_KV 1u  /* read K/V with non-temporal loads, which keeps them from
                                    displacing other cache contents.  A cache hint only:
                                    results are identical.  Measured on MI355X: +6..13% when

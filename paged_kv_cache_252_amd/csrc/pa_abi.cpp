@@ -277,6 +277,8 @@ const char* pa_status_string(int status) {
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
         case PA_ERR_VALIDATE: return "PA_ERR_VALIDATE";
+        case PA_ERR_NO_SPACE: return "PA_ERR_NO_SPACE";
+        case PA_ERR_NOT_FOUND: return "PA_ERR_NOT_FOUND";
         default: return "PA_ERR_UNKNOWN";
     }
 }

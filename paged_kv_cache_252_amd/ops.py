@@ -25,7 +25,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
-HEADER = os.path.join(os.path.dirname(HERE), "include", "pa.h")
+HEADERS = [os.path.join(os.path.dirname(HERE), "include", h) for h in ("pa.h", "pa_blocks.h")]
 
 PA_F32, PA_BF16 = 0, 1
 PA_DECODE_STREAM_KV = 1
@@ -104,6 +104,7 @@ def kv_pool(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
 _lib = None
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
 _SIGNATURES = {
     "pa_abi_version": (ctypes.c_int, []),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -121,6 +122,21 @@ _SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P,
                                         _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
+    # host-side block manager (include/pa_blocks.h)
+    "pa_bm_create": (ctypes.c_int, [_I64, _I32, ctypes.c_uint32, ctypes.c_uint64,
+                                    ctypes.POINTER(_P)]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_num_free": (_I64, [_P]),
+    "pa_bm_num_cached": (_I64, [_P]),
+    "pa_bm_add": (ctypes.c_int, [_P, _P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "pa_bm_fork": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I64)]),
+    "pa_bm_free": (ctypes.c_int, [_P, _I64]),
+    "pa_bm_append": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, ctypes.POINTER(_I32)]),
+    "pa_bm_slots": (ctypes.c_int, [_P, _I64, _I64, _I64, _P]),
+    "pa_bm_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P]),
+    "pa_bm_seq_info": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]),
+    "pa_bm_refcount": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_I32)]),
+    "pa_bm_block_key": (ctypes.c_uint64, [ctypes.c_uint64, _P, _I32]),
 }
 
 
@@ -141,11 +157,13 @@ def lib() -> ctypes.CDLL:
 
 
 def header_functions() -> list:
-    """Names of the functions ``include/pa.h`` declares."""
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+    """Names of the functions ``include/pa.h`` and ``include/pa_blocks.h`` declare."""
+    names = set()
+    for path in HEADERS:
+        with open(path) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def abi_version() -> int:
@@ -363,3 +381,118 @@ def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tabl
         float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
         _flags(stream_kv, group_shared), _stream(dev)))
     return out
+
+
+# ---- host-side block manager (include/pa_blocks.h) ---------------------------
+
+PA_BM_PREFIX_CACHE = 1
+
+
+def _host_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+class BlockManager:
+    """``pa_bm_*``: the pool's free list, reference counts, tables, growth,
+    fork, free, copy-on-write decisions and (optionally) the prefix cache of
+    full blocks.  Host-side: arguments and results are numpy arrays."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_cache: bool = False,
+                 salt: int = 0):
+        import numpy as np
+        self._np = np
+        self.block_size = block_size
+        h = ctypes.c_void_p()
+        _check("pa_bm_create", lib().pa_bm_create(
+            num_blocks, block_size, PA_BM_PREFIX_CACHE if prefix_cache else 0,
+            ctypes.c_uint64(salt & ((1 << 64) - 1)), ctypes.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    @property
+    def num_cached(self) -> int:
+        return int(lib().pa_bm_num_cached(self._h))
+
+    def add(self, num_tokens: int = 0, tokens=None) -> tuple:
+        """Admit a request; returns (seq_id, cached prompt tokens)."""
+        np = self._np
+        t = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+        n = num_tokens if t is None else int(t.size)
+        sid, cached = _I64(), _I64()
+        _check("pa_bm_add", lib().pa_bm_add(self._h, _host_ptr(t), n, ctypes.byref(sid),
+                                             ctypes.byref(cached)))
+        return sid.value, cached.value
+
+    def fork(self, parent: int) -> int:
+        child = _I64()
+        _check("pa_bm_fork", lib().pa_bm_fork(self._h, parent, ctypes.byref(child)))
+        return child.value
+
+    def free(self, seq_id: int) -> None:
+        _check("pa_bm_free", lib().pa_bm_free(self._h, seq_id))
+
+    def append(self, seq_ids, tokens=None) -> tuple:
+        """One decode step; returns (slots int64 [n], cow_pairs int64 [k, 2])."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = int(ids.size)
+        t = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+        if t is not None and t.size != n:
+            raise ValueError("one token id per request")
+        slots = np.empty(n, dtype=np.int64)
+        pairs = np.empty((n, 2), dtype=np.int64)
+        k = _I32()
+        _check("pa_bm_append", lib().pa_bm_append(self._h, _host_ptr(ids), _host_ptr(t), n,
+                                                   _host_ptr(slots), _host_ptr(pairs),
+                                                   ctypes.byref(k)))
+        return slots, pairs[:k.value].copy()
+
+    def slots(self, seq_id: int, start: int, count: int):
+        np = self._np
+        out = np.empty(count, dtype=np.int64)
+        _check("pa_bm_slots", lib().pa_bm_slots(self._h, seq_id, start, count, _host_ptr(out)))
+        return out
+
+    def tables(self, seq_ids, max_blocks: int) -> tuple:
+        """(tables int32 [n, max_blocks] with -1 padding, lens int32 [n])."""
+        np = self._np
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        n = int(ids.size)
+        tab = np.empty((n, max_blocks), dtype=np.int32)
+        lens = np.empty(n, dtype=np.int32)
+        _check("pa_bm_tables", lib().pa_bm_tables(self._h, _host_ptr(ids), n, max_blocks,
+                                                   _host_ptr(tab), _host_ptr(lens)))
+        return tab, lens
+
+    def seq_info(self, seq_id: int) -> tuple:
+        length, nb = _I64(), _I64()
+        _check("pa_bm_seq_info", lib().pa_bm_seq_info(self._h, seq_id, ctypes.byref(length),
+                                                       ctypes.byref(nb)))
+        return length.value, nb.value
+
+    def refcount(self, block: int) -> int:
+        r = _I32()
+        _check("pa_bm_refcount", lib().pa_bm_refcount(self._h, block, ctypes.byref(r)))
+        return r.value
+
+
+def block_key(parent: int, tokens) -> int:
+    """``pa_bm_block_key``: the prefix-cache key of one full block."""
+    import numpy as np
+    t = np.ascontiguousarray(tokens, dtype=np.int32)
+    return int(lib().pa_bm_block_key(ctypes.c_uint64(parent & ((1 << 64) - 1)), _host_ptr(t),
+                                      int(t.size)))

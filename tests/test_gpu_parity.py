@@ -568,3 +568,88 @@ def test_full_size_sampled(name):
         assert err <= BF16_TOL, f"{name} seq={seq} h={h}: err {err}"
     del w, out
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# the native block manager driving the device path
+# ----------------------------------------------------------------------------
+
+def _kv_of_prefix(prefix, hkv, d):
+    """K and V rows [2, Hkv, D] of a position, drawn from a seed that is a hash
+    of the token ids up to and including it: a stand-in for a model, in which
+    equal prefixes give equal keys and values."""
+    import hashlib
+    digest = hashlib.blake2b(np.asarray(prefix, dtype=np.int32).tobytes(), digest_size=8).digest()
+    rows = np.random.default_rng(int.from_bytes(digest, "little")).standard_normal((2, hkv, d))
+    return torch.from_numpy(rows.astype(np.float32)).to(torch.bfloat16)
+
+
+def test_block_manager_session():
+    """A session run by the native block manager with its prefix cache: three
+    prompts sharing a system prompt (the second and third skip the cached
+    span's prefill), two forked branches, then decode steps of copy-on-write
+    copies + token writes + decode.  After every step each request's gathered
+    history is exactly the keys and values of its own token prefixes (so the
+    cache shared only identical prefixes and every copy-on-write landed), and
+    decode, ungrouped and grouped, matches the oracle on the same pool."""
+    say("block manager session")
+    bs, hkv, hq, d, nb = 16, 2, 8, 128, 96
+    spec, kc, vc = ops.kv_pool(nb, bs, hkv, d, "bf16", DEV, fill=float("nan"))
+    bm = ops.BlockManager(nb, bs, prefix_cache=True, salt=3)
+    rng = np.random.default_rng(21)
+    system = rng.integers(0, 1000, size=3 * bs + 5).tolist()
+    tokens = {}
+
+    def write(slots, rows):
+        kv = torch.stack(rows)
+        ops.write_kv(spec, kc, vc, kv[:, 0].contiguous().to(DEV), kv[:, 1].contiguous().to(DEV),
+                     torch.as_tensor(np.asarray(slots, dtype=np.int64), device=DEV))
+
+    def admit(toks):
+        sid, cached = bm.add(tokens=np.asarray(toks, dtype=np.int32))
+        if len(toks) > cached:                        # prefill only the uncached span
+            write(bm.slots(sid, cached, len(toks) - cached),
+                  [_kv_of_prefix(toks[:p + 1], hkv, d) for p in range(cached, len(toks))])
+        tokens[sid] = list(toks)
+        return cached
+
+    assert admit(system + [1, 2, 3]) == 0
+    assert admit(system + [4]) == 3 * bs
+    assert admit(system[:2 * bs] + [9] * 7) == 2 * bs
+    live = sorted(tokens)
+    for _ in range(2):
+        kid = bm.fork(live[0])
+        tokens[kid] = list(tokens[live[0]])
+    live = sorted(tokens)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    for step in range(4):
+        new = rng.integers(0, 1000, size=len(live)).tolist()
+        slots, pairs = bm.append(live, new)
+        if step == 0:
+            assert len(pairs) >= 2                    # the branches diverge in a shared block
+        if len(pairs):
+            ops.copy_blocks(spec, kc, vc, torch.as_tensor(pairs, device=DEV))
+        for sid, t in zip(live, new):
+            tokens[sid].append(t)
+        write(slots, [_kv_of_prefix(tokens[sid], hkv, d) for sid in live])
+        tab, lens = bm.tables(live, 8)
+        tab_d = torch.as_tensor(tab, device=DEV)
+        lens_d = torch.as_tensor(lens, device=DEV)
+        for i, sid in enumerate(live):
+            kg, vg = ops.gather_kv(spec, kc, vc, tab_d[i].contiguous(), int(lens[i]))
+            want = torch.stack([_kv_of_prefix(tokens[sid][:p + 1], hkv, d)
+                                for p in range(int(lens[i]))])
+            assert torch.equal(bits(kg.cpu()), bits(want[:, 0])), (step, sid)
+            assert torch.equal(bits(vg.cpu()), bits(want[:, 1])), (step, sid)
+        q = torch.randn(len(live), hq, d, generator=gen, device=DEV).to(torch.bfloat16)
+        ref = paged.decode(to_np(q), to_np(kc), to_np(vc), tab, lens, d ** -0.5,
+                           num_kv_heads=hkv, block_size=bs, head_dim=d, dtype="bf16")
+        outs = []
+        for group in (False, True):
+            out = ops.decode(spec, q, kc, vc, tab_d, lens_d, int(lens.max()), d ** -0.5,
+                             group_shared=group)
+            got = paged.to_f64(to_np(out), "bf16")
+            assert np.isfinite(got).all() and float(np.max(np.abs(got - ref))) <= BF16_TOL
+            outs.append(out)
+        assert same_bits(outs[0], outs[1])
