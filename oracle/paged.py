@@ -251,6 +251,36 @@ def decode_one_head(q_group, k_pool, v_pool, block_table, context_len: int, kv_h
     return attend(to_f64(np.asarray(q_group), dtype), keys, values, scale)
 
 
+def prefill(q, q_start, k_pool, v_pool, block_tables, context_lens, scale: float,
+            num_kv_heads: int, block_size: int, head_dim: int, dtype: str) -> np.ndarray:
+    """Several new query tokens per request over the paged history.
+
+    ``q`` is ``[T][Hq][D]`` raw storage holding every request's query tokens
+    back to back: request i owns rows ``q_start[i] .. q_start[i+1]-1``.  They
+    are the request's last ``n_i`` positions (their keys and values are in the
+    cache, counted in ``context_lens[i] = L_i``), so its token j sits at
+    position ``L_i - n_i + j`` and sees positions ``0 .. L_i - n_i + j``: its
+    own and earlier ones, never a later one ([KG] "A Tiny Block-Table Example",
+    closing paragraphs).  A token at a negative position sees nothing and
+    gives zeros.  Returns fp64 ``[T][Hq][D]``.
+    """
+    q = np.asarray(q)
+    q_start = [int(x) for x in q_start]
+    total, num_q_heads, _ = q.shape
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    for i in range(len(q_start) - 1):
+        n = q_start[i + 1] - q_start[i]
+        L = int(context_lens[i])
+        kc, vc = gather_kv(k_pool, v_pool, block_tables[i], max(L, 0), num_kv_heads,
+                           block_size, head_dim, dtype)
+        keys, values = to_f64(kc, dtype), to_f64(vc, dtype)
+        for j in range(n):
+            visible = max(L - n + j + 1, 0)
+            row = q_start[i] + j
+            out[row] = attend(to_f64(q[row], dtype), keys[:visible], values[:visible], scale)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # cache writes
 # ----------------------------------------------------------------------------

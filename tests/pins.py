@@ -572,6 +572,73 @@ def check_prefix_collision_safe():
     assert cb == 0 and b.table[0] != a.table[0]
 
 
+# ---- several query tokens per request (chunked prefill) ----------------------
+
+def _pool_f32(k, v, bs):
+    """A pool in the documented layout, built by the scalar formulas, holding
+    rows ``k``/``v`` [L][Hkv][D] at identity placement (NaN elsewhere)."""
+    L, hkv, d = k.shape
+    x = 4
+    nb = max(paged.blocks_needed(L, bs), 1)
+    kp = np.full(nb * hkv * bs * d, np.nan, dtype=np.float32)
+    vp = np.full(nb * hkv * bs * d, np.nan, dtype=np.float32)
+    for t in range(L):
+        b, o = divmod(t, bs)
+        for h in range(hkv):
+            for e in range(d):
+                kp[(((b * hkv + h) * (d // x) + e // x) * bs + o) * x + e % x] = k[t, h, e]
+                vp[((b * hkv + h) * d + e) * bs + o] = v[t, h, e]
+    return kp.reshape(nb, -1), vp.reshape(nb, -1), nb
+
+
+def check_prefill_causal_sdpa(seed=41):
+    """A chunk of n query tokens at the end of an L-token history: token j sees
+    positions 0 .. L-n+j.  Checked against torch SDPA with that mask (fp64)."""
+    rng = np.random.default_rng(seed)
+    for (hq, hkv, d, bs, L, n) in ((2, 2, 16, 4, 9, 3), (8, 2, 16, 4, 23, 7), (4, 1, 8, 16, 12, 12),
+                                   (6, 3, 8, 1, 5, 1)):
+        k = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((L, hkv, d)).astype(np.float32)
+        q = rng.standard_normal((n, hq, d)).astype(np.float32)
+        kp, vp, nb = _pool_f32(k, v, bs)
+        scale = 0.7 / math.sqrt(d)
+        got = paged.prefill(q, [0, n], kp, vp, [list(range(nb))], [L], scale, hkv, bs, d, "f32")
+        g = hq // hkv
+        qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2).unsqueeze(0)
+        kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2).repeat_interleave(g, 0)
+        mask = torch.tensor([[t <= L - n + j for t in range(L)] for j in range(n)])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt.unsqueeze(0).contiguous(), vt.unsqueeze(0).contiguous(), attn_mask=mask,
+            scale=scale)
+        ref = ref[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got - ref)) <= 1e-12, np.max(np.abs(got - ref))
+
+
+def check_prefill_rows_are_decodes(seed=42):
+    """Each query token of a chunk is a decode over the history cut at its own
+    position; a one-token chunk is exactly ``decode``; several requests are
+    independent, and a token before position 0 sees nothing."""
+    w = _rand_workload(seed, num_seqs=3, len_lo=1, len_hi=23)
+    kp, vp = to_np(w.k_cache), to_np(w.v_cache)
+    bt, lens = to_np(w.block_tables), to_np(w.context_lens)
+    rng = np.random.default_rng(seed)
+    ns = [int(rng.integers(1, int(L) + 1)) for L in lens]
+    q_start = np.concatenate([[0], np.cumsum(ns)])
+    qf = rng.standard_normal((int(q_start[-1]), w.num_q_heads, w.head_dim)).astype(np.float32)
+    got = paged.prefill(qf, q_start, kp, vp, bt, lens, w.scale, **oracle_args(w))
+    for i in range(len(ns)):
+        for j in range(ns[i]):
+            pos = int(lens[i]) - ns[i] + j
+            one = paged.decode(qf[q_start[i] + j][None], kp, vp, bt[i:i + 1], [pos + 1],
+                               w.scale, **oracle_args(w))
+            assert np.array_equal(got[q_start[i] + j], one[0])
+    last = paged.decode(qf[q_start[1:] - 1], kp, vp, bt, lens, w.scale, **oracle_args(w))
+    assert np.array_equal(got[q_start[1:] - 1], last)
+    early = paged.prefill(qf[:3], [0, 3], kp, vp, bt[:1], [1], w.scale, **oracle_args(w))
+    assert not early[:2].any() and early[2].any()
+
+
 ALL_CHECKS = [
     check_worked_address, check_fixed_blocks_16, check_block_growth, check_tail_waste_bound,
     check_layout_contract, check_sdpa_identity_tables, check_closed_forms,
@@ -580,5 +647,5 @@ ALL_CHECKS = [
     check_refcount_free, check_fanout_scenario, check_fnv_vectors, check_block_key_chaining,
     check_prefix_admission, check_prefix_partial_block_private, check_prefix_eviction,
     check_prefix_in_use_not_evicted, check_prefix_decode_registration,
-    check_prefix_collision_safe,
+    check_prefix_collision_safe, check_prefill_causal_sdpa, check_prefill_rows_are_decodes,
 ]

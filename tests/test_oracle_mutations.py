@@ -208,6 +208,41 @@ def _admit_registers_partial(self, tokens):
 
 
 _orig_admit = opc.PrefixCachePool.admit
+_orig_prefill = paged.prefill
+
+
+def _prefill_positions_from_start(q, q_start, k_pool, v_pool, block_tables, context_lens, scale,
+                                  num_kv_heads, block_size, head_dim, dtype):
+    out = np.zeros((np.asarray(q).shape[0], np.asarray(q).shape[1], head_dim))
+    for i in range(len(q_start) - 1):
+        n = int(q_start[i + 1]) - int(q_start[i])
+        kc, vc = paged.gather_kv(k_pool, v_pool, block_tables[i], int(context_lens[i]),
+                                 num_kv_heads, block_size, head_dim, dtype)
+        for j in range(n):
+            r = int(q_start[i]) + j
+            out[r] = paged.attend(paged.to_f64(np.asarray(q)[r], dtype), paged.to_f64(kc, dtype)[:j + 1],
+                                  paged.to_f64(vc, dtype)[:j + 1], scale)
+    return out
+
+
+def _prefill_excludes_self(q, q_start, k_pool, v_pool, block_tables, context_lens, scale,
+                           num_kv_heads, block_size, head_dim, dtype):
+    lens = [max(int(L) - 1, 0) for L in context_lens]
+    return _orig_prefill(q, q_start, k_pool, v_pool, block_tables, lens, scale, num_kv_heads,
+                         block_size, head_dim, dtype)
+
+
+def _prefill_no_causal_mask(q, q_start, k_pool, v_pool, block_tables, context_lens, scale,
+                            num_kv_heads, block_size, head_dim, dtype):
+    out = np.zeros((np.asarray(q).shape[0], np.asarray(q).shape[1], head_dim))
+    for i in range(len(q_start) - 1):
+        L = int(context_lens[i])
+        kc, vc = paged.gather_kv(k_pool, v_pool, block_tables[i], L, num_kv_heads, block_size,
+                                 head_dim, dtype)
+        for r in range(int(q_start[i]), int(q_start[i + 1])):
+            out[r] = paged.attend(paged.to_f64(np.asarray(q)[r], dtype), paged.to_f64(kc, dtype),
+                                  paged.to_f64(vc, dtype), scale)
+    return out
 
 
 MUTATIONS = {
@@ -235,6 +270,9 @@ MUTATIONS = {
     "free_head_first": (opc.PrefixCachePool, "free", _pc_free_head_first),
     "decode_blocks_not_registered": (opc.PrefixCachePool, "append", _pc_append_no_registration),
     "partial_block_registered": (opc.PrefixCachePool, "admit", _admit_registers_partial),
+    "prefill_positions_from_start": (paged, "prefill", _prefill_positions_from_start),
+    "prefill_excludes_own_token": (paged, "prefill", _prefill_excludes_self),
+    "prefill_sees_future": (paged, "prefill", _prefill_no_causal_mask),
 }
 
 
