@@ -1,6 +1,6 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout]
+    python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout|prefill]
 
 A step is one pass of the whole hot path over one batch of synthetic
 requests: copy-on-write block copies (only the fan-out workload has any),
@@ -49,6 +49,10 @@ WORKLOADS = {
     "long": dict(make=inputs.long_context, replicas=1,
                  desc="long context: 8 requests, context U[32768,131072], 64 q / 8 KV heads, "
                       "head_dim 128, block 16, bf16, pool sized to fit"),
+    "prefill": dict(make=inputs.prefill_chunk, replicas=4,
+                    desc="chunked prefill after a prefix-cache hit: 16 requests, U[1024,3072] "
+                         "cached positions + 256 new query tokens each attending causally, "
+                         "32 q / 8 KV heads, head_dim 128, block 16, bf16"),
     "fanout": dict(make=inputs.fanout, replicas=1,
                    desc="fan-out step: 128 prompts x 4 branches, prompt U[256,2048] with a "
                         "partial last block, copy-on-write of that block per branch, one new "
@@ -169,6 +173,160 @@ def measured_traffic(workload: str, part: int, stream_kv: bool):
     return int(rec["traffic_bytes_per_launch"])
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(w) -> int:
+    """Matrix flops of one pa_prefill call: per query row and query head, 2*D
+    for the scores and 2*D for the values, times the positions it sees."""
+    lens = w.context_lens.cpu().numpy()
+    qs = w.q_start.cpu().numpy()
+    vis = 0
+    for i in range(w.num_seqs):
+        n = int(qs[i + 1] - qs[i])
+        L = int(lens[i])
+        vis += sum(max(L - n + j + 1, 0) for j in range(n))
+    return 4 * w.head_dim * w.num_q_heads * vis
+
+
+def cpu_baseline_prefill(w, budget_s: float = 10.0) -> dict:
+    """The CPU oracle's prefill on the first query rows of the first request."""
+    from oracle import paged
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        threads = 1
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    bt = host(w.block_tables[:1])
+    L = int(w.context_lens[0])
+    n = int(w.q_start[1] - w.q_start[0])
+    used = np.unique(bt[bt >= 0])
+    sel = torch.as_tensor(used, device=w.k_cache.device)
+    kp, vp = host(w.k_cache[sel]), host(w.v_cache[sel])
+    remap = np.full(w.num_blocks, -1, dtype=np.int64)
+    remap[used] = np.arange(used.size)
+    bt_c = np.where(bt >= 0, remap[np.maximum(bt, 0)], -1)
+    q = host(w.q_chunk[:n])
+    args = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim,
+                dtype=w.dtype)
+    done, flops = 0, 0
+    t0 = time.perf_counter()
+    while done < n and (time.perf_counter() - t0) < budget_s:
+        k = min(16, n - done)
+        # rows done .. done+k-1 of the chunk, as a chunk of their own ending at their last position
+        paged.prefill(q[done:done + k], [0, k], kp, vp, bt_c, [L - n + done + k], w.scale, **args)
+        flops += 4 * w.head_dim * w.num_q_heads * sum(L - n + j + 1 for j in range(done, done + k))
+        done += k
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {done} of {n} query rows of request 0 (context {L}), fp64, {dt:.2f} s",
+            "seconds": dt}
+
+
+def run_prefill(args, dev, copy_gbs) -> int:
+    """``--workload prefill``: a step writes each request's new chunk of K/V
+    (pa_write_kv) and runs pa_prefill for the chunk's queries."""
+    cfg = WORKLOADS["prefill"]
+    log("generating prefill")
+    w = cfg["make"](device=dev, poison=False)
+    spec = ops.CacheSpec.of(w)
+    reps = args.replicas or cfg["replicas"]
+    tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
+    max_len = w.max_context_len
+    qs = w.q_start.cpu().numpy()
+    lens = w.context_lens.cpu().numpy()
+    seq_ids, pos = [], []
+    for i in range(w.num_seqs):
+        n = int(qs[i + 1] - qs[i])
+        seq_ids += [i] * n
+        pos += list(range(int(lens[i]) - n, int(lens[i])))
+    seq_ids = torch.as_tensor(seq_ids, dtype=torch.int32, device=dev)
+    pos = torch.as_tensor(pos, dtype=torch.int32, device=dev)
+    slots = [ops.slot_mapping(w.block_size, t, pos, seq_ids) for t in tables]
+    total_q = w.q_chunk.shape[0]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    k_new = torch.randn((total_q, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(w.k_cache.dtype)
+    v_new = torch.randn((total_q, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(w.k_cache.dtype)
+    part = args.partition
+    need = ops.prefill_workspace_bytes(spec, w.num_seqs, total_q, w.max_q_len, w.num_q_heads,
+                                       max_len, part)
+    workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(w.q_chunk) for _ in tables]
+    log(f"{w.num_seqs} requests, {total_q} query rows, max len {max_len}, workspace {need} B, "
+        f"{reps} replicas")
+
+    def attend(r):
+        ops.prefill(spec, w.q_chunk, w.q_start, w.k_cache, w.v_cache, tables[r], w.context_lens,
+                    w.max_q_len, max_len, w.scale, out=outs[r], workspace=workspace,
+                    partition_tokens=part)
+
+    def step(r):
+        ops.write_kv(spec, w.k_cache, w.v_cache, k_new, v_new, slots[r])
+        attend(r)
+
+    for i in range(args.warmup):
+        step(i % reps)
+    for r in range(reps):
+        step(r)
+    torch.cuda.synchronize()
+    for r in range(1, reps):
+        if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
+            log("replica outputs differ")
+            return 1
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % reps)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.kernel_iters):
+        attend(i % reps)
+    ev1.record(stream)
+    ev1.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
+    flops = prefill_flops(w)
+    db = decode_bytes(w)
+    e = 2
+    qo = 2 * total_q * w.num_q_heads * w.head_dim * e
+    write = 2 * 2 * total_q * w.num_kv_heads * w.head_dim * e + 8 * total_q
+    step_bytes = db["kv_unique"] + qo + write
+    tflops = flops / (us * 1e-6) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg["desc"], "name": "prefill", "requests": w.num_seqs,
+                   "query_rows": total_q, "max_context_len": max_len, "replicas": reps,
+                   "partition_tokens": part},
+        "tokens_per_s": round(total_q / (ms * 1e-3), 1),
+        "copy_probe_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel": "pa_prefill", "flops_per_launch": flops,
+                     "kv_bytes_per_launch": db["kv_unique"], "avg_launch_us": round(us, 3),
+                     "kv_gbs": round(db["kv_unique"] / (us * 1e-6) / 1e9, 2)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline_prefill(w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def copy_probe(dev, mib: int) -> float:
     """Read+write GB/s of a plain device-to-device copy of ``mib`` MiB."""
     src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
@@ -217,6 +375,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copy_gbs = copy_probe(dev, args.copy_probe_mib) if args.copy_probe_mib > 0 else None
+    if args.workload == "prefill":
+        return run_prefill(args, dev, copy_gbs)
     cfg = WORKLOADS[args.workload]
     log(f"generating {args.workload}")
     w = cfg["make"](device=dev, poison=False)

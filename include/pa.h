@@ -302,6 +302,45 @@ int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, con
                      void* workspace, size_t workspace_bytes, int32_t partition_tokens,
                      uint32_t flags, void* stream);
 
+/*
+ * pa_prefill -- several new query tokens per request against the paged
+ * history: a chunk of a prompt whose earlier part is cached (e.g. found by
+ * the prefix cache), a chunked prefill, or several tokens checked at once.
+ *
+ * Request i's query tokens are rows q_start[i] .. q_start[i+1]-1 of q, n_i of
+ * them.  They are the request's last n_i positions and their K/V are already
+ * in the cache (pa_write_kv), counted in L = context_lens[i]; token j sits at
+ * position L - n_i + j and, for query head hq with h = hq / (Hq / Hkv), gives
+ *     s_t = scale * <q[row][hq], K_i[t][h]>      for t = 0 .. L - n_i + j
+ *     out[row][hq] = sum_t softmax(s)_t * V_i[t][h]
+ * -- its own position and earlier ones, never a later one ([KG] "A Tiny
+ * Block-Table Example", closing paragraphs).  A token whose position is
+ * negative (n_i > L) sees nothing and gives zeros.  With n_i = 1 this is
+ * pa_decode.
+ *
+ * Arguments: as pa_decode, plus
+ *   q, out        [total_q][Hq][head_dim] packed rows (dtype == c->dtype)
+ *   q_start       [num_seqs + 1] int32, q_start[0] = 0, non-decreasing,
+ *                 q_start[num_seqs] = total_q (device)
+ *   total_q       rows of q and out, 0 .. 65535 (host)
+ *   max_q_len     >= every n_i (host); sizes the grid
+ *   workspace     >= pa_prefill_workspace_bytes(...) bytes
+ *   flags         0
+ * Compiled set: bf16, head_dim 128, block_size 16, Hq/Hkv dividing 16; other
+ * shapes return PA_ERR_UNSUPPORTED.  Indices and row offsets read on the
+ * device are clamped into range (no fault); PA_VALIDATE=1 rejects them.
+ */
+size_t pa_prefill_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+               const void* q, const int32_t* q_start, const int32_t* block_tables,
+               const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+               int32_t max_q_len, int32_t num_q_heads, int32_t max_blocks_per_seq,
+               int32_t max_context_len, float scale, void* out, void* workspace,
+               size_t workspace_bytes, int32_t partition_tokens, uint32_t flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

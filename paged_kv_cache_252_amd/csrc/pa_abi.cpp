@@ -164,6 +164,51 @@ int check_heads(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads)
     return PA_OK;
 }
 
+// Several query tokens per request: 16 / g tokens per wave.
+bool prefill_shape_ok(const pa_cache_desc_t* c, int group) {
+    return fast_path_ok(c, group) && 16 % group == 0;
+}
+
+int64_t prefill_waves_rows(int32_t num_seqs, int32_t max_q_len, int group) {
+    const int per = 16 / group;
+    return static_cast<int64_t>(num_seqs) * ceil_div(std::max(max_q_len, 0), per);
+}
+
+// The partials of decode's layout for total_q rows, then the rows' visible
+// lengths [total_q] int32 (for the merge).
+size_t prefill_workspace(const pa_cache_desc_t* c, int32_t total_q, int32_t num_q_heads,
+                         int32_t max_context_len, int32_t part) {
+    const size_t partials = workspace_bytes(c, total_q, num_q_heads, max_context_len, part);
+    if (partials == 0) return 0;
+    return partials + static_cast<size_t>(ceil_div(static_cast<int64_t>(total_q) * 4, 16) * 16);
+}
+
+// A prefill wave walks any number of 64-block chunks, so its partition is not
+// capped at 1024 tokens: the history is split only when there are too few
+// (request, query tile, KV head) waves to fill the device.
+constexpr int32_t kMaxPrefillPartitionTokens = 1 << 20;
+
+int prefill_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t max_q_len,
+                      int32_t num_q_heads, int32_t max_context_len, int32_t requested,
+                      int32_t* out) {
+    if (requested != 0) {
+        if (requested < 16 || requested > kMaxPrefillPartitionTokens || requested % 16 != 0)
+            return fail(PA_ERR_SHAPE, "partition_tokens %d must be a multiple of 16 in [16, %d]",
+                        requested, kMaxPrefillPartitionTokens);
+        *out = requested;
+        return PA_OK;
+    }
+    const int64_t waves = prefill_waves_rows(num_seqs, max_q_len, num_q_heads / c->num_kv_heads) *
+                          c->num_kv_heads;
+    const int64_t target = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
+    const int64_t whole = std::max<int64_t>(ceil_div(std::max(max_context_len, 1), 16) * 16, 16);
+    const int64_t splits = std::max<int64_t>(1, ceil_div(target, std::max<int64_t>(waves, 1)));
+    int64_t p = ceil_div(ceil_div(whole, splits), 16) * 16;
+    p = std::max<int64_t>(std::min<int64_t>(p, whole), std::min<int64_t>(whole, kMinAutoPartitionTokens));
+    *out = static_cast<int32_t>(std::min<int64_t>(p, kMaxPrefillPartitionTokens));
+    return PA_OK;
+}
+
 }  // namespace
 }  // namespace pa
 
@@ -401,6 +446,128 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
     return decode_impl("pa_decode", c, k_cache, v_cache, nullptr, nullptr, q, block_tables,
                        context_lens, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
                        scale, out, workspace, workspace_bytes, partition_tokens, flags, stream);
+}
+
+size_t pa_prefill_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, int32_t total_q,
+                                  int32_t max_q_len, int32_t num_q_heads,
+                                  int32_t max_context_len, int32_t partition_tokens) {
+    if (check_desc(c) || check_heads(c, num_seqs, num_q_heads) || total_q < 0 || max_q_len < 0)
+        return 0;
+    int32_t part = 0;
+    if (prefill_partition(c, num_seqs, max_q_len, num_q_heads, max_context_len, partition_tokens, &part))
+        return 0;
+    return prefill_workspace(c, total_q, num_q_heads, max_context_len, part);
+}
+
+int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
+               const void* q, const int32_t* q_start, const int32_t* block_tables,
+               const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+               int32_t max_q_len, int32_t num_q_heads, int32_t max_blocks_per_seq,
+               int32_t max_context_len, float scale, void* out, void* workspace,
+               size_t workspace_bytes_given, int32_t partition_tokens, uint32_t flags,
+               void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
+    const int group = num_q_heads / c->num_kv_heads;
+    if (!prefill_shape_ok(c, group))
+        return fail(PA_ERR_UNSUPPORTED,
+                    "pa_prefill supports bf16, head_dim 128, block_size 16 and Hq/Hkv dividing 16");
+    if (total_q < 0 || total_q > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "total_q %d outside [0, %d]", total_q, kMaxGridYZ);
+    if (max_q_len < 0) return fail(PA_ERR_SHAPE, "max_q_len %d < 0", max_q_len);
+    if (max_blocks_per_seq < 1) return fail(PA_ERR_SHAPE, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+    if (max_context_len < 0) return fail(PA_ERR_SHAPE, "max_context_len %d < 0", max_context_len);
+    if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * c->block_size)
+        return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
+                    max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
+    if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+    if (flags != 0) return fail(PA_ERR_UNSUPPORTED, "unknown prefill flags 0x%x", flags);
+    const int64_t rows = prefill_waves_rows(num_seqs, max_q_len, group);
+    if (rows > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "num_seqs * ceil(max_q_len / %d) = %lld exceeds %d", 16 / group,
+                    (long long)rows, kMaxGridYZ);
+    if (num_seqs == 0 || total_q == 0) return ok();
+    if (!k_cache || !v_cache || !q || !q_start || !block_tables || !context_lens || !out)
+        return fail(PA_ERR_NULL, "pa_prefill: a required pointer is NULL");
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
+        return fail(PA_ERR_ALIGN, "pa_prefill: caches, q and out must be 16-byte aligned");
+    int32_t part = 0;
+    if ((st = prefill_partition(c, num_seqs, max_q_len, num_q_heads, max_context_len, partition_tokens, &part)))
+        return st;
+    const size_t need = prefill_workspace(c, total_q, num_q_heads, max_context_len, part);
+    if (need > 0) {
+        if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_prefill needs %zu bytes of workspace, got NULL", need);
+        if (workspace_bytes_given < need)
+            return fail(PA_ERR_WORKSPACE, "pa_prefill needs %zu bytes of workspace, got %zu", need,
+                        workspace_bytes_given);
+        if (!aligned16(workspace)) return fail(PA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
+    hipStream_t s = as_stream(stream);
+    if (validate_enabled()) {
+        std::vector<int32_t> starts, lens, tables;
+        if ((st = fetch(starts, q_start, static_cast<size_t>(num_seqs) + 1, s))) return st;
+        if ((st = fetch(lens, context_lens, num_seqs, s))) return st;
+        if ((st = fetch(tables, block_tables, static_cast<size_t>(num_seqs) * max_blocks_per_seq, s))) return st;
+        if (starts[0] != 0 || starts[num_seqs] != total_q)
+            return fail(PA_ERR_VALIDATE, "q_start must run from 0 to total_q = %d", total_q);
+        for (int32_t i = 0; i < num_seqs; ++i) {
+            const int32_t n = starts[i + 1] - starts[i];
+            if (n < 0 || n > max_q_len)
+                return fail(PA_ERR_VALIDATE, "request %d has %d query tokens (max_q_len %d)", i, n, max_q_len);
+            const int32_t L = lens[i];
+            if (L < 0 || L > max_context_len)
+                return fail(PA_ERR_VALIDATE, "context_lens[%d] = %d outside [0, %d]", i, L, max_context_len);
+            const int32_t nb = (L + c->block_size - 1) / c->block_size;
+            for (int32_t j = 0; j < nb; ++j) {
+                const int32_t b = tables[static_cast<size_t>(i) * max_blocks_per_seq + j];
+                if (b < 0 || b >= c->num_blocks)
+                    return fail(PA_ERR_VALIDATE, "block_tables[%d][%d] = %d outside [0, %lld)", i, j, b,
+                                (long long)c->num_blocks);
+            }
+        }
+    }
+    const int64_t parts64 = std::max<int64_t>(1, ceil_div(max_context_len, part));
+    if (parts64 > kMaxGridYZ)
+        return fail(PA_ERR_SHAPE, "max_context_len %d needs %lld partitions of %d tokens (> %d)",
+                    max_context_len, (long long)parts64, part, kMaxGridYZ);
+    PrefillArgs p;
+    DecodeArgs& a = p.d;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.q = q;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.num_blocks = c->num_blocks;
+    a.block_stride = block_stride(c);
+    a.block_size = c->block_size;
+    a.num_kv_heads = c->num_kv_heads;
+    a.head_dim = c->head_dim;
+    a.dtype = c->dtype;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.group = group;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.len_clamp = max_context_len;
+    a.part_tokens = part;
+    a.max_parts = static_cast<int32_t>(parts64);
+    a.scale = scale;
+    a.flags = 0;
+    a.out = out;
+    const size_t slots = static_cast<size_t>(total_q) * num_q_heads * a.max_parts;
+    float* ws = need ? static_cast<float*>(workspace) : nullptr;
+    a.ws_acc = ws;
+    a.ws_m = need ? ws + slots * c->head_dim : nullptr;
+    a.ws_l = need ? ws + slots * (c->head_dim + 1) : nullptr;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.stream = s;
+    p.q_start = q_start;
+    p.total_q = total_q;
+    p.max_q_len = max_q_len;
+    p.ws_len = need ? reinterpret_cast<int32_t*>(ws + slots * (c->head_dim + 2)) : nullptr;
+    if ((st = launch_prefill(p))) return st;
+    return ok();
 }
 
 int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,

@@ -1095,6 +1095,142 @@ int launch_grouped_r(const DecodeArgs& a) {
     return launch_grouped<16, NT, APPEND>(a, members);
 }
 
+// ============================================================================
+// Several query tokens per request (chunked prefill, several-token checks)
+// ============================================================================
+//
+// A request's query tokens are its last n positions: token j (position
+// L - n + j) sees positions [0, L - n + j] ([KG] "A Tiny Block-Table
+// Example", closing paragraphs: never a later token).  One wave takes 16/g
+// consecutive tokens of one request and KV head: MFMA row r is token
+// j0 + r / g, query head h * g + r % g.  All rows read the same physical
+// blocks, so each tile is loaded once for the wave and masked row by row;
+// the partitions and their merge are those of decode, per query row.
+template <bool NT>
+__global__ __launch_bounds__(64) void prefill_kernel(
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int64_t num_blocks, int64_t blk_stride, int total_q, int num_q_heads, int group,
+    int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
+    float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
+    const int h = blockIdx.x;
+    const int seq = blockIdx.y / tiles_per_seq;
+    const int tile = blockIdx.y - seq * tiles_per_seq;
+    const int part = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int row = lane & 15;
+    const int quad = lane >> 4;
+    auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+
+    // rows are clamped to [0, total_q): a bad q_start cannot move an access
+    const int qs = clampi(q_start[seq], 0, total_q);
+    const int n = clampi(q_start[seq + 1], qs, total_q) - qs;
+    const int per = FG / group;                 // query tokens per wave
+    const int j0 = tile * per;
+    if (j0 >= n) return;
+    const int L = clampi(context_lens[seq], 0, len_clamp);
+    const int j = j0 + row / group;
+    const bool row_ok = j < n;
+    const int qi = qs + (row_ok ? j : j0);
+    const int hq = h * group + row % group;
+    const int lim = row_ok ? clampi(L - n + j + 1, 0, L) : 0;   // positions this row sees
+    const int lim_min = clampi(L - n + j0 + 1, 0, L);
+    const int lim_max = clampi(L - n + min(j0 + per, n), 0, L);
+
+    if (max_parts > 1 && part == 0 && h == 0 && row_ok && row % group == 0 && quad == 0)
+        ws_len[qi] = lim;                       // the merge's per-row partition count
+    auto write_zero_row = [&]() {
+        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+    };
+    const int tok0 = part * part_tokens;
+    if (tok0 >= lim_max) {
+        if (part == 0 && row_ok && lim == 0) write_zero_row();
+        return;
+    }
+    const int tok1 = min(lim_max, tok0 + part_tokens);
+
+    bf16x8 qv[4];
+    {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            q + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            bf16x8 v = qp[4 * s4 + quad];
+            qv[s4] = row_ok ? v : bf16x8{};
+        }
+    }
+    SoftmaxState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) st.acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
+    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
+    // The partition is walked in chunks of 64 blocks, one table entry per lane.
+    for (int c0 = tok0; c0 < tok1; c0 += 64 * FBS) {
+        const int blk0 = c0 / FBS;
+        const int nblk = (min(tok1, c0 + 64 * FBS) - c0 + FBS - 1) / FBS;   // 1..64
+        const int my_phys = lane < nblk
+            ? clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
+                          num_blocks)
+            : 0;
+        auto load_blk = [&](Tile& t, int b) {
+            const int64_t o = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, b)) * blk_stride;
+            load_tile<NT>(t, k_head + o, v_head + o, lane);
+        };
+        auto consume_blk = [&](Tile& t, int b) {
+            const int start = c0 + FBS * b;
+            const int row_valid = clampi(lim - start, 0, FBS);
+            const int v_valid = clampi(lim_max - start, 0, FBS);
+            consume_tile_rows(st, t, qv, scale_log2, lane, row_valid, v_valid, start + FBS > lim_min);
+        };
+        // two tiles in flight; past the end the prefetch repeats the last tile
+        Tile ta, tb;
+        load_blk(ta, 0);
+        for (int b = 0; b < nblk; b += 2) {
+            load_blk(tb, min(b + 1, nblk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            consume_blk(ta, b);
+            __builtin_amdgcn_sched_barrier(0);
+            if (b + 1 >= nblk) break;
+            load_blk(ta, min(b + 2, nblk - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            consume_blk(tb, b + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    const float lsum = sum_across_rows(st.l);
+    if (!row_ok) return;
+    if (tok0 >= lim) {                          // nothing of this partition is visible
+        if (part == 0 && lim == 0) write_zero_row();
+        return;
+    }
+    const int my_nparts = (lim + part_tokens - 1) / part_tokens;
+    if (my_nparts == 1) {
+        const float inv = 1.f / lsum;
+        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
+                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
+        return;
+    }
+    const int64_t pidx = (static_cast<int64_t>(qi) * num_q_heads + hq) * max_parts + part;
+    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
+    if (quad == 0) {
+        ws_m[pidx] = st.m;
+        ws_l[pidx] = lsum;
+    }
+}
+
 }  // namespace
 
 int launch_decode(const DecodeArgs& a) {
@@ -1118,6 +1254,27 @@ int launch_decode(const DecodeArgs& a) {
     }
     if (a.dtype == PA_BF16) return launch_generic_d<uint16_t>(a);
     return launch_generic_d<float>(a);
+}
+
+int launch_prefill(const PrefillArgs& p) {
+    const DecodeArgs& a = p.d;
+    const int per = FG / a.group;
+    const int tiles = (p.max_q_len + per - 1) / per;
+    if (a.num_seqs == 0 || tiles == 0) return PA_OK;
+    dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
+    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(64), 0, a.stream,
+                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
+                       static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
+                       a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
+                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts,
+                       a.scale * kLog2e, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       p.ws_len);
+    int st = check_launch("prefill");
+    if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
+    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, p.total_q), dim3(kMergeThreads),
+                       0, a.stream, p.ws_len, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
+                       a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
+    return check_launch("prefill reduce");
 }
 
 }  // namespace pa

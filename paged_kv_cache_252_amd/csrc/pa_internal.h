@@ -88,6 +88,17 @@ struct DecodeArgs {
 
 int launch_decode(const DecodeArgs& a);
 
+// Several query tokens per request: the DecodeArgs fields above plus these.
+struct PrefillArgs {
+    DecodeArgs d;            // num_seqs, q (packed rows), out (packed rows), ws_* per query row
+    const int32_t* q_start;  // [num_seqs + 1] row offsets of each request's query tokens
+    int32_t total_q;         // rows of q and out
+    int32_t max_q_len;       // longest chunk; sizes the grid
+    int32_t* ws_len;         // [total_q] visible positions per query row, for the merge
+};
+
+int launch_prefill(const PrefillArgs& a);
+
 int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
                     const void* v_new, const int64_t* slots, int32_t num_tokens,
                     hipStream_t stream);

@@ -69,6 +69,9 @@ class Workload:
     # structure, for tests: which blocks are shared by several tables
     shared_blocks: np.ndarray | None = None
     parent_tables: list | None = None        # fan-out: the prompt tables before copy-on-write
+    q_chunk: torch.Tensor | None = None      # packed [total, Hq, D] queries of the last positions
+    q_start: torch.Tensor | None = None      # int32 [S + 1] row offsets into q_chunk
+    max_q_len: int = 0
     extra: dict = field(default_factory=dict)
 
     @property
@@ -321,6 +324,36 @@ def add_step_tokens(w: Workload) -> Workload:
     return w
 
 
+def add_query_chunks(w: Workload, chunk_lens) -> Workload:
+    """Give request i a chunk of ``chunk_lens[i]`` query tokens: its last
+    positions, whose K/V are already in the cache.  Sets ``w.q_chunk`` (packed
+    [total, Hq, D], N(0,1)), ``w.q_start`` (int32 [S + 1]) and
+    ``w.max_q_len``."""
+    dev = w.q.device
+    n = [int(c) for c in chunk_lens]
+    if len(n) != w.num_seqs or min(n, default=0) < 0:
+        raise ValueError("one non-negative chunk length per request")
+    start = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    w.q_chunk = _values(w.extra["gen"], (int(start[-1]), w.num_q_heads, w.head_dim), w.dtype, dev)
+    w.q_start = torch.as_tensor(start, device=dev)
+    w.max_q_len = max(n, default=0)
+    return w
+
+
+def prefill_chunk(seed: int = 5, device="cpu", poison: bool = True, num_seqs: int = 16,
+                  cached_lo: int = 1024, cached_hi: int = 3072, chunk: int = 256,
+                  num_blocks: int = 65536) -> Workload:
+    """Chunked prefill after a prefix-cache hit: ``num_seqs`` requests, each
+    with U[cached_lo, cached_hi] cached positions followed by ``chunk`` new
+    ones whose queries attend causally; 32 q / 8 KV heads, D 128, bs 16,
+    bf16, blocks shuffled from the pool."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = (rng.integers(cached_lo, cached_hi, size=num_seqs, endpoint=True) + chunk).tolist()
+    w = paged_random("prefill", num_seqs, 0, cached_hi + chunk, 32, 8, seed=seed,
+                     num_blocks=num_blocks, device=device, poison=poison, lens=lens)
+    return add_query_chunks(w, [chunk] * num_seqs)
+
+
 def replicate(w: Workload, replicas: int, seed_offset: int = 1000) -> list:
     """Tables for ``replicas`` copies of the workload at disjoint physical blocks.
 
@@ -360,4 +393,5 @@ PRESETS = {
     "prefix": shared_prefix,
     "long": long_context,
     "fanout": fanout,
+    "prefill": prefill_chunk,
 }

@@ -122,6 +122,11 @@ _SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P,
                                         _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
+    "pa_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32,
+                                                     _I32, _I32, _I32]),
+    "pa_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                  _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                  _I32, ctypes.c_uint32, _P]),
     # host-side block manager (include/pa_blocks.h)
     "pa_bm_create": (ctypes.c_int, [_I64, _I32, ctypes.c_uint32, ctypes.c_uint64,
                                     ctypes.POINTER(_P)]),
@@ -380,6 +385,49 @@ def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tabl
         _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1], max_context_len,
         float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
         _flags(stream_kv, group_shared), _stream(dev)))
+    return out
+
+
+def prefill_workspace_bytes(spec: CacheSpec, num_seqs: int, total_q: int, max_q_len: int,
+                            num_q_heads: int, max_context_len: int,
+                            partition_tokens: int = 0) -> int:
+    d = spec.desc()
+    return int(lib().pa_prefill_workspace_bytes(ctypes.byref(d), num_seqs, total_q, max_q_len,
+                                                num_q_heads, max_context_len, partition_tokens))
+
+
+def prefill(spec: CacheSpec, q, q_start, k_cache, v_cache, block_tables, context_lens,
+            max_q_len: int, max_context_len: int, scale: float, out=None, workspace=None,
+            partition_tokens: int = 0):
+    """``pa_prefill``: each request's last n_i positions as queries (rows
+    ``q_start[i] .. q_start[i+1]-1`` of the packed ``q`` [total_q, Hq, head_dim]),
+    each seeing its own and earlier positions.  Returns ``out`` like ``q``."""
+    dev = _cache_pair(spec, k_cache, v_cache)
+    _need(q, "q", spec.torch_dtype, dev)
+    _need(q_start, "q_start", torch.int32, dev)
+    _need(block_tables, "block_tables", torch.int32, dev)
+    _need(context_lens, "context_lens", torch.int32, dev)
+    if q.dim() != 3 or q.shape[2] != spec.head_dim:
+        raise ValueError("q must be [total_q, Hq, head_dim]")
+    s = context_lens.numel()
+    if q_start.numel() != s + 1 or block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("q_start must be [num_seqs + 1] and block_tables [num_seqs, max_blocks]")
+    total_q, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", spec.torch_dtype, dev)
+    need = prefill_workspace_bytes(spec, s, total_q, max_q_len, hq, max_context_len,
+                                   partition_tokens)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = spec.desc()
+    _check("pa_prefill", lib().pa_prefill(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q),
+                                          _ptr(q_start), _ptr(block_tables), _ptr(context_lens), s,
+                                          total_q, max_q_len, hq, block_tables.shape[1],
+                                          max_context_len, float(scale), _ptr(out),
+                                          _ptr(workspace), ws_bytes, partition_tokens, 0,
+                                          _stream(dev)))
     return out
 
 

@@ -108,3 +108,29 @@ def test_cache_op_argument_checks(lib):
     assert lib.pa_slot_mapping(0, p, 1, 1, None, p, 1, p, None) == 2
     assert lib.pa_slot_mapping(16, p, 1, 1, None, None, 1, p, None) == 1
     assert lib.pa_gather_kv(ctypes.byref(d), p, p, p, -1, p, p, None) == 2
+
+
+def _prefill(lib, d, num_seqs=2, total_q=4, max_q_len=2, num_q_heads=32, max_blocks=4,
+             max_len=64, part=0, flags=0, scale=0.1):
+    p = ctypes.c_void_p(1 << 20)
+    return lib.pa_prefill(ctypes.byref(d), p, p, p, p, p, p, num_seqs, total_q, max_q_len,
+                          num_q_heads, max_blocks, max_len, scale, p, p, 1 << 30, part, flags, None)
+
+
+def test_prefill_argument_checks(lib):
+    """pa_prefill rejects what it cannot run before touching the device."""
+    d = _desc()
+    assert _prefill(lib, d, num_q_heads=24) == 5                   # g = 3 does not divide 16
+    assert _prefill(lib, _desc(dtype=0, head_dim=32)) == 5         # outside the compiled set
+    assert _prefill(lib, d, total_q=-1) == 2
+    assert _prefill(lib, d, total_q=70000) == 2
+    assert _prefill(lib, d, max_q_len=-3) == 2
+    assert _prefill(lib, d, max_len=65) == 2                       # beyond table capacity
+    assert _prefill(lib, d, flags=1) == 5
+    assert _prefill(lib, d, part=24) == 2
+    assert _prefill(lib, d, num_seqs=40000, max_q_len=8) == 2      # grid rows above 65535
+    assert _prefill(lib, d, num_seqs=0) == 0                        # nothing to do
+    assert _prefill(lib, d, total_q=0) == 0
+    ws = lib.pa_prefill_workspace_bytes(ctypes.byref(d), 2, 4, 2, 32, 64, 16)
+    assert ws == 4 * 32 * 4 * (128 + 2) * 4 + 16                    # partials + row lengths
+    assert lib.pa_prefill_workspace_bytes(ctypes.byref(d), 2, 4, 2, 32, 16, 16) == 0

@@ -653,3 +653,104 @@ def test_block_manager_session():
             assert np.isfinite(got).all() and float(np.max(np.abs(got - ref))) <= BF16_TOL
             outs.append(out)
         assert same_bits(outs[0], outs[1])
+
+
+# ----------------------------------------------------------------------------
+# several query tokens per request (pa_prefill)
+# ----------------------------------------------------------------------------
+
+def _oracle_prefill(w, rows=None):
+    return paged.prefill(to_np(w.q_chunk), to_np(w.q_start), to_np(w.k_cache), to_np(w.v_cache),
+                         to_np(w.block_tables), to_np(w.context_lens), w.scale, **oracle_args(w))
+
+
+def _run_prefill(w, **kw):
+    spec = ops.CacheSpec.of(w)
+    return ops.prefill(spec, w.q_chunk, w.q_start, w.k_cache, w.v_cache, w.block_tables,
+                       w.context_lens, w.max_q_len, w.max_context_len, w.scale, **kw)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("part", [0, 16, 64])
+def test_prefill_matches_oracle(group, part):
+    """Chunks of 0..L query tokens (whole prompts, single tokens, empty
+    chunks, chunks longer than the history) against the oracle."""
+    say(f"prefill g={group} part={part}")
+    hkv = 2
+    lens = [1, 15, 16, 17, 40, 100, 0, 77, 33]
+    w = inputs.paged_random("pf", len(lens), 0, 100, hkv * group, hkv, num_blocks=200, seed=61,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    chunks = [1, 15, 3, 17, 40, 9, 2, 0, 35]          # request 6 (L = 0) and 8 (n > L) see nothing early
+    inputs.add_query_chunks(w, chunks)
+    out = _run_prefill(w, partition_tokens=part)
+    assert_close(w, out, _oracle_prefill(w), f"prefill g={group}")
+
+
+def test_prefill_one_token_equals_decode():
+    """A one-token chunk per request is a decode: with the same partitions,
+    the same bits as pa_decode."""
+    say("prefill one token == decode")
+    for part in (32, 256, 1024):
+        w = inputs.paged_random("pf1", 12, 1, 700, 32, 8, num_blocks=800, seed=62, device=DEV)
+        poison_tails(w)
+        inputs.add_query_chunks(w, [1] * w.num_seqs)
+        w.q = w.q_chunk.view(w.num_seqs, w.num_q_heads, w.head_dim)
+        got = _run_prefill(w, partition_tokens=part)
+        want = run_decode(w, partition_tokens=part)
+        assert same_bits(got.view_as(want), want)
+
+
+def test_prefill_placement_invariance():
+    """Moving the blocks (pool rows and table entries together) changes no bit."""
+    say("prefill placement invariance")
+    w = inputs.paged_random("pfp", 5, 20, 300, 32, 8, num_blocks=200, seed=63, device=DEV)
+    inputs.add_query_chunks(w, [7, 20, 1, 64, 33])
+    a = _run_prefill(w, partition_tokens=64)
+    perm = torch.randperm(w.num_blocks, generator=torch.Generator().manual_seed(3)).to(DEV)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(w.num_blocks, device=DEV)
+    k2, v2 = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache[perm] = k2
+    w.v_cache[perm] = v2
+    bt = w.block_tables.clone()
+    ok = bt >= 0
+    bt[ok] = perm[bt[ok].long()].int()
+    w.block_tables = bt
+    b = _run_prefill(w, partition_tokens=64)
+    assert same_bits(a, b)
+
+
+def test_prefill_full_size_sampled():
+    """Chunked prefill after a cache hit (16 requests, 1024..3072 cached + 256
+    new tokens, 32q/8kv) in the launch configuration the benchmark times;
+    sampled query rows checked against the oracle one by one."""
+    say("prefill full size sampled")
+    w = inputs.prefill_chunk(device=DEV, poison=True)
+    out = to_np(_run_prefill(w))
+    split = to_np(_run_prefill(w, partition_tokens=512))       # split + merge route too
+    rng = np.random.default_rng(64)
+    kp, vp, bt = to_np(w.k_cache), to_np(w.v_cache), to_np(w.block_tables)
+    lens, qs, qn = to_np(w.context_lens), to_np(w.q_start), to_np(w.q_chunk)
+    for i in rng.choice(w.num_seqs, size=4, replace=False):
+        n = int(qs[i + 1] - qs[i])
+        for j in [0, n - 1, int(rng.integers(0, n))]:
+            row = int(qs[i]) + j
+            ref = paged.prefill(qn[row:row + 1], [0, 1], kp, vp, bt[i:i + 1],
+                                [int(lens[i]) - n + j + 1], w.scale, **oracle_args(w))
+            for o in (out, split):
+                got = paged.to_f64(o[row:row + 1], "bf16")
+                assert np.max(np.abs(got - ref)) <= BF16_TOL, (i, j)
+
+
+def test_prefill_validate_rejects_bad_offsets(monkeypatch):
+    say("prefill PA_VALIDATE")
+    monkeypatch.setenv("PA_VALIDATE", "1")
+    w = inputs.paged_random("pfv", 3, 10, 40, 8, 2, num_blocks=64, seed=65, device=DEV)
+    inputs.add_query_chunks(w, [2, 3, 4])
+    bad = w.q_start.clone()
+    bad[1] = 7                                      # request 0 claims 7 > max_q_len rows
+    with pytest.raises(ops.PagedKVError) as e:
+        ops.prefill(ops.CacheSpec.of(w), w.q_chunk, bad, w.k_cache, w.v_cache, w.block_tables,
+                    w.context_lens, w.max_q_len, w.max_context_len, w.scale)
+    assert e.value.status == 8
