@@ -137,13 +137,23 @@ def tail_waste(num_tokens: int, block_size: int) -> int:
 # the in-block layout (library contract) seen through numpy views
 # ----------------------------------------------------------------------------
 
+def tile_tokens(block_size: int) -> int:
+    """Positions per tile inside a block: 16 when the block is a multiple of
+    16 positions, else the whole block."""
+    return 16 if block_size % 16 == 0 else block_size
+
+
 def _k_view(k_pool: np.ndarray, num_kv_heads: int, block_size: int, head_dim: int, dtype: str):
+    # [block][head][tile][D/x][position in tile][x]
     x = 16 // ELEM_BYTES[dtype]
-    return np.asarray(k_pool).reshape(-1, num_kv_heads, head_dim // x, block_size, x)
+    t = tile_tokens(block_size)
+    return np.asarray(k_pool).reshape(-1, num_kv_heads, block_size // t, head_dim // x, t, x)
 
 
 def _v_view(v_pool: np.ndarray, num_kv_heads: int, block_size: int, head_dim: int):
-    return np.asarray(v_pool).reshape(-1, num_kv_heads, head_dim, block_size)
+    # [block][head][tile][D][position in tile]
+    t = tile_tokens(block_size)
+    return np.asarray(v_pool).reshape(-1, num_kv_heads, block_size // t, head_dim, t)
 
 
 def block_tokens(k_pool, v_pool, physical_block: int, num_kv_heads: int, block_size: int,
@@ -151,14 +161,15 @@ def block_tokens(k_pool, v_pool, physical_block: int, num_kv_heads: int, block_s
     """All ``block_size`` token rows of one physical block, as raw storage.
 
     Returns ``(K, V)``, each ``[block_size][num_kv_heads][head_dim]`` in the
-    storage dtype (bit patterns untouched).
+    storage dtype (bit patterns untouched).  Position p of the block is
+    position p % T of tile p // T (T = ``tile_tokens``).
     """
-    k5 = _k_view(k_pool, num_kv_heads, block_size, head_dim, dtype)[physical_block]
-    # k5: [Hkv][D/x][bs][x] -> [bs][Hkv][D/x][x] -> [bs][Hkv][D]
-    k_rows = k5.transpose(2, 0, 1, 3).reshape(block_size, num_kv_heads, head_dim)
-    v4 = _v_view(v_pool, num_kv_heads, block_size, head_dim)[physical_block]
-    # v4: [Hkv][D][bs] -> [bs][Hkv][D]
-    v_rows = v4.transpose(2, 0, 1)
+    k6 = _k_view(k_pool, num_kv_heads, block_size, head_dim, dtype)[physical_block]
+    # [Hkv][tiles][D/x][T][x] -> [tiles][T][Hkv][D/x][x] -> [bs][Hkv][D]
+    k_rows = k6.transpose(1, 3, 0, 2, 4).reshape(block_size, num_kv_heads, head_dim)
+    v5 = _v_view(v_pool, num_kv_heads, block_size, head_dim)[physical_block]
+    # [Hkv][tiles][D][T] -> [tiles][T][Hkv][D] -> [bs][Hkv][D]
+    v_rows = v5.transpose(1, 3, 0, 2).reshape(block_size, num_kv_heads, head_dim)
     return k_rows, v_rows
 
 
@@ -296,9 +307,10 @@ def write_kv(k_pool, v_pool, k_new, v_new, slots, num_kv_heads: int, block_size:
     """
     k_out = np.array(k_pool, copy=True)
     v_out = np.array(v_pool, copy=True)
-    k5 = _k_view(k_out, num_kv_heads, block_size, head_dim, dtype)
-    v4 = _v_view(v_out, num_kv_heads, block_size, head_dim)
+    k6 = _k_view(k_out, num_kv_heads, block_size, head_dim, dtype)
+    v5 = _v_view(v_out, num_kv_heads, block_size, head_dim)
     x = 16 // ELEM_BYTES[dtype]
+    tt = tile_tokens(block_size)
     k_new = np.asarray(k_new)
     v_new = np.asarray(v_new)
     for t, slot in enumerate(slots):
@@ -306,8 +318,9 @@ def write_kv(k_pool, v_pool, k_new, v_new, slots, num_kv_heads: int, block_size:
         if slot < 0:
             continue
         block, offset = divmod(slot, block_size)
-        k5[block, :, :, offset, :] = k_new[t].reshape(num_kv_heads, head_dim // x, x)
-        v4[block, :, :, offset] = v_new[t]
+        tile, pos = divmod(offset, tt)
+        k6[block, :, tile, :, pos, :] = k_new[t].reshape(num_kv_heads, head_dim // x, x)
+        v5[block, :, tile, :, pos] = v_new[t]
     return k_out, v_out
 
 

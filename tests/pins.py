@@ -110,8 +110,13 @@ def check_tail_waste_bound(max_bs=64, max_len=600):
 # ----------------------------------------------------------------------------
 
 def check_layout_contract():
-    for dtype, x in (("f32", 4), ("bf16", 8)):
-        nb, hkv, bs, d = 3, 2, 4, 16
+    """The in-block layout, element by element, against its scalar formulas:
+    per (block, head), positions in tiles of T = 16 when the block size is a
+    multiple of 16 (else T = the block size); K [tile][D/x][T][x] with x = 16
+    bytes of elements, V [tile][D][T]."""
+    for dtype, x, bs in (("f32", 4, 4), ("bf16", 8, 4), ("bf16", 8, 32), ("f32", 4, 48)):
+        nb, hkv, d = 3, 2, 16
+        tt = 16 if bs % 16 == 0 else bs
         n = hkv * bs * d
         # element id = its (block, head, offset, dim) coordinates packed as an int
         k_pool = np.zeros((nb, n), dtype=np.int64)
@@ -119,10 +124,12 @@ def check_layout_contract():
         for b in range(nb):
             for h in range(hkv):
                 for t in range(bs):
+                    tile, p = divmod(t, tt)
                     for e in range(d):
                         code = ((b * 10 + h) * 100 + t) * 1000 + e
-                        ki = (((b * hkv + h) * (d // x) + e // x) * bs + t) * x + e % x
-                        vi = ((b * hkv + h) * d + e) * bs + t
+                        head = (b * hkv + h) * bs * d + tile * tt * d
+                        ki = head + ((e // x) * tt + p) * x + e % x
+                        vi = head + e * tt + p
                         k_pool.reshape(-1)[ki] = code
                         v_pool.reshape(-1)[vi] = code
         for b in range(nb):
