@@ -48,16 +48,22 @@
  *  keys feed the gfx950 matrix cores straight from 16-byte loads:
  *
  *    x = 16 / sizeof(element)           (8 for bf16, 4 for f32)
+ *    T = 16 if block_size is a multiple of 16, else block_size
+ *        (positions per tile; a block holds block_size / T tiles)
  *    S = block_stride (or Hkv * block_size * D when it is 0)
+ *    for offset t in the block: tile u = t / T, position p = t % T, and
+ *    R = b * S + h * block_size * D + u * T * D  (the tile's region)
  *    K element (block b, kv head h, offset t, dim d) at index
- *        b * S + ((h * (D / x) + d / x) * block_size + t) * x + d % x
+ *        R + ((d / x) * T + p) * x + d % x
  *    V element (block b, kv head h, offset t, dim d) at index
- *        b * S + (h * D + d) * block_size + t
+ *        R + d * T + p
  *
- *  i.e. each block of K is [Hkv][D/x][block_size][x] and each block of V is
- *  [Hkv][D][block_size].  A (block, head) tile is contiguous (4 KiB for K
- *  and 4 KiB for V at block_size 16, D 128, bf16).  Both buffers must be
- *  16-byte aligned and S * sizeof(element) a multiple of 16.
+ *  i.e. each block of K is [Hkv][tiles][D/x][T][x] and each block of V is
+ *  [Hkv][tiles][D][T]; for block sizes up to 16 that is [Hkv][D/x][bs][x]
+ *  and [Hkv][D][bs].  A (block, head) region is contiguous, and so is each
+ *  16-position tile in it (4 KiB of K and 4 KiB of V at D 128, bf16), which
+ *  is what one MFMA step consumes.  Both buffers must be 16-byte aligned
+ *  and S * sizeof(element) a multiple of 16.
  *
  *  Recommended allocation: one buffer of [num_blocks][2][Hkv * block_size *
  *  D] elements with k_cache = its start, v_cache = start + Hkv * block_size

@@ -100,16 +100,20 @@ int device_cu_count() {
 namespace {
 
 int granule(const pa_cache_desc_t* c, int group) {
-    return fast_path_ok(c, group) ? 16 : c->block_size;
+    return fast_decode_ok(c, group) ? fast_granule(c->block_size) : c->block_size;
+}
+
+int max_partition(const pa_cache_desc_t* c, int group) {
+    return fast_decode_ok(c, group) ? fast_max_partition(c->block_size) : kMaxPartitionTokens;
 }
 
 int32_t plan_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads,
                        int32_t max_context_len) {
     const int group = num_q_heads / c->num_kv_heads;
     const int g = granule(c, group);
-    const int cap = (kMaxPartitionTokens / g) * g;
+    const int cap = (max_partition(c, group) / g) * g;
     if (max_context_len <= 0) return g;
-    const int64_t units = static_cast<int64_t>(num_seqs) * (fast_path_ok(c, group) ? c->num_kv_heads : num_q_heads);
+    const int64_t units = static_cast<int64_t>(num_seqs) * (fast_decode_ok(c, group) ? c->num_kv_heads : num_q_heads);
     const int64_t target = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
     int64_t p = ceil_div(static_cast<int64_t>(max_context_len) * std::max<int64_t>(units, 1), target);
     p = std::max<int64_t>(p, kMinAutoPartitionTokens);
@@ -147,10 +151,11 @@ int resolve_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_
     }
     const int group = num_q_heads / c->num_kv_heads;
     const int g = granule(c, group);
-    if (requested < c->block_size || requested > kMaxPartitionTokens || requested % g != 0)
+    const int cap = max_partition(c, group);
+    if (requested < c->block_size || requested > cap || requested % g != 0)
         return fail(PA_ERR_SHAPE,
                     "partition_tokens %d must be a multiple of %d in [%d, %d]", requested, g,
-                    c->block_size, kMaxPartitionTokens);
+                    c->block_size, cap);
     *out = requested;
     return PA_OK;
 }

@@ -40,15 +40,14 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
         const int h = i / chunks;
         const int c = i - h * chunks;
         const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
-        E* dst = k_cache + b * blk_stride + h * tile + (static_cast<int64_t>(c) * block_size + o) * X;
+        E* dst = k_cache + b * blk_stride + h * tile + k_elem(o, c * X, block_size, head_dim, X);
         *reinterpret_cast<uint4*>(dst) = v;
     }
     // V: (head, dim) elements.
     for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
         const int h = i / head_dim;
         const int d = i - h * head_dim;
-        v_cache[b * blk_stride + h * tile + static_cast<int64_t>(d) * block_size + o] =
-            v_new[row + i];
+        v_cache[b * blk_stride + h * tile + v_elem(o, d, block_size, head_dim)] = v_new[row + i];
     }
 }
 
@@ -82,13 +81,13 @@ __global__ __launch_bounds__(256) void append_kv_kernel(E* __restrict__ k_cache,
         const int h = i / chunks;
         const int c = i - h * chunks;
         const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
-        E* dst = k_cache + b * blk_stride + h * tile + (static_cast<int64_t>(c) * block_size + o) * X;
+        E* dst = k_cache + b * blk_stride + h * tile + k_elem(o, c * X, block_size, head_dim, X);
         *reinterpret_cast<uint4*>(dst) = v;
     }
     for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
         const int h = i / head_dim;
         const int d = i - h * head_dim;
-        v_cache[b * blk_stride + h * tile + static_cast<int64_t>(d) * block_size + o] = v_new[row + i];
+        v_cache[b * blk_stride + h * tile + v_elem(o, d, block_size, head_dim)] = v_new[row + i];
     }
 }
 
@@ -155,8 +154,8 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const E* __restrict__ k_
     int phys = table[lb];
     if (phys < 0 || phys >= num_blocks) phys = 0;
     const int64_t tile = static_cast<int64_t>(phys) * blk_stride + static_cast<int64_t>(h) * head_dim * block_size;
-    k_out[i] = k_cache[tile + (static_cast<int64_t>(d / X) * block_size + o) * X + d % X];
-    v_out[i] = v_cache[tile + static_cast<int64_t>(d) * block_size + o];
+    k_out[i] = k_cache[tile + k_elem(o, d, block_size, head_dim, X)];
+    v_out[i] = v_cache[tile + v_elem(o, d, block_size, head_dim)];
 }
 
 }  // namespace

@@ -112,6 +112,30 @@ __device__ __forceinline__ void load_tile(Tile& t, const __bf16* __restrict__ k_
     for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 64 * j);
 }
 
+// The same tile out of blocks of BS tokens: tile `sub` of one block when BS
+// is a multiple of 16 (the block holds BS/16 such tiles back to back); for
+// BS = 8 (K [D/8][8][8], V [D][8] per head) the tile's first 8 tokens come
+// from block `a`, the next 8 from block `b` (K rows 8..15 and V token groups
+// 2..3).  k_a/v_a, k_b/v_b point at the head's region in blocks a and b.
+template <bool NT, int BS>
+__device__ __forceinline__ void load_tile_bs(Tile& t, const __bf16* __restrict__ k_a,
+                                             const __bf16* __restrict__ v_a,
+                                             const __bf16* __restrict__ k_b,
+                                             const __bf16* __restrict__ v_b, int sub, int lane) {
+    const int row = lane & 15, quad = lane >> 4;
+    if constexpr (BS >= 16) {                 // tile `sub` of the block: a 16-position tile
+        load_tile<NT>(t, k_a + sub * FTILE, v_a + sub * FTILE, lane);
+    } else {
+        static_assert(BS == 8, "blocks of 8, 16, 32 or 64 tokens");
+        const bf16x8* kp = reinterpret_cast<const bf16x8*>(row < 8 ? k_a : k_b) + (row & 7);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
+        const s16x4* vp = reinterpret_cast<const s16x4*>(quad < 2 ? v_a : v_b) + row * 2 + (quad & 1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 32 * j);
+    }
+}
+
 struct SoftmaxState {
     float m;        // running max of log2-domain scores for query row lane%16
     float l;        // this lane's share of the running sum
@@ -202,7 +226,7 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
 // workgroup (wave w = partition w, at most kMaxWgParts of them) and are
 // merged through LDS after a workgroup barrier, instead of by the merge
 // kernel.  Waves without a partition wait at the barrier.
-template <int NBUF, bool NT, bool APPEND, bool WGM>
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS>
 __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
@@ -242,9 +266,12 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     const bool active = tok0 < L;
     const int tok1 = min(L, tok0 + part_tokens);
     const int nparts = (L + part_tokens - 1) / part_tokens;
-    const int blk0 = tok0 / FBS;
-    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64
+    // tiles of 16 tokens; table entries (blocks of BS tokens), one per lane
+    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;
     const int last_valid = tok1 - (tok0 + (nblk - 1) * FBS);
+    const int blk0 = tok0 / BS;
+    const int nent = (tok1 - tok0 + BS - 1) / BS;     // 1..64
+    constexpr int HT = BS * FD;                       // elements of one (block, head) tile
 
     SoftmaxState st;
     st.m = -INFINITY;
@@ -256,7 +283,7 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     if (active) {
     // Block-table entries of this partition: one per lane, read back with readlane.
     int my_phys = 0;
-    if (lane < nblk)
+    if (lane < nent)
         my_phys = clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
                               num_blocks);
 
@@ -265,7 +292,8 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     // (the same chunk order as the K tile); the 16 lanes of quad o/4 hold its
     // 128 value dims (dim 16*j + row).  They also store them to the cache.
     const bool append_here = APPEND && part == nparts - 1;
-    const int o_new = (L - 1) % FBS;
+    const int o_new = (L - 1) % FBS;                  // slot within the last tile
+    const int ob_new = (L - 1) % BS;                  // slot within the last block
     bf16x8 fk[4];
     short fv[8];
     if constexpr (APPEND) {
@@ -277,17 +305,21 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
             for (int s4 = 0; s4 < 4; ++s4) fk[s4] = kn[4 * s4 + quad];
 #pragma unroll
             for (int j = 0; j < 8; ++j) fv[j] = vn[16 * j + row];
-            const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, nblk - 1)) *
-                                     blk_stride + static_cast<int64_t>(h) * FTILE;
+            const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, nent - 1)) *
+                                     blk_stride + static_cast<int64_t>(h) * HT;
+            // the slot's tile inside the block, and its position in that tile
+            constexpr int TT = BS >= 16 ? 16 : BS;
+            const int64_t tile_base = toff + static_cast<int64_t>(ob_new / TT) * TT * FD;
+            const int pt = ob_new % TT;
             if (row == o_new) {
-                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff);
+                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + tile_base);
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * FBS + o_new] = fk[s4];
+                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * TT + pt] = fk[s4];
             }
             if (quad == o_new / 4) {
-                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + toff);
+                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + tile_base);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * FBS + o_new] = fv[j];
+                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * TT + pt] = fv[j];
             }
         }
     }
@@ -304,8 +336,8 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
         }
     }
 
-    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
-    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
+    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * HT;
+    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * HT;
 
     // A ring of NBUF tiles: while block j is consumed, blocks j+1 .. j+NBUF-1
     // are in flight.  Loads are unconditional (past the end they repeat the
@@ -315,23 +347,26 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     // tile's arithmetic; without them the compiler sinks loads next to their
     // first use and every block waits a full memory latency.
     Tile buf[NBUF];
-    auto tile_off = [&](int jj) {
+    auto entry_off = [&](int e) {
+        return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, e < nent ? e : nent - 1)) * blk_stride;
+    };
+    auto load_t = [&](Tile& t, int jj) {     // tile jj (clamped to the last)
         const int jc = jj < nblk ? jj : nblk - 1;
-        return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, jc)) * blk_stride;
+        if constexpr (BS >= 16) {
+            const int64_t o = entry_off(jc / (BS / 16));
+            load_tile_bs<NT, BS>(t, k_head + o, v_head + o, nullptr, nullptr, jc % (BS / 16), lane);
+        } else {
+            const int64_t oa = entry_off(2 * jc), ob = entry_off(2 * jc + 1);
+            load_tile_bs<NT, BS>(t, k_head + oa, v_head + oa, k_head + ob, v_head + ob, 0, lane);
+        }
     };
 #pragma unroll
-    for (int u = 0; u < NBUF - 1; ++u) {
-        const int64_t o = tile_off(u);
-        load_tile<NT>(buf[u], k_head + o, v_head + o, lane);
-    }
+    for (int u = 0; u < NBUF - 1; ++u) load_t(buf[u], u);
     for (int j0 = 0; j0 < nblk; j0 += NBUF) {
 #pragma unroll
         for (int u = 0; u < NBUF; ++u) {
             const int j = j0 + u;
-            {
-                const int64_t o = tile_off(j + NBUF - 1);
-                load_tile<NT>(buf[(u + NBUF - 1) % NBUF], k_head + o, v_head + o, lane);
-            }
+            load_t(buf[(u + NBUF - 1) % NBUF], j + NBUF - 1);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (APPEND) {
                 if (append_here && j == nblk - 1) {
@@ -878,8 +913,8 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
         for (int r = 0; r < DPL; ++r) {
             const int d = lane + 64 * r;
             if (d < D) {
-                kd[r] = load_f32(k_cache + base + (static_cast<int64_t>(d / X) * block_size + o) * X + d % X);
-                vd[r] = load_f32(v_cache + base + static_cast<int64_t>(d) * block_size + o);
+                kd[r] = load_f32(k_cache + base + k_elem(o, d, block_size, D, X));
+                vd[r] = load_f32(v_cache + base + v_elem(o, d, block_size, D));
             } else {
                 kd[r] = 0.f;
                 vd[r] = 0.f;
@@ -1031,13 +1066,13 @@ int launch_generic_d(const DecodeArgs& a) {
     }
 }
 
-template <bool NT, bool APPEND>
+template <bool NT, bool APPEND, int BS>
 int launch_fast(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
     const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (FD + 4) * sizeof(float);
     if (a.max_parts >= 2 && a.max_parts <= kMaxWgParts && wg_lds <= kMaxWgLds) {
         // partitions of a request are the waves of one workgroup, merged in LDS
-        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true>),
+        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true, BS>),
                            dim3(a.num_kv_heads, a.num_seqs, 1), dim3(64 * a.max_parts), wg_lds,
                            a.stream, static_cast<const __bf16*>(a.k_cache),
                            static_cast<const __bf16*>(a.v_cache), static_cast<const __bf16*>(a.q),
@@ -1049,7 +1084,7 @@ int launch_fast(const DecodeArgs& a) {
         return check_launch("decode (fast, workgroup merge)");
     }
     dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false>), grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_q_heads, a.group,
@@ -1084,6 +1119,12 @@ int launch_grouped(const DecodeArgs& a, int members) {
                        0, a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
                        a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
     return check_launch("decode reduce");
+}
+
+template <int BS>
+int launch_fast_bs(const DecodeArgs& a, bool nt) {
+    if (a.k_new) return nt ? launch_fast<true, true, BS>(a) : launch_fast<false, true, BS>(a);
+    return nt ? launch_fast<true, false, BS>(a) : launch_fast<false, false, BS>(a);
 }
 
 template <bool NT, bool APPEND>
@@ -1242,9 +1283,13 @@ int launch_decode(const DecodeArgs& a) {
         if (a.k_new) return nt ? launch_grouped_r<true, true>(a) : launch_grouped_r<false, true>(a);
         return nt ? launch_grouped_r<true, false>(a) : launch_grouped_r<false, false>(a);
     }
-    if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0) {
-        if (a.k_new) return nt ? launch_fast<true, true>(a) : launch_fast<false, true>(a);
-        return nt ? launch_fast<true, false>(a) : launch_fast<false, false>(a);
+    if (fast_decode_ok(&c, a.group) && a.part_tokens % fast_granule(a.block_size) == 0) {
+        switch (a.block_size) {
+            case 8: return launch_fast_bs<8>(a, nt);
+            case 32: return launch_fast_bs<32>(a, nt);
+            case 64: return launch_fast_bs<64>(a, nt);
+            default: return launch_fast_bs<16>(a, nt);
+        }
     }
     if (a.k_new) {   // generic path: append with its own kernel, then decode
         int st = launch_append_kv(&c, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache),

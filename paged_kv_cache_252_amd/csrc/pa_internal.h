@@ -43,16 +43,56 @@ inline int64_t block_stride(const pa_cache_desc_t* c) {
     return c->block_stride ? c->block_stride : block_elems(c);
 }
 
+// ---- in-block layout ----------------------------------------------------------
+//
+// One (block, head) region holds block_size * head_dim elements.  Positions
+// are grouped in tiles of T = 16 when the block size is a multiple of 16
+// (else T = the block size): K is [tile][D/X][T][X] with X elements = 16
+// bytes, V is [tile][D][T].  A 16-position tile is thus the same 4 KiB K and
+// 4 KiB V (bf16, D 128) whatever the block size.
+
+__host__ __device__ inline int tile_tokens(int block_size) {
+    return block_size % 16 == 0 ? 16 : block_size;
+}
+
+// Offset of K element (position pos, dim d) inside its (block, head) region.
+__host__ __device__ inline int64_t k_elem(int pos, int d, int block_size, int head_dim, int x) {
+    const int t = tile_tokens(block_size);
+    const int tile = pos / t, p = pos - tile * t;
+    return static_cast<int64_t>(tile) * t * head_dim + (static_cast<int64_t>(d / x) * t + p) * x + d % x;
+}
+
+// Offset of V element (position pos, dim d) inside its (block, head) region.
+__host__ __device__ inline int64_t v_elem(int pos, int d, int block_size, int head_dim) {
+    const int t = tile_tokens(block_size);
+    const int tile = pos / t, p = pos - tile * t;
+    return static_cast<int64_t>(tile) * t * head_dim + static_cast<int64_t>(d) * t + p;
+}
+
 // ---- decode planning --------------------------------------------------------
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
 
-// The fast MFMA kernel handles this shape.
+// The MFMA kernels for block size 16 (decode, grouped decode, prefill) handle this shape.
 inline bool fast_path_ok(const pa_cache_desc_t* c, int group) {
     return c->dtype == PA_BF16 && c->head_dim == 128 && c->block_size == 16 && group >= 1 &&
            group <= 16;
 }
+
+// The MFMA decode kernel handles this shape (blocks of 8 pair up into its
+// 16-token tiles; blocks of 32 or 64 split into them).
+inline bool fast_decode_ok(const pa_cache_desc_t* c, int group) {
+    const int bs = c->block_size;
+    return c->dtype == PA_BF16 && c->head_dim == 128 && (bs == 8 || bs == 16 || bs == 32 || bs == 64) &&
+           group >= 1 && group <= 16;
+}
+
+// Partitions of the MFMA decode kernel are whole tiles and whole blocks.
+inline int fast_granule(int block_size) { return block_size > 16 ? block_size : 16; }
+
+// ... and hold at most one block-table entry per lane of a wave.
+inline int fast_max_partition(int block_size) { return 64 * block_size < 1024 ? 64 * block_size : 1024; }
 
 // ---- kernel launchers (defined in the .hip files) --------------------------
 

@@ -74,6 +74,11 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, _desc(), num_seqs=-1) == 2
     assert _decode(lib, _desc(), part=24) == 2                      # not a multiple of 16
     assert _decode(lib, _desc(), part=2048) == 2                    # above 1024
+    # the MFMA decode at other block sizes: whole blocks and tiles, one table
+    # entry per lane (at most 64 blocks of 8 = 512 tokens)
+    assert _decode(lib, _desc(block_size=8), max_blocks=8, part=1024) == 2
+    assert _decode(lib, _desc(block_size=8), max_blocks=8, part=8) == 2
+    assert _decode(lib, _desc(block_size=32), max_blocks=2, part=16) == 2
     assert _decode(lib, _desc(), ptr=(1 << 20) + 8) == 4            # misaligned buffers
     assert _decode(lib, _desc(), flags=4) == 5                      # unknown flag bit
     d = _desc()

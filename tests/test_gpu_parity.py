@@ -95,14 +95,18 @@ def test_slot_mapping_random(bs):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("make", ["tiny", "bf16"])
+@pytest.mark.parametrize("make", ["tiny", "bf16", "bf16_bs32", "f32_bs48"])
 def test_gather_bit_exact(make):
     say(f"gather_kv {make}")
     if make == "tiny":
         w = inputs.tiny(device=DEV)
-    else:
+    elif make == "bf16":
         w = inputs.paged_random("g", 3, 1, 70, 8, 2, head_dim=64, block_size=8, dtype="bf16",
                                 num_blocks=64, seed=5, device=DEV)
+    else:                                         # blocks of several 16-position tiles
+        dtype, bs = ("bf16", 32) if make == "bf16_bs32" else ("f32", 48)
+        w = inputs.paged_random("g", 3, 1, 150, 8, 2, head_dim=64, block_size=bs, dtype=dtype,
+                                num_blocks=32, seed=6, device=DEV)
     spec = ops.CacheSpec.of(w)
     kp, vp = to_np(w.k_cache), to_np(w.v_cache)
     for i in range(w.num_seqs):
@@ -117,11 +121,11 @@ def test_gather_bit_exact(make):
 # cache writes (bit-exact, whole pools compared including NaN poison)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_write_kv_bit_exact(dtype):
-    say(f"write_kv {dtype}")
+@pytest.mark.parametrize("dtype,bs", [("f32", 16), ("bf16", 16), ("bf16", 32), ("f32", 48)])
+def test_write_kv_bit_exact(dtype, bs):
+    say(f"write_kv {dtype} bs={bs}")
     w = inputs.paged_random("w", 5, 1, 60, 4, 2, head_dim=32 if dtype == "f32" else 128,
-                            block_size=16, dtype=dtype, num_blocks=40, seed=7, device=DEV)
+                            block_size=bs, dtype=dtype, num_blocks=40, seed=7, device=DEV)
     inputs.add_step_tokens(w)
     spec = ops.CacheSpec.of(w)
     pos = w.new_pos.clone()
@@ -211,7 +215,7 @@ def test_separate_dense_pools(dtype):
 @pytest.mark.parametrize("dtype,d,bs,hq,hkv", [
     ("f32", 16, 4, 2, 2), ("f32", 128, 16, 8, 2), ("f32", 32, 1, 3, 1),
     ("bf16", 64, 8, 4, 2), ("bf16", 256, 16, 8, 2), ("bf16", 128, 4, 4, 4),
-    ("bf16", 128, 16, 40, 2),
+    ("bf16", 128, 16, 40, 2), ("f32", 64, 32, 4, 2), ("bf16", 64, 48, 8, 2),
 ])
 @pytest.mark.parametrize("part", [0, 64])
 def test_generic_path_shapes(dtype, d, bs, hq, hkv, part):
@@ -754,3 +758,64 @@ def test_prefill_validate_rejects_bad_offsets(monkeypatch):
         ops.prefill(ops.CacheSpec.of(w), w.q_chunk, bad, w.k_cache, w.v_cache, w.block_tables,
                     w.context_lens, w.max_q_len, w.max_context_len, w.scale)
     assert e.value.status == 8
+
+
+# ----------------------------------------------------------------------------
+# the MFMA decode path at block sizes 8, 32 and 64
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bs", [8, 32, 64])
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_fast_path_block_sizes(bs, group):
+    """Blocks of 8 pair up into the 16-token MFMA tile, blocks of 32 and 64
+    split into it: against the oracle at several partition sizes (lengths
+    around block and tile edges, L = 0), with the streaming hint giving the
+    same bits, and the folded append equal to write + decode."""
+    hkv = 2
+    lens = [0, 1, 7, 8, 9, 15, 16, 17, 31, 33, 63, 64, 65, 200, 511, 700]
+    w = inputs.paged_random("fbs", len(lens), 0, 700, hkv * group, hkv, block_size=bs,
+                            num_blocks=-(-700 // bs) * len(lens) + 8, seed=70 + bs + group,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    ref = oracle_decode(w)
+    g = max(16, bs)
+    cap = min(64 * bs, 1024)
+    for part in sorted({0, g, 3 * g, cap}):
+        say(f"decode bs={bs} g={group} part={part}")
+        out = run_decode(w, partition_tokens=part)
+        assert_close(w, out, ref, f"bs={bs} g={group} part={part}")
+        assert not to_np(out)[0].any()
+        assert same_bits(out, run_decode(w, partition_tokens=part, stream_kv=True))
+    # the folded append: same cache bytes and output bits as write + decode
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = run_decode(w, partition_tokens=g)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                              w.context_lens, w.max_context_len, w.scale, partition_tokens=g)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+    assert same_bits(fused, sep)
+    assert_close(w, fused, oracle_decode(w), f"bs={bs} append")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_size_placement_invariance(bs):
+    say(f"placement invariance bs={bs}")
+    w = inputs.paged_random("pbs", 6, 1, 600, 32, 8, block_size=bs, num_blocks=-(-600 // bs) * 6 + 16,
+                            seed=80 + bs, device=DEV)
+    a = run_decode(w).clone()
+    perm = torch.randperm(w.num_blocks, generator=torch.Generator().manual_seed(bs)).to(DEV)
+    k2, v2 = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache[perm] = k2
+    w.v_cache[perm] = v2
+    bt = w.block_tables.clone()
+    ok = bt >= 0
+    bt[ok] = perm[bt[ok].long()].int()
+    w.block_tables = bt
+    assert same_bits(a, run_decode(w))
