@@ -3,9 +3,9 @@
     python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout|prefill]
 
 A step is one pass of the whole hot path over one batch of synthetic
-requests: copy-on-write block copies (only the fan-out workload has any),
-then ``pa_decode_append``, which writes each request's newest token at its
-slot and runs decode attention over every request's paged history.  Inputs are resident in HBM
+requests: ``pa_decode_step``, which makes each request's copy-on-write copy
+(only the fan-out workload has any), writes its newest token at its slot
+and runs decode attention over every request's paged history.  Inputs are resident in HBM
 before timing starts.  Steps cycle through R replicas of the batch placed
 at disjoint physical blocks, so the 256 MB Infinity Cache cannot hold the
 working set between steps (every replica holds the same bytes, so every
@@ -401,14 +401,25 @@ def main() -> int:
     log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
         f"workspace {ws_bytes} B, {reps} replicas")
 
+    cow_src = None
+    if w.cow_pairs is not None:
+        # the step's copy-on-write pairs given per request: the source of the
+        # copy into the block that holds the request's newest position
+        by_dst = {int(d): int(s_) for s_, d in w.cow_pairs.cpu().numpy()}
+        bt0, lens0 = tables[0].cpu().numpy(), w.context_lens.cpu().numpy()
+        src = [by_dst.get(int(bt0[i, (int(lens0[i]) - 1) // w.block_size]), -1)
+               for i in range(w.num_seqs)]
+        if reps > 1 or sum(x >= 0 for x in src) != w.cow_pairs.shape[0]:
+            log("copy-on-write pairs do not map one per request")
+            return 1
+        cow_src = torch.as_tensor(src, dtype=torch.int32, device=dev)
+
     def step(r: int) -> None:
-        # copy-on-write copies, then one call that appends each request's new
-        # token at position L-1 and attends (pa_decode_append)
-        if w.cow_pairs is not None:
-            ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
-        ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, tables[r],
-                          w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
-                          partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared)
+        # one call: each request's copy-on-write copy (fan-out only), the
+        # append of its new token at position L-1, and decode (pa_decode_step)
+        ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src, tables[r],
+                        w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
+                        partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared)
 
     for i in range(args.warmup):
         step(i % reps)

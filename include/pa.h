@@ -309,6 +309,33 @@ int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, con
                      uint32_t flags, void* stream);
 
 /*
+ * pa_decode_step -- one decode step with its copy-on-write copies folded in.
+ *
+ * Exactly pa_copy_blocks of the pairs {cow_src[i], B_i} for every request i
+ * with cow_src[i] >= 0, where B_i = block_tables[i][(L_i - 1) / block_size]
+ * is the block that holds the request's newest position, followed by
+ * pa_decode_append ([ZQ] answer and [KG] "Shared Blocks Must Not Be Changed
+ * in Place": a request that writes into a shared block gets a fresh copy of
+ * it first; the block manager's pa_bm_append reports exactly such pairs).
+ * With block size 16 on the MFMA path the wave that reads the request's last
+ * block reads it from cow_src[i] and writes it back whole, new token
+ * included, to B_i: the copy and the token write become full-line stores and
+ * the block is read once.  Other shapes copy first with a kernel of their own.
+ *
+ * Arguments: as pa_decode_append, plus
+ *   cow_src   [num_seqs] int32 device array (may be NULL = no copies):
+ *             the source block of request i's copy, or -1.  Each B_i with a
+ *             copy must be distinct and must not be another request's source;
+ *             out-of-range sources are skipped (PA_VALIDATE=1 rejects them).
+ */
+int pa_decode_step(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                   const void* v_new, const int32_t* cow_src, const void* q,
+                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                   float scale, void* out, void* workspace, size_t workspace_bytes,
+                   int32_t partition_tokens, uint32_t flags, void* stream);
+
+/*
  * pa_prefill -- several new query tokens per request against the paged
  * history: a chunk of a prompt whose earlier part is cached (e.g. found by
  * the prefix cache), a chunked prefill, or several tokens checked at once.

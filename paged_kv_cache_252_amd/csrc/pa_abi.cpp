@@ -220,7 +220,8 @@ int prefill_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t max_q_
 using namespace pa;
 
 static int decode_impl(const char* fn, const pa_cache_desc_t* c, const void* k_cache,
-                       const void* v_cache, const void* k_new, const void* v_new, const void* q,
+                       const void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* cow_src, const void* q,
                        const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                        int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
                        float scale, void* out, void* workspace, size_t workspace_bytes_given,
@@ -271,6 +272,31 @@ static int decode_impl(const char* fn, const pa_cache_desc_t* c, const void* k_c
                     return fail(PA_ERR_VALIDATE, "block_tables[%d][%d] = %d outside [0, %lld)", i, j, b, (long long)c->num_blocks);
             }
         }
+        if (cow_src) {
+            // the copies: sources in range, each destination (a request's block
+            // holding L-1) named once, and no destination also a source
+            std::vector<int32_t> srcs;
+            if ((st = fetch(srcs, cow_src, num_seqs, s))) return st;
+            std::vector<int64_t> dsts;
+            std::vector<int64_t> all_src;
+            for (int32_t i = 0; i < num_seqs; ++i) {
+                if (srcs[i] < 0) continue;
+                if (srcs[i] >= c->num_blocks)
+                    return fail(PA_ERR_VALIDATE, "cow_src[%d] = %d outside [0, %lld)", i, srcs[i], (long long)c->num_blocks);
+                if (lens[i] <= 0)
+                    return fail(PA_ERR_VALIDATE, "cow_src[%d] set for a request with no positions", i);
+                dsts.push_back(tables[static_cast<size_t>(i) * max_blocks_per_seq + (lens[i] - 1) / c->block_size]);
+                all_src.push_back(srcs[i]);
+            }
+            std::vector<int64_t> d2 = dsts;
+            std::sort(d2.begin(), d2.end());
+            if (std::adjacent_find(d2.begin(), d2.end()) != d2.end())
+                return fail(PA_ERR_VALIDATE, "two copy-on-write destinations are the same block");
+            std::sort(all_src.begin(), all_src.end());
+            for (int64_t d : dsts)
+                if (std::binary_search(all_src.begin(), all_src.end(), d))
+                    return fail(PA_ERR_VALIDATE, "copy-on-write destination %lld is also a source", (long long)d);
+        }
     }
     const int64_t parts64 = std::max<int64_t>(1, ceil_div(max_context_len, part));
     if (parts64 > kMaxGridYZ)
@@ -306,6 +332,7 @@ static int decode_impl(const char* fn, const pa_cache_desc_t* c, const void* k_c
     a.ws_l = need ? ws + slots * (c->head_dim + 1) : nullptr;
     a.k_new = k_new;
     a.v_new = v_new;
+    a.cow_src = cow_src;
     a.stream = s;
     if ((st = launch_decode(a))) return st;
     return ok();
@@ -448,7 +475,7 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
               int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
               int32_t max_context_len, float scale, void* out, void* workspace,
               size_t workspace_bytes, int32_t partition_tokens, uint32_t flags, void* stream) {
-    return decode_impl("pa_decode", c, k_cache, v_cache, nullptr, nullptr, q, block_tables,
+    return decode_impl("pa_decode", c, k_cache, v_cache, nullptr, nullptr, nullptr, q, block_tables,
                        context_lens, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
                        scale, out, workspace, workspace_bytes, partition_tokens, flags, stream);
 }
@@ -583,9 +610,24 @@ int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, con
                      uint32_t flags, void* stream) {
     if (num_seqs > 0 && (!k_new || !v_new))
         return fail(PA_ERR_NULL, "pa_decode_append: k_new and v_new are required");
-    return decode_impl("pa_decode_append", c, k_cache, v_cache, k_new, v_new, q, block_tables,
-                       context_lens, num_seqs, num_q_heads, max_blocks_per_seq, max_context_len,
-                       scale, out, workspace, workspace_bytes, partition_tokens, flags, stream);
+    return decode_impl("pa_decode_append", c, k_cache, v_cache, k_new, v_new, nullptr, q,
+                       block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                       max_context_len, scale, out, workspace, workspace_bytes, partition_tokens,
+                       flags, stream);
+}
+
+int pa_decode_step(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
+                   const void* v_new, const int32_t* cow_src, const void* q,
+                   const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                   int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
+                   float scale, void* out, void* workspace, size_t workspace_bytes,
+                   int32_t partition_tokens, uint32_t flags, void* stream) {
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PA_ERR_NULL, "pa_decode_step: k_new and v_new are required");
+    return decode_impl("pa_decode_step", c, k_cache, v_cache, k_new, v_new, cow_src, q,
+                       block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                       max_context_len, scale, out, workspace, workspace_bytes, partition_tokens,
+                       flags, stream);
 }
 
 }  // extern "C"

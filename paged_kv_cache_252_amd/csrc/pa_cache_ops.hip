@@ -111,6 +111,30 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_
     v_cache[dst * vecs_stride + i] = vv;
 }
 
+// ---- copy-on-write of each request's last block from cow_src[i] ---------------
+// The decode step's copies given per request: request i's block holding
+// position L-1 (its table entry) receives a copy of block cow_src[i]
+// (skipped when negative).  grid.x is the request, grid.y as copy_blocks.
+__global__ __launch_bounds__(256) void cow_last_block_kernel(
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const int32_t* __restrict__ cow_src,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int max_blocks_per_seq, int len_clamp, int block_size, int64_t num_blocks,
+    int64_t vecs_per_block, int64_t vecs_stride) {
+    const int seq = blockIdx.x;
+    const int64_t src = cow_src[seq];
+    int L = context_lens[seq];
+    L = L > len_clamp ? len_clamp : L;
+    if (src < 0 || src >= num_blocks || L <= 0) return;
+    const int64_t dst = block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + (L - 1) / block_size];
+    if (dst < 0 || dst >= num_blocks) return;
+    const int64_t i = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x;
+    if (i >= vecs_per_block) return;
+    const uint4 kv = k_cache[src * vecs_stride + i];
+    const uint4 vv = v_cache[src * vecs_stride + i];
+    k_cache[dst * vecs_stride + i] = kv;
+    v_cache[dst * vecs_stride + i] = vv;
+}
+
 // ---- translate: [KG] "Follow One Token Address" ----------------------------
 __global__ __launch_bounds__(256) void slot_mapping_kernel(
     int block_size, const int32_t* __restrict__ block_tables, int num_seqs,
@@ -212,6 +236,21 @@ int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
                        0, stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
                        pairs, c->num_blocks, vecs, vstride);
     return check_launch("copy_blocks");
+}
+
+int launch_cow_last_block(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                          const int32_t* cow_src, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t len_clamp, hipStream_t stream) {
+    if (num_seqs == 0) return PA_OK;
+    const int64_t vecs = block_elems(c) * elem_bytes(c->dtype) / 16;
+    const int64_t vstride = block_stride(c) * elem_bytes(c->dtype) / 16;
+    const int64_t gy = (vecs + 255) / 256;
+    hipLaunchKernelGGL(cow_last_block_kernel, dim3(num_seqs, static_cast<unsigned>(gy)), dim3(256),
+                       0, stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache),
+                       cow_src, block_tables, context_lens, max_blocks_per_seq, len_clamp,
+                       c->block_size, c->num_blocks, vecs, vstride);
+    return check_launch("copy-on-write of last blocks");
 }
 
 int launch_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,

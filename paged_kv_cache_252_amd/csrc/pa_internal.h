@@ -123,6 +123,8 @@ struct DecodeArgs {
     float* ws_l;             // [S][Hq][max_parts]
     const void* k_new;       // non-null: append each request's token at position L-1
     const void* v_new;
+    const int32_t* cow_src;  // non-null (with k_new): request i's block holding L-1 first
+                             // receives a copy of block cow_src[i] (negative: none)
     hipStream_t stream;
 };
 
@@ -145,6 +147,11 @@ int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, cons
 
 int launch_copy_blocks(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
                        const int64_t* pairs, int32_t num_pairs, hipStream_t stream);
+
+int launch_cow_last_block(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                          const int32_t* cow_src, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int32_t len_clamp, hipStream_t stream);
 
 int launch_slot_mapping(int32_t block_size, const int32_t* block_tables, int32_t num_seqs,
                         int32_t max_blocks_per_seq, const int32_t* seq_ids,

@@ -122,6 +122,9 @@ _SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P,
                                         _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                         ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
+    "pa_decode_step": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
+                                      ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32,
                                                      _I32, _I32, _I32]),
     "pa_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _I32, _I32,
@@ -384,6 +387,32 @@ def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tabl
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q),
         _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1], max_context_len,
         float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
+        _flags(stream_kv, group_shared), _stream(dev)))
+    return out
+
+
+def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, block_tables,
+                context_lens, max_context_len: int, scale: float, out=None, workspace=None,
+                partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False):
+    """``pa_decode_step``: copy-on-write of each request's last block from
+    ``cow_src[i]`` (int32 [num_seqs], -1 = none), then append + decode."""
+    dev, s, hq, out, workspace, ws_bytes = _decode_args(
+        spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, workspace,
+        partition_tokens)
+    _need(k_new, "k_new", spec.torch_dtype, dev)
+    _need(v_new, "v_new", spec.torch_dtype, dev)
+    if cow_src is not None:
+        _need(cow_src, "cow_src", torch.int32, dev)
+        if cow_src.numel() != s:
+            raise ValueError("cow_src must be [num_seqs]")
+    per = s * spec.num_kv_heads * spec.head_dim
+    if k_new.numel() != per or v_new.numel() != per:
+        raise ValueError("k_new/v_new must be [num_seqs, Hkv, head_dim]")
+    d = spec.desc()
+    _check("pa_decode_step", lib().pa_decode_step(
+        ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
+        _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
+        max_context_len, float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
         _flags(stream_kv, group_shared), _stream(dev)))
     return out
 

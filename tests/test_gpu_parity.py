@@ -819,3 +819,102 @@ def test_block_size_placement_invariance(bs):
     bt[ok] = perm[bt[ok].long()].int()
     w.block_tables = bt
     assert same_bits(a, run_decode(w))
+
+
+# ----------------------------------------------------------------------------
+# pa_decode_step: copy-on-write folded into the decode step
+# ----------------------------------------------------------------------------
+
+def _cow_src_of(w, pairs=None):
+    """Per request, the source of the copy whose destination is the block
+    holding its newest position (or -1)."""
+    pairs = to_np(w.cow_pairs) if pairs is None else np.asarray(pairs)
+    bt, lens = to_np(w.block_tables), to_np(w.context_lens)
+    by_dst = {int(d): int(s_) for s_, d in pairs}
+    src = np.full(w.num_seqs, -1, dtype=np.int32)
+    for i in range(w.num_seqs):
+        if int(lens[i]) > 0:
+            src[i] = by_dst.get(int(bt[i, (int(lens[i]) - 1) // w.block_size]), -1)
+    return torch.as_tensor(src, device=DEV)
+
+
+def _step_both_ways(w, spec, pairs, cow_src, **kw):
+    """(copy_blocks + decode_append) and decode_step from the same cache:
+    returns (out_ref, out_step) and checks the caches end bit-identical."""
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    if pairs.numel():
+        ops.copy_blocks(spec, w.k_cache, w.v_cache, pairs)
+    ref = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                            w.context_lens, w.max_context_len, w.scale, **kw)
+    k_ref, v_ref = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    got = ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src,
+                          w.block_tables, w.context_lens, w.max_context_len, w.scale, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_ref)) and torch.equal(bits(w.v_cache), bits(v_ref))
+    return ref, got
+
+
+@pytest.mark.parametrize("grouped", [False, True])
+@pytest.mark.parametrize("stream_kv", [False, True])
+@pytest.mark.parametrize("part", [0, 64])
+def test_decode_step_fanout(grouped, stream_kv, part):
+    """The fan-out step with its copies folded in equals copy + append +
+    decode: the same pool bytes (NaN-poisoned free blocks included) and the
+    same output bits."""
+    say(f"decode_step fan-out grouped={grouped} stream={stream_kv} part={part}")
+    w = inputs.fanout(num_prompts=9, branches=4, prompt_lo=20, prompt_hi=300, num_blocks=500,
+                      device=DEV)
+    spec = ops.CacheSpec.of(w)
+    cow_src = _cow_src_of(w)
+    assert int((cow_src >= 0).sum()) == w.cow_pairs.shape[0]
+    ref, got = _step_both_ways(w, spec, w.cow_pairs, cow_src, partition_tokens=part,
+                               stream_kv=stream_kv, group_shared=grouped)
+    assert same_bits(got, ref)
+    assert_close(w, got, oracle_decode(w), "decode_step fan-out")
+
+
+@pytest.mark.parametrize("dtype,bs,d,hq", [("bf16", 16, 128, 8), ("bf16", 32, 128, 8),
+                                           ("bf16", 8, 128, 32), ("f32", 16, 64, 4)])
+def test_decode_step_block_manager_pairs(dtype, bs, d, hq):
+    """Requests forked by the block manager, then one step: the pairs
+    pa_bm_append reports, given per request, fold into pa_decode_step on
+    every path (fused at block size 16, a copy kernel first elsewhere)."""
+    say(f"decode_step bm pairs {dtype} bs={bs} d={d}")
+    hkv = 2
+    nb = 96
+    bm = ops.BlockManager(nb, bs)
+    parents = [bm.add(n)[0] for n in (5, 17, 33, 40, 1)]
+    kids = [bm.fork(p) for p in parents for _ in range(2)]
+    ids = kids + parents[:2]
+    slots, pairs = bm.append(ids)
+    assert len(pairs) >= 5
+    max_blocks = 8
+    tab, lens = bm.tables(ids, max_blocks)
+    spec, kc, vc = ops.kv_pool(nb, bs, hkv, d, dtype, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(bs + d)
+    kc.copy_(torch.randn(kc.shape, generator=gen, device=DEV).to(kc.dtype))
+    vc.copy_(torch.randn(vc.shape, generator=gen, device=DEV).to(vc.dtype))
+    s = len(ids)
+    tdt = spec.torch_dtype
+
+    class W:                                  # the fields the helpers read
+        pass
+    w = W()
+    w.k_cache, w.v_cache = kc, vc
+    w.block_tables = torch.as_tensor(tab, device=DEV)
+    w.context_lens = torch.as_tensor(lens, device=DEV)
+    w.max_context_len = int(lens.max())
+    w.q = torch.randn((s, hq, d), generator=gen, device=DEV).to(tdt)
+    w.new_k = torch.randn((s, hkv, d), generator=gen, device=DEV).to(tdt)
+    w.new_v = torch.randn((s, hkv, d), generator=gen, device=DEV).to(tdt)
+    w.scale = d ** -0.5
+    w.num_seqs, w.block_size, w.num_kv_heads, w.head_dim, w.dtype = s, bs, hkv, d, dtype
+    pairs_t = torch.as_tensor(pairs, device=DEV)
+    cow_src = _cow_src_of(w, pairs)
+    assert int((cow_src >= 0).sum()) == len(pairs)
+    ref, got = _step_both_ways(w, spec, pairs_t, cow_src)
+    assert same_bits(got, ref)
+    assert_close(w, got, oracle_decode(w), f"decode_step {dtype} bs={bs}")
