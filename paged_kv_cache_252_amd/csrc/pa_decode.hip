@@ -1198,12 +1198,14 @@ int launch_grouped_r(const DecodeArgs& a) {
 //
 // A request's query tokens are its last n positions: token j (position
 // L - n + j) sees positions [0, L - n + j] ([KG] "A Tiny Block-Table
-// Example", closing paragraphs: never a later token).  One wave takes 16/g
-// consecutive tokens of one request and KV head: MFMA row r is token
-// j0 + r / g, query head h * g + r % g.  All rows read the same physical
-// blocks, so each tile is loaded once for the wave and masked row by row;
-// the partitions and their merge are those of decode, per query row.
-template <bool NT>
+// Example", closing paragraphs: never a later token).  One wave takes
+// RG * 16/g consecutive tokens of one request and KV head as RG groups of
+// 16 MFMA rows: row r of group u is token j0 + u * 16/g + r / g, query head
+// h * g + r % g.  All rows read the same physical blocks, so each tile is
+// loaded once and consumed by every group, masked row by row (RG groups per
+// load cut the tile reads from L2 RG times); the partitions and their merge
+// are those of decode, per query row.
+template <bool NT, int RG>
 __global__ __launch_bounds__(64) void prefill_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
@@ -1224,47 +1226,59 @@ __global__ __launch_bounds__(64) void prefill_kernel(
     // rows are clamped to [0, total_q): a bad q_start cannot move an access
     const int qs = clampi(q_start[seq], 0, total_q);
     const int n = clampi(q_start[seq + 1], qs, total_q) - qs;
-    const int per = FG / group;                 // query tokens per wave
-    const int j0 = tile * per;
+    const int tpg = FG / group;                 // query tokens per row group
+    const int j0 = tile * RG * tpg;
     if (j0 >= n) return;
     const int L = clampi(context_lens[seq], 0, len_clamp);
-    const int j = j0 + row / group;
-    const bool row_ok = j < n;
-    const int qi = qs + (row_ok ? j : j0);
     const int hq = h * group + row % group;
-    const int lim = row_ok ? clampi(L - n + j + 1, 0, L) : 0;   // positions this row sees
-    const int lim_min = clampi(L - n + j0 + 1, 0, L);
-    const int lim_max = clampi(L - n + min(j0 + per, n), 0, L);
-
-    if (max_parts > 1 && part == 0 && h == 0 && row_ok && row % group == 0 && quad == 0)
-        ws_len[qi] = lim;                       // the merge's per-row partition count
-    auto write_zero_row = [&]() {
-        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
+    int qi[RG], lim[RG];
+    bool row_ok[RG];
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+    for (int u = 0; u < RG; ++u) {
+        const int j = j0 + u * tpg + row / group;
+        row_ok[u] = j < n;
+        qi[u] = qs + (row_ok[u] ? j : j0);
+        lim[u] = row_ok[u] ? clampi(L - n + j + 1, 0, L) : 0;   // positions this row sees
+    }
+    const int lim_min = clampi(L - n + j0 + 1, 0, L);
+    const int lim_max = clampi(L - n + min(j0 + RG * tpg, n), 0, L);
+
+#pragma unroll
+    for (int u = 0; u < RG; ++u)
+        if (max_parts > 1 && part == 0 && h == 0 && row_ok[u] && row % group == 0 && quad == 0)
+            ws_len[qi[u]] = lim[u];             // the merge's per-row partition count
+    auto out_row = [&](int u) {
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
     };
     const int tok0 = part * part_tokens;
     if (tok0 >= lim_max) {
-        if (part == 0 && row_ok && lim == 0) write_zero_row();
+#pragma unroll
+        for (int u = 0; u < RG; ++u)
+            if (part == 0 && row_ok[u] && lim[u] == 0) {
+                uint2* o = out_row(u);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+            }
         return;
     }
     const int tok1 = min(lim_max, tok0 + part_tokens);
 
-    bf16x8 qv[4];
-    {
+    bf16x8 qv[RG][4];
+    SoftmaxState st[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            q + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
+            q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
             bf16x8 v = qp[4 * s4 + quad];
-            qv[s4] = row_ok ? v : bf16x8{};
+            qv[u][s4] = row_ok[u] ? v : bf16x8{};
         }
-    }
-    SoftmaxState st;
-    st.m = -INFINITY;
-    st.l = 0.f;
+        st[u].m = -INFINITY;
+        st[u].l = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) st.acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
     const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
@@ -1282,9 +1296,12 @@ __global__ __launch_bounds__(64) void prefill_kernel(
         };
         auto consume_blk = [&](Tile& t, int b) {
             const int start = c0 + FBS * b;
-            const int row_valid = clampi(lim - start, 0, FBS);
             const int v_valid = clampi(lim_max - start, 0, FBS);
-            consume_tile_rows(st, t, qv, scale_log2, lane, row_valid, v_valid, start + FBS > lim_min);
+            const bool masked = start + FBS > lim_min;
+#pragma unroll
+            for (int u = 0; u < RG; ++u)   // (the V masking is the same for every group)
+                consume_tile_rows(st[u], t, qv[u], scale_log2, lane, clampi(lim[u] - start, 0, FBS),
+                                  v_valid, masked);
         };
         // two tiles in flight; past the end the prefetch repeats the last tile
         Tile ta, tb;
@@ -1302,29 +1319,36 @@ __global__ __launch_bounds__(64) void prefill_kernel(
         }
     }
 
-    const float lsum = sum_across_rows(st.l);
-    if (!row_ok) return;
-    if (tok0 >= lim) {                          // nothing of this partition is visible
-        if (part == 0 && lim == 0) write_zero_row();
-        return;
-    }
-    const int my_nparts = (lim + part_tokens - 1) / part_tokens;
-    if (my_nparts == 1) {
-        const float inv = 1.f / lsum;
-        uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi) * num_q_heads + hq) * FD);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
-                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
-        return;
-    }
-    const int64_t pidx = (static_cast<int64_t>(qi) * num_q_heads + hq) * max_parts + part;
-    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+    for (int u = 0; u < RG; ++u) {
+        const float lsum = sum_across_rows(st[u].l);
+        if (!row_ok[u]) continue;
+        if (tok0 >= lim[u]) {                   // nothing of this partition is visible
+            if (part == 0 && lim[u] == 0) {
+                uint2* o = out_row(u);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
-    if (quad == 0) {
-        ws_m[pidx] = st.m;
-        ws_l[pidx] = lsum;
+                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+            }
+            continue;
+        }
+        const int my_nparts = (lim[u] + part_tokens - 1) / part_tokens;
+        if (my_nparts == 1) {
+            const float inv = 1.f / lsum;
+            uint2* o = out_row(u);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                o[4 * jj + quad] = make_uint2(pack_bf16x2(st[u].acc[jj][0] * inv, st[u].acc[jj][1] * inv),
+                                              pack_bf16x2(st[u].acc[jj][2] * inv, st[u].acc[jj][3] * inv));
+            continue;
+        }
+        const int64_t pidx = (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * max_parts + part;
+        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st[u].acc[jj];
+        if (quad == 0) {
+            ws_m[pidx] = st[u].m;
+            ws_l[pidx] = lsum;
+        }
     }
 }
 
@@ -1367,20 +1391,29 @@ int launch_decode(const DecodeArgs& a_in) {
     return launch_generic_d<float>(a);
 }
 
-int launch_prefill(const PrefillArgs& p) {
+template <int RG>
+int launch_prefill_rg(const PrefillArgs& p) {
     const DecodeArgs& a = p.d;
-    const int per = FG / a.group;
+    const int per = RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
-    if (a.num_seqs == 0 || tiles == 0) return PA_OK;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL(prefill_kernel<false>, grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((prefill_kernel<false, RG>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts,
                        a.scale * kLog2e, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        p.ws_len);
-    int st = check_launch("prefill");
+    return check_launch("prefill");
+}
+
+int launch_prefill(const PrefillArgs& p) {
+    const DecodeArgs& a = p.d;
+    if (a.num_seqs == 0 || p.max_q_len == 0) return PA_OK;
+    // two row groups per wave once a chunk fills them: half the tile reads
+    // (measured on the chunked-prefill workload: 1 group 431 us, 2 groups
+    // 273 us, 4 groups 368 us -- 332 VGPRs leave one wave per SIMD)
+    const int st = p.max_q_len >= 2 * (FG / a.group) ? launch_prefill_rg<2>(p) : launch_prefill_rg<1>(p);
     if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
     hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, p.total_q), dim3(kMergeThreads),
                        0, a.stream, p.ws_len, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
