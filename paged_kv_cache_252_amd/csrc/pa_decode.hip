@@ -553,6 +553,63 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
+// consume_tile_rows with a lazily moved running maximum: a row's reference
+// maximum is raised only when a new score exceeds it by more than
+// kLazyMaxLog2 (probabilities then stay below 2^kLazyMaxLog2, safe in bf16 and
+// fp32), and the rescale of the 32 accumulator registers runs only when some
+// row of the wave raised it.  The result is the same softmax up to rounding
+// (any reference value cancels between numerator and denominator, and the
+// merge rescales partitions by their own reference values).  Used where the
+// VALU, not memory, bounds the loop: several query tokens per request.
+constexpr float kLazyMaxLog2 = 8.f;
+
+__device__ __forceinline__ void consume_tile_rows_lazy(SoftmaxState& st, Tile& t,
+                                                       const bf16x8 (&qv)[4], float scale_log2,
+                                                       int lane, int row_valid, int v_valid,
+                                                       bool masked) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
+    const int tok_base = 4 * (lane >> 4);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
+    if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok_base + i >= v_valid) t.v[j][i] = 0;
+    }
+    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    const bool raise = mx > st.m + kLazyMaxLog2;   // false for rows that see nothing
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+        const float alpha = raise ? fast_exp2(st.m - mx) : 1.f;
+        st.m = raise ? mx : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+    }
+    const bool dead = st.m == -INFINITY;           // nothing visible to this row yet
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
+    const unsigned p01 = pack_bf16x2(p[0], p[1]);
+    const unsigned p23 = pack_bf16x2(p[2], p[3]);
+    s16x4 pb;
+    pb[0] = static_cast<short>(p01 & 0xffff);
+    pb[1] = static_cast<short>(p01 >> 16);
+    pb[2] = static_cast<short>(p23 & 0xffff);
+    pb[3] = static_cast<short>(p23 >> 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
+}
+
 // A task is one tile to consume: block position j of the partition, for all
 // members (r = kShared) or for member r alone.
 constexpr int kShared = -1;
@@ -1205,8 +1262,8 @@ int launch_grouped_r(const DecodeArgs& a) {
 // loaded once and consumed by every group, masked row by row (RG groups per
 // load cut the tile reads from L2 RG times); the partitions and their merge
 // are those of decode, per query row.
-template <bool NT, int RG>
-__global__ __launch_bounds__(64) void prefill_kernel(
+template <bool NT, int RG, int W>
+__global__ __launch_bounds__(64 * W) void prefill_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -1214,11 +1271,14 @@ __global__ __launch_bounds__(64) void prefill_kernel(
     int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
     float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
+    // W waves of a workgroup take W consecutive query tiles of one request and
+    // KV head: they read the same blocks at about the same time, so most of
+    // their tile loads are served by the CU's L1.
     const int h = blockIdx.x;
     const int seq = blockIdx.y / tiles_per_seq;
-    const int tile = blockIdx.y - seq * tiles_per_seq;
+    const int tile = (blockIdx.y - seq * tiles_per_seq) * W + static_cast<int>(threadIdx.x >> 6);
     const int part = blockIdx.z;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int row = lane & 15;
     const int quad = lane >> 4;
     auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
@@ -1300,8 +1360,8 @@ __global__ __launch_bounds__(64) void prefill_kernel(
             const bool masked = start + FBS > lim_min;
 #pragma unroll
             for (int u = 0; u < RG; ++u)   // (the V masking is the same for every group)
-                consume_tile_rows(st[u], t, qv[u], scale_log2, lane, clampi(lim[u] - start, 0, FBS),
-                                  v_valid, masked);
+                consume_tile_rows_lazy(st[u], t, qv[u], scale_log2, lane,
+                                       clampi(lim[u] - start, 0, FBS), v_valid, masked);
         };
         // two tiles in flight; past the end the prefetch repeats the last tile
         Tile ta, tb;
@@ -1391,13 +1451,18 @@ int launch_decode(const DecodeArgs& a_in) {
     return launch_generic_d<float>(a);
 }
 
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 2
+#endif
+
 template <int RG>
 int launch_prefill_rg(const PrefillArgs& p) {
     const DecodeArgs& a = p.d;
-    const int per = RG * (FG / a.group);
+    constexpr int W = PA_PREFILL_WAVES;
+    const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_kernel<false, RG>), grid, dim3(64), 0, a.stream,
+    hipLaunchKernelGGL((prefill_kernel<false, RG, W>), grid, dim3(64 * W), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,

@@ -692,8 +692,9 @@ def test_prefill_matches_oracle(group, part):
 
 
 def test_prefill_one_token_equals_decode():
-    """A one-token chunk per request is a decode: with the same partitions,
-    the same bits as pa_decode."""
+    """A one-token chunk per request is a decode: pa_prefill and pa_decode agree
+    with each other (to rounding: prefill raises its running maximum lazily)
+    and with the oracle's decode."""
     say("prefill one token == decode")
     for part in (32, 256, 1024):
         w = inputs.paged_random("pf1", 12, 1, 700, 32, 8, num_blocks=800, seed=62, device=DEV)
@@ -702,7 +703,11 @@ def test_prefill_one_token_equals_decode():
         w.q = w.q_chunk.view(w.num_seqs, w.num_q_heads, w.head_dim)
         got = _run_prefill(w, partition_tokens=part)
         want = run_decode(w, partition_tokens=part)
-        assert same_bits(got.view_as(want), want)
+        ref = oracle_decode(w)
+        assert_close(w, got.view_as(want), ref, f"prefill one token part={part}")
+        assert_close(w, want, ref, f"decode part={part}")
+        diff = (got.view_as(want).float() - want.float()).abs().max().item()
+        assert diff <= BF16_TOL, diff
 
 
 def test_prefill_placement_invariance():
