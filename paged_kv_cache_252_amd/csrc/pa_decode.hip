@@ -185,40 +185,54 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
            (static_cast<unsigned>(float_to_bf16_bits(hi)) << 16);
 }
 
-// One block of 16 tokens.  `valid` = number of this block's tokens that are
-// visible (16 except in the last block of a request).
-__device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf16x8 (&qv)[4],
-                                             float scale_log2, int lane, int valid) {
+// One block of 16 tokens for rows with their own visibility.  row_valid:
+// tokens of this tile visible to this lane's row; v_valid: tokens whose V may
+// be read (the rest are zeroed); rows that have seen nothing yet stay at
+// m = -inf.  The running maximum is moved lazily: a row's reference maximum is
+// raised only when a new score exceeds it by more than kLazyMaxLog2
+// (probabilities then stay below 2^kLazyMaxLog2, safe in bf16 and fp32), and
+// the rescale of the 32 accumulator registers runs only when some row of the
+// wave raised it.  The result is the same softmax up to rounding (any
+// reference value cancels between numerator and denominator, and the merge
+// rescales partitions by their own reference values); it saves VALU work
+// where the VALU, not memory, bounds the loop.
+constexpr float kLazyMaxLog2 = 8.f;
+
+__device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
+                                                  const bf16x8 (&qv)[4], float scale_log2,
+                                                  int lane, int row_valid, int v_valid,
+                                                  bool masked) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
-
     const int tok_base = 4 * (lane >> 4);
-    const bool masked = valid < FBS;   // uniform
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
     if (masked) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (tok_base + i >= valid) sc[i] = -INFINITY;
+            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (tok_base + i >= valid) t.v[j][i] = 0;
+                if (tok_base + i >= v_valid) t.v[j][i] = 0;
     }
     const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const float m_new = fmaxf(st.m, mx);
-    const float alpha = fast_exp2(st.m - m_new);
+    const bool raise = mx > st.m + kLazyMaxLog2;   // false for rows that see nothing
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+        const float alpha = raise ? fast_exp2(st.m - mx) : 1.f;
+        st.m = raise ? mx : st.m;
+        st.l *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+    }
+    const bool dead = st.m == -INFINITY;           // nothing visible to this row yet
     float p[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_new);
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    st.m = m_new;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
-
+    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
+    st.l += (p[0] + p[1]) + (p[2] + p[3]);
     const unsigned p01 = pack_bf16x2(p[0], p[1]);
     const unsigned p23 = pack_bf16x2(p[2], p[3]);
     s16x4 pb;
@@ -229,6 +243,13 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
+}
+
+// One block of 16 tokens seen alike by every row: `valid` of its tokens are
+// visible (16 except in the last block of a request).
+__device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf16x8 (&qv)[4],
+                                             float scale_log2, int lane, int valid) {
+    consume_tile_rows(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
 }
 
 // APPEND: the call also appends each request's newest token (position L-1):
@@ -505,110 +526,6 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
 // with the other members' rows masked out.  Rows keep separate online-softmax
 // states, so the arithmetic per row is the same as one request per wave; only
 // the partition's tile sequence differs.
-
-// consume_tile for rows with their own visibility.  row_valid: tokens of this
-// tile visible to this lane's row; v_valid: tokens whose V may be read (the
-// rest are zeroed); rows that have seen nothing yet stay at m = -inf.
-__device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
-                                                  const bf16x8 (&qv)[4], float scale_log2,
-                                                  int lane, int row_valid, int v_valid,
-                                                  bool masked) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
-    const int tok_base = 4 * (lane >> 4);
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
-    if (masked) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (tok_base + i >= v_valid) t.v[j][i] = 0;
-    }
-    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const float m_new = fmaxf(st.m, mx);
-    const bool dead = m_new == -INFINITY;   // nothing visible to this row yet
-    const float alpha = dead ? 1.f : fast_exp2(st.m - m_new);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - m_new);
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    st.m = m_new;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
-    const unsigned p01 = pack_bf16x2(p[0], p[1]);
-    const unsigned p23 = pack_bf16x2(p[2], p[3]);
-    s16x4 pb;
-    pb[0] = static_cast<short>(p01 & 0xffff);
-    pb[1] = static_cast<short>(p01 >> 16);
-    pb[2] = static_cast<short>(p23 & 0xffff);
-    pb[3] = static_cast<short>(p23 >> 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
-}
-
-// consume_tile_rows with a lazily moved running maximum: a row's reference
-// maximum is raised only when a new score exceeds it by more than
-// kLazyMaxLog2 (probabilities then stay below 2^kLazyMaxLog2, safe in bf16 and
-// fp32), and the rescale of the 32 accumulator registers runs only when some
-// row of the wave raised it.  The result is the same softmax up to rounding
-// (any reference value cancels between numerator and denominator, and the
-// merge rescales partitions by their own reference values).  Used where the
-// VALU, not memory, bounds the loop: several query tokens per request.
-constexpr float kLazyMaxLog2 = 8.f;
-
-__device__ __forceinline__ void consume_tile_rows_lazy(SoftmaxState& st, Tile& t,
-                                                       const bf16x8 (&qv)[4], float scale_log2,
-                                                       int lane, int row_valid, int v_valid,
-                                                       bool masked) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
-    const int tok_base = 4 * (lane >> 4);
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
-    if (masked) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (tok_base + i >= v_valid) t.v[j][i] = 0;
-    }
-    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const bool raise = mx > st.m + kLazyMaxLog2;   // false for rows that see nothing
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
-        const float alpha = raise ? fast_exp2(st.m - mx) : 1.f;
-        st.m = raise ? mx : st.m;
-        st.l *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
-    }
-    const bool dead = st.m == -INFINITY;           // nothing visible to this row yet
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
-    st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    const unsigned p01 = pack_bf16x2(p[0], p[1]);
-    const unsigned p23 = pack_bf16x2(p[2], p[3]);
-    s16x4 pb;
-    pb[0] = static_cast<short>(p01 & 0xffff);
-    pb[1] = static_cast<short>(p01 >> 16);
-    pb[2] = static_cast<short>(p23 & 0xffff);
-    pb[3] = static_cast<short>(p23 >> 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
-}
 
 // A task is one tile to consume: block position j of the partition, for all
 // members (r = kShared) or for member r alone.
@@ -1360,7 +1277,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
             const bool masked = start + FBS > lim_min;
 #pragma unroll
             for (int u = 0; u < RG; ++u)   // (the V masking is the same for every group)
-                consume_tile_rows_lazy(st[u], t, qv[u], scale_log2, lane,
+                consume_tile_rows(st[u], t, qv[u], scale_log2, lane,
                                        clampi(lim[u] - start, 0, FBS), v_valid, masked);
         };
         // two tiles in flight; past the end the prefetch repeats the last tile
