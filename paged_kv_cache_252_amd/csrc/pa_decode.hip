@@ -186,9 +186,9 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 }
 
 // One block of 16 tokens for rows with their own visibility.  row_valid:
-// tokens of this tile visible to this lane's row; v_valid: tokens whose V may
-// be read (the rest are zeroed); rows that have seen nothing yet stay at
-// m = -inf.  The running maximum is moved lazily: a row's reference maximum is
+// tokens of this tile visible to this lane's row (applied when `masked`);
+// v_valid: tokens whose V may be read (the rest are zeroed); rows that have
+// seen nothing yet stay at m = -inf.  The running maximum is moved lazily: a row's reference maximum is
 // raised only when a new score exceeds it by more than kLazyMaxLog2
 // (probabilities then stay below 2^kLazyMaxLog2, safe in bf16 and fp32), and
 // the rescale of the 32 accumulator registers runs only when some row of the
@@ -213,6 +213,8 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (tok_base + i >= row_valid) sc[i] = -INFINITY;
+    }
+    if (v_valid < FBS) {   // (wave-uniform) values past the history may be stale bytes
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -614,6 +616,7 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
     // has no tokens), then whether position j is shared.
     int phys[MAXR];
     int p_sh = 0, v_sh = 0;
+    int mem_at = 0;          // lane j: the members with tokens at position j (a bit each)
     bool sh = true, full = true;
 #pragma unroll
     for (int r = 0; r < MAXR; ++r) {
@@ -622,6 +625,7 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
             const int Lm = __builtin_amdgcn_readlane(Lr, r);
             const int valid = min(max(Lm - (tok0 + FBS * lane), 0), FBS);
             if (lane < nblk && valid > 0) {
+                mem_at |= 1 << r;
                 phys[r] = clamp_block(
                     block_tables[static_cast<int64_t>(seq0 + r) * max_blocks_per_seq + blk0 + lane],
                     num_blocks);
@@ -668,11 +672,8 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
     auto first_task = [&](int j) {
         if (!grouped) return valid_of(r_wave, j) > 0 ? r_wave : MAXR;
         if (is_shared(j)) return kShared;
-        int rr = MAXR;
-#pragma unroll
-        for (int r = MAXR - 1; r >= 0; --r)
-            if (r < nmem && valid_of(r, j) > 0) rr = r;
-        return rr;
+        const unsigned m = static_cast<unsigned>(__builtin_amdgcn_readlane(mem_at, j));
+        return m != 0 ? static_cast<int>(__builtin_ctz(m)) : MAXR;
     };
     struct Cursor { int j, r; };
     auto advance = [&](Cursor c) {
@@ -680,12 +681,10 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
             const int j = c.j + 1;
             return (j < nblk && valid_of(r_wave, j) > 0) ? Cursor{j, r_wave} : Cursor{nblk, 0};
         }
-        if (c.r != kShared) {
-            int rr = MAXR;
-#pragma unroll
-            for (int r = MAXR - 1; r >= 0; --r)
-                if (r > c.r && r < nmem && valid_of(r, c.j) > 0) rr = r;
-            if (rr < MAXR) return Cursor{c.j, rr};
+        if (c.r != kShared) {   // the next member with tokens at this position
+            const unsigned m = static_cast<unsigned>(__builtin_amdgcn_readlane(mem_at, c.j)) &
+                               ~((2u << c.r) - 1u);
+            if (m != 0) return Cursor{c.j, static_cast<int>(__builtin_ctz(m))};
         }
         const int j = c.j + 1;
         return Cursor{j, j < nblk ? first_task(j) : 0};
