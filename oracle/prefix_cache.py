@@ -19,7 +19,7 @@ manager's prefix cache.  What it follows:
   cached block whose count reaches zero is kept for reuse, and only such
   blocks are ever evicted, oldest first.
 
-Readings where the pages are silent (each is stated in the design doc as well):
+Readings where the pages are silent:
 
 * The hash is 64-bit FNV-1a (Fowler, Noll and Vo's published definition)
   over the parent hash (8 bytes, little-endian; the salt for the first

@@ -198,7 +198,7 @@ int64_t pa_bm_num_cached(const pa_bm_t* bm) {
     return bm ? static_cast<int64_t>(bm->by_key.size()) : -1;
 }
 
-int pa_bm_add(pa_bm_t* bm, const int32_t* tokens, int64_t num_tokens, int64_t* seq_id,
+static int pa_bm_add_impl(pa_bm_t* bm, const int32_t* tokens, int64_t num_tokens, int64_t* seq_id,
               int64_t* num_cached_tokens) {
     if (bm == nullptr || seq_id == nullptr) return fail(PA_ERR_NULL, "manager or seq_id is NULL");
     if (num_tokens < 0 || num_tokens > INT32_MAX)
@@ -254,7 +254,7 @@ int pa_bm_add(pa_bm_t* bm, const int32_t* tokens, int64_t num_tokens, int64_t* s
     return ok();
 }
 
-int pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t* child) {
+static int pa_bm_fork_impl(pa_bm_t* bm, int64_t parent, int64_t* child) {
     if (bm == nullptr || child == nullptr) return fail(PA_ERR_NULL, "manager or child is NULL");
     auto it = bm->seqs.find(parent);
     if (it == bm->seqs.end()) return fail(PA_ERR_NOT_FOUND, "unknown sequence %lld", (long long)parent);
@@ -276,7 +276,7 @@ int pa_bm_free(pa_bm_t* bm, int64_t seq_id) {
     return ok();
 }
 
-int pa_bm_append(pa_bm_t* bm, const int64_t* seq_ids, const int32_t* tokens, int32_t n,
+static int pa_bm_append_impl(pa_bm_t* bm, const int64_t* seq_ids, const int32_t* tokens, int32_t n,
                  int64_t* slots, int64_t* cow_pairs, int32_t* num_cow) {
     if (bm == nullptr || num_cow == nullptr) return fail(PA_ERR_NULL, "manager or num_cow is NULL");
     if (n < 0) return fail(PA_ERR_SHAPE, "n %d < 0", n);
@@ -365,7 +365,7 @@ int pa_bm_slots(const pa_bm_t* bm, int64_t seq_id, int64_t start, int64_t count,
     return ok();
 }
 
-int pa_bm_tables(const pa_bm_t* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+static int pa_bm_tables_impl(const pa_bm_t* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                  int32_t* tables, int32_t* lens) {
     if (bm == nullptr) return fail(PA_ERR_NULL, "manager is NULL");
     if (n < 0 || max_blocks < 1) return fail(PA_ERR_SHAPE, "n %d or max_blocks %d out of range", n, max_blocks);
@@ -406,6 +406,44 @@ int pa_bm_refcount(const pa_bm_t* bm, int64_t block, int32_t* refcount) {
         return fail(PA_ERR_SHAPE, "block %lld outside [0, %d)", (long long)block, bm->num_blocks);
     *refcount = bm->refcount[block];
     return ok();
+}
+
+}  // extern "C"
+
+// Host memory exhaustion inside a container operation must not cross the C
+// boundary as an exception: it is reported as PA_ERR_NO_SPACE, after which
+// the manager may hold a partly applied operation and should be destroyed.
+template <typename F>
+static int guarded(const char* fn, F&& f) {
+    try {
+        return f();
+    } catch (const std::bad_alloc&) {
+        return fail(PA_ERR_NO_SPACE, "%s: out of host memory", fn);
+    } catch (...) {
+        return fail(PA_ERR_NO_SPACE, "%s: unexpected host failure", fn);
+    }
+}
+
+extern "C" {
+
+int pa_bm_add(pa_bm_t* bm, const int32_t* tokens, int64_t num_tokens, int64_t* seq_id,
+              int64_t* num_cached_tokens) {
+    return guarded("pa_bm_add", [&] { return pa_bm_add_impl(bm, tokens, num_tokens, seq_id, num_cached_tokens); });
+}
+
+int pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t* child) {
+    return guarded("pa_bm_fork", [&] { return pa_bm_fork_impl(bm, parent, child); });
+}
+
+int pa_bm_append(pa_bm_t* bm, const int64_t* seq_ids, const int32_t* tokens, int32_t n,
+                 int64_t* slots, int64_t* cow_pairs, int32_t* num_cow) {
+    return guarded("pa_bm_append",
+                   [&] { return pa_bm_append_impl(bm, seq_ids, tokens, n, slots, cow_pairs, num_cow); });
+}
+
+int pa_bm_tables(const pa_bm_t* bm, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                 int32_t* tables, int32_t* lens) {
+    return guarded("pa_bm_tables", [&] { return pa_bm_tables_impl(bm, seq_ids, n, max_blocks, tables, lens); });
 }
 
 }  // extern "C"
