@@ -158,19 +158,26 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
 
 def measured_traffic(workload: str, part: int, stream_kv: bool):
     """HBM bytes per decode call from the committed counter summary, or None when
-    there is none for this workload or the decode source has changed since."""
-    import hashlib
+    there is none for this workload or the decode sources have changed since."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    if (digest != rec["source_sha256"] or rec["partition_tokens"] != part
+    if (sources_digest(rec["sources"]) != rec["sources_sha256"] or rec["partition_tokens"] != part
             or rec["stream_kv"] != stream_kv):
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def sources_digest(paths) -> str:
+    """sha256 over the given source files, in order (the decode kernel's)."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

@@ -22,7 +22,7 @@ LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pa_abi.cpp", "pa_decode.hip", "pa_cache_ops.hip", "pa_blocks.cpp"]
+SOURCES = ["pa_abi.cpp", "pa_decode.hip", "pa_prefill.hip", "pa_cache_ops.hip", "pa_blocks.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -32,227 +32,21 @@
 //
 // Generic path (fp32 or bf16, other head_dim / block_size): one wave per
 // (request, query head, partition), one token per step, lanes over dims.
-
-#include <math.h>
-
-#include "pa_internal.h"
+#include "pa_tile.h"
 
 namespace pa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
-    return __uint_as_float(static_cast<uint32_t>(b) << 16);
-}
-
-__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-    __bf16 h = static_cast<__bf16>(f);   // round to nearest even (v_cvt_pk_bf16_f32)
-    return __builtin_bit_cast(uint16_t, h);
-}
-
-template <typename T> __device__ __forceinline__ float load_f32(const T* p);
-template <> __device__ __forceinline__ float load_f32<float>(const float* p) { return *p; }
-template <> __device__ __forceinline__ float load_f32<uint16_t>(const uint16_t* p) {
-    return bf16_bits_to_float(*p);
-}
-
-template <typename T> __device__ __forceinline__ void store_f32(T* p, float v);
-template <> __device__ __forceinline__ void store_f32<float>(float* p, float v) { *p = v; }
-template <> __device__ __forceinline__ void store_f32<uint16_t>(uint16_t* p, float v) {
-    *p = float_to_bf16_bits(v);
-}
-
-__device__ __forceinline__ int clamp_block(int e, int64_t num_blocks) {
-    return (e >= 0 && static_cast<int64_t>(e) < num_blocks) ? e : 0;
-}
-
-// ============================================================================
-// Fast path
-// ============================================================================
 
 #ifndef PA_FAST_NBUF
 #define PA_FAST_NBUF 2           // tiles in the load ring of the fast path
 #endif
 
-
-constexpr int FD = 128;          // head_dim
-constexpr int FBS = 16;          // block_size
-constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile
-constexpr int FG = 16;           // query rows of the score MFMA
 constexpr int kMaxWgParts = 8;   // partitions merged inside one workgroup
 constexpr size_t kMaxWgLds = 32768;
 
-struct Tile {
-    bf16x8 k[4];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
-    s16x4 v[8];    // V: dim 16*j + l%16, tokens 4*(l/16)..+3 -> A operand of PV j
-};
-
-// NT: non-temporal loads (streaming hint), for batches without shared blocks.
-template <bool NT, typename V>
-__device__ __forceinline__ V load16(const V* p) {
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
-template <bool NT>
-__device__ __forceinline__ void load_tile(Tile& t, const __bf16* __restrict__ k_tile,
-                                          const __bf16* __restrict__ v_tile, int lane) {
-    const bf16x8* kp = reinterpret_cast<const bf16x8*>(k_tile) + lane;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + 64 * s);
-    const s16x4* vp = reinterpret_cast<const s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 64 * j);
-}
-
-// The inverse of load_tile: the tile's bytes back to a block (whole lines),
-// with the non-temporal hint (measured: 2.4 us less on the fan-out step).
-__device__ __forceinline__ void store_tile(const Tile& t, __bf16* __restrict__ k_tile,
-                                           __bf16* __restrict__ v_tile, int lane) {
-    bf16x8* kp = reinterpret_cast<bf16x8*>(k_tile) + lane;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) __builtin_nontemporal_store(t.k[s], kp + 64 * s);
-    s16x4* vp = reinterpret_cast<s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(t.v[j], vp + 64 * j);
-}
-
-// The same tile out of blocks of BS tokens: tile `sub` of one block when BS
-// is a multiple of 16 (the block holds BS/16 such tiles back to back); for
-// BS = 8 (K [D/8][8][8], V [D][8] per head) the tile's first 8 tokens come
-// from block `a`, the next 8 from block `b` (K rows 8..15 and V token groups
-// 2..3).  k_a/v_a, k_b/v_b point at the head's region in blocks a and b.
-template <bool NT, int BS>
-__device__ __forceinline__ void load_tile_bs(Tile& t, const __bf16* __restrict__ k_a,
-                                             const __bf16* __restrict__ v_a,
-                                             const __bf16* __restrict__ k_b,
-                                             const __bf16* __restrict__ v_b, int sub, int lane) {
-    const int row = lane & 15, quad = lane >> 4;
-    if constexpr (BS >= 16) {                 // tile `sub` of the block: a 16-position tile
-        load_tile<NT>(t, k_a + sub * FTILE, v_a + sub * FTILE, lane);
-    } else {
-        static_assert(BS == 8, "blocks of 8, 16, 32 or 64 tokens");
-        const bf16x8* kp = reinterpret_cast<const bf16x8*>(row < 8 ? k_a : k_b) + (row & 7);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
-        const s16x4* vp = reinterpret_cast<const s16x4*>(quad < 2 ? v_a : v_b) + row * 2 + (quad & 1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 32 * j);
-    }
-}
-
-struct SoftmaxState {
-    float m;        // running max of log2-domain scores for query row lane%16
-    float l;        // this lane's share of the running sum
-    f32x4 acc[8];   // output accumulator
-};
-
-// Reductions across the four 16-lane rows of the wave with the gfx950 row
-// swaps: permlane16_swap exchanges rows (0,1) and (2,3), permlane32_swap
-// exchanges rows (0,2) and (1,3); each lane keeps its position in the row.
-__device__ __forceinline__ float max_across_rows(float x) {
-    const unsigned u = __float_as_uint(x);
-    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const unsigned w = __float_as_uint(y);
-    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float sum_across_rows(float x) {
-    const unsigned u = __float_as_uint(x);
-    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const unsigned w = __float_as_uint(y);
-    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ f32x4 fma4(f32x4 a, float w, f32x4 c) {
-    return f32x4{__builtin_fmaf(a[0], w, c[0]), __builtin_fmaf(a[1], w, c[1]),
-                 __builtin_fmaf(a[2], w, c[2]), __builtin_fmaf(a[3], w, c[3])};
-}
-
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    return static_cast<unsigned>(float_to_bf16_bits(lo)) |
-           (static_cast<unsigned>(float_to_bf16_bits(hi)) << 16);
-}
-
-// One block of 16 tokens for rows with their own visibility.  row_valid:
-// tokens of this tile visible to this lane's row (applied when `masked`);
-// v_valid: tokens whose V may be read (the rest are zeroed); rows that have
-// seen nothing yet stay at m = -inf.  The running maximum is moved lazily: a row's reference maximum is
-// raised only when a new score exceeds it by more than kLazyMaxLog2
-// (probabilities then stay below 2^kLazyMaxLog2, safe in bf16 and fp32), and
-// the rescale of the 32 accumulator registers runs only when some row of the
-// wave raised it.  The result is the same softmax up to rounding (any
-// reference value cancels between numerator and denominator, and the merge
-// rescales partitions by their own reference values); it saves VALU work
-// where the VALU, not memory, bounds the loop.
-constexpr float kLazyMaxLog2 = 8.f;
-
-__device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
-                                                  const bf16x8 (&qv)[4], float scale_log2,
-                                                  int lane, int row_valid, int v_valid,
-                                                  bool masked) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
-    const int tok_base = 4 * (lane >> 4);
-    float sc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = s[i] * scale_log2;
-    if (masked) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (tok_base + i >= row_valid) sc[i] = -INFINITY;
-    }
-    if (v_valid < FBS) {   // (wave-uniform) values past the history may be stale bytes
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (tok_base + i >= v_valid) t.v[j][i] = 0;
-    }
-    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const bool raise = mx > st.m + kLazyMaxLog2;   // false for rows that see nothing
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
-        const float alpha = raise ? fast_exp2(st.m - mx) : 1.f;
-        st.m = raise ? mx : st.m;
-        st.l *= alpha;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
-    }
-    const bool dead = st.m == -INFINITY;           // nothing visible to this row yet
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
-    st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    const unsigned p01 = pack_bf16x2(p[0], p[1]);
-    const unsigned p23 = pack_bf16x2(p[2], p[3]);
-    s16x4 pb;
-    pb[0] = static_cast<short>(p01 & 0xffff);
-    pb[1] = static_cast<short>(p01 >> 16);
-    pb[2] = static_cast<short>(p23 & 0xffff);
-    pb[3] = static_cast<short>(p23 >> 16);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
-}
-
-// One block of 16 tokens seen alike by every row: `valid` of its tokens are
-// visible (16 except in the last block of a request).
-__device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf16x8 (&qv)[4],
-                                             float scale_log2, int lane, int valid) {
-    consume_tile_rows(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
-}
+// ============================================================================
+// Fast path
+// ============================================================================
 
 // APPEND: the call also appends each request's newest token (position L-1):
 // the wave of the request's last partition stores k_new/v_new into the cache
@@ -1165,170 +959,17 @@ int launch_grouped_r(const DecodeArgs& a) {
     return launch_grouped<16, NT, APPEND>(a, members);
 }
 
-// ============================================================================
-// Several query tokens per request (chunked prefill, several-token checks)
-// ============================================================================
-//
-// A request's query tokens are its last n positions: token j (position
-// L - n + j) sees positions [0, L - n + j] ([KG] "A Tiny Block-Table
-// Example", closing paragraphs: never a later token).  One wave takes
-// RG * 16/g consecutive tokens of one request and KV head as RG groups of
-// 16 MFMA rows: row r of group u is token j0 + u * 16/g + r / g, query head
-// h * g + r % g.  All rows read the same physical blocks, so each tile is
-// loaded once and consumed by every group, masked row by row (RG groups per
-// load cut the tile reads from L2 RG times); the partitions and their merge
-// are those of decode, per query row.
-template <bool NT, int RG, int W>
-__global__ __launch_bounds__(64 * W) void prefill_kernel(
-    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
-    const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int64_t num_blocks, int64_t blk_stride, int total_q, int num_q_heads, int group,
-    int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
-    float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
-    // W waves of a workgroup take W consecutive query tiles of one request and
-    // KV head: they read the same blocks at about the same time, so most of
-    // their tile loads are served by the CU's L1.
-    const int h = blockIdx.x;
-    const int seq = blockIdx.y / tiles_per_seq;
-    const int tile = (blockIdx.y - seq * tiles_per_seq) * W + static_cast<int>(threadIdx.x >> 6);
-    const int part = blockIdx.z;
-    const int lane = threadIdx.x & 63;
-    const int row = lane & 15;
-    const int quad = lane >> 4;
-    auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
-
-    // rows are clamped to [0, total_q): a bad q_start cannot move an access
-    const int qs = clampi(q_start[seq], 0, total_q);
-    const int n = clampi(q_start[seq + 1], qs, total_q) - qs;
-    const int tpg = FG / group;                 // query tokens per row group
-    const int j0 = tile * RG * tpg;
-    if (j0 >= n) return;
-    const int L = clampi(context_lens[seq], 0, len_clamp);
-    const int hq = h * group + row % group;
-    int qi[RG], lim[RG];
-    bool row_ok[RG];
-#pragma unroll
-    for (int u = 0; u < RG; ++u) {
-        const int j = j0 + u * tpg + row / group;
-        row_ok[u] = j < n;
-        qi[u] = qs + (row_ok[u] ? j : j0);
-        lim[u] = row_ok[u] ? clampi(L - n + j + 1, 0, L) : 0;   // positions this row sees
-    }
-    const int lim_min = clampi(L - n + j0 + 1, 0, L);
-    const int lim_max = clampi(L - n + min(j0 + RG * tpg, n), 0, L);
-
-#pragma unroll
-    for (int u = 0; u < RG; ++u)
-        if (max_parts > 1 && part == 0 && h == 0 && row_ok[u] && row % group == 0 && quad == 0)
-            ws_len[qi[u]] = lim[u];             // the merge's per-row partition count
-    auto out_row = [&](int u) {
-        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
-    };
-    const int tok0 = part * part_tokens;
-    if (tok0 >= lim_max) {
-#pragma unroll
-        for (int u = 0; u < RG; ++u)
-            if (part == 0 && row_ok[u] && lim[u] == 0) {
-                uint2* o = out_row(u);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
-            }
-        return;
-    }
-    const int tok1 = min(lim_max, tok0 + part_tokens);
-
-    bf16x8 qv[RG][4];
-    SoftmaxState st[RG];
-#pragma unroll
-    for (int u = 0; u < RG; ++u) {
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            bf16x8 v = qp[4 * s4 + quad];
-            qv[u][s4] = row_ok[u] ? v : bf16x8{};
-        }
-        st[u].m = -INFINITY;
-        st[u].l = 0.f;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
-    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
-    // The partition is walked in chunks of 64 blocks, one table entry per lane.
-    for (int c0 = tok0; c0 < tok1; c0 += 64 * FBS) {
-        const int blk0 = c0 / FBS;
-        const int nblk = (min(tok1, c0 + 64 * FBS) - c0 + FBS - 1) / FBS;   // 1..64
-        const int my_phys = lane < nblk
-            ? clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
-                          num_blocks)
-            : 0;
-        auto load_blk = [&](Tile& t, int b) {
-            const int64_t o = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, b)) * blk_stride;
-            load_tile<NT>(t, k_head + o, v_head + o, lane);
-        };
-        auto consume_blk = [&](Tile& t, int b) {
-            const int start = c0 + FBS * b;
-            const int v_valid = clampi(lim_max - start, 0, FBS);
-            const bool masked = start + FBS > lim_min;
-#pragma unroll
-            for (int u = 0; u < RG; ++u)   // (the V masking is the same for every group)
-                consume_tile_rows(st[u], t, qv[u], scale_log2, lane,
-                                       clampi(lim[u] - start, 0, FBS), v_valid, masked);
-        };
-        // two tiles in flight; past the end the prefetch repeats the last tile
-        Tile ta, tb;
-        load_blk(ta, 0);
-        for (int b = 0; b < nblk; b += 2) {
-            load_blk(tb, min(b + 1, nblk - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            consume_blk(ta, b);
-            __builtin_amdgcn_sched_barrier(0);
-            if (b + 1 >= nblk) break;
-            load_blk(ta, min(b + 2, nblk - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            consume_blk(tb, b + 1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-#pragma unroll
-    for (int u = 0; u < RG; ++u) {
-        const float lsum = sum_across_rows(st[u].l);
-        if (!row_ok[u]) continue;
-        if (tok0 >= lim[u]) {                   // nothing of this partition is visible
-            if (part == 0 && lim[u] == 0) {
-                uint2* o = out_row(u);
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
-            }
-            continue;
-        }
-        const int my_nparts = (lim[u] + part_tokens - 1) / part_tokens;
-        if (my_nparts == 1) {
-            const float inv = 1.f / lsum;
-            uint2* o = out_row(u);
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                o[4 * jj + quad] = make_uint2(pack_bf16x2(st[u].acc[jj][0] * inv, st[u].acc[jj][1] * inv),
-                                              pack_bf16x2(st[u].acc[jj][2] * inv, st[u].acc[jj][3] * inv));
-            continue;
-        }
-        const int64_t pidx = (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * max_parts + part;
-        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st[u].acc[jj];
-        if (quad == 0) {
-            ws_m[pidx] = st[u].m;
-            ws_l[pidx] = lsum;
-        }
-    }
-}
-
 }  // namespace
+
+int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t len_clamp,
+                 int32_t part_tokens, int32_t max_parts, const float* ws_acc, const float* ws_m,
+                 const float* ws_l, void* out, hipStream_t stream) {
+    if (rows == 0) return PA_OK;
+    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(num_q_heads, rows), dim3(kMergeThreads), 0,
+                       stream, lens, num_q_heads, len_clamp, part_tokens, max_parts, ws_acc, ws_m, ws_l,
+                       static_cast<uint16_t*>(out));
+    return check_launch("merge");
+}
 
 int launch_decode(const DecodeArgs& a_in) {
     pa_cache_desc_t c{a_in.num_blocks, a_in.block_size, a_in.num_kv_heads, a_in.head_dim, a_in.dtype,
@@ -1365,41 +1006,6 @@ int launch_decode(const DecodeArgs& a_in) {
     }
     if (a.dtype == PA_BF16) return launch_generic_d<uint16_t>(a);
     return launch_generic_d<float>(a);
-}
-
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 2
-#endif
-
-template <int RG>
-int launch_prefill_rg(const PrefillArgs& p) {
-    const DecodeArgs& a = p.d;
-    constexpr int W = PA_PREFILL_WAVES;
-    const int per = W * RG * (FG / a.group);
-    const int tiles = (p.max_q_len + per - 1) / per;
-    dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_kernel<false, RG, W>), grid, dim3(64 * W), 0, a.stream,
-                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
-                       static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
-                       a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
-                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts,
-                       a.scale * kLog2e, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
-                       p.ws_len);
-    return check_launch("prefill");
-}
-
-int launch_prefill(const PrefillArgs& p) {
-    const DecodeArgs& a = p.d;
-    if (a.num_seqs == 0 || p.max_q_len == 0) return PA_OK;
-    // two row groups per wave once a chunk fills them: half the tile reads
-    // (measured on the chunked-prefill workload: 1 group 431 us, 2 groups
-    // 273 us, 4 groups 368 us -- 332 VGPRs leave one wave per SIMD)
-    const int st = p.max_q_len >= 2 * (FG / a.group) ? launch_prefill_rg<2>(p) : launch_prefill_rg<1>(p);
-    if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
-    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, p.total_q), dim3(kMergeThreads),
-                       0, a.stream, p.ws_len, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
-                       a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
-    return check_launch("prefill reduce");
 }
 
 }  // namespace pa

@@ -141,6 +141,14 @@ struct PrefillArgs {
 
 int launch_prefill(const PrefillArgs& a);
 
+// The split-K merge of bf16, head_dim 128 partials: row r (of `rows`) and
+// query head hq combine the ceil(lens[r] / part_tokens) partitions of
+// ws_* [rows][Hq][max_parts] into out[r][hq] (rows with one partition are
+// left alone: their kernel wrote them).
+int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t len_clamp,
+                 int32_t part_tokens, int32_t max_parts, const float* ws_acc, const float* ws_m,
+                 const float* ws_l, void* out, hipStream_t stream);
+
 int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
                     const void* v_new, const int64_t* slots, int32_t num_tokens,
                     hipStream_t stream);
