@@ -134,9 +134,11 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
     pairs = remap[host(w.cow_pairs)] if w.cow_pairs is not None else None
     e = 2 if w.dtype == "bf16" else 4
     per_tok = w.num_kv_heads * w.head_dim * 2 * e
-    done, kv_bytes = 0, 0
+    done, kv_bytes, total = 0, 0, 0
     t0 = time.perf_counter()
-    while done < w.num_seqs and (time.perf_counter() - t0) < budget_s:
+    while (time.perf_counter() - t0) < budget_s:      # whole passes repeat until the budget
+        if done == w.num_seqs:
+            done = 0
         n = min(w.num_seqs - done, max(1, w.num_seqs // 8))
         rows = slice(done, done + n)
         k_use, v_use = kp, vp
@@ -149,11 +151,14 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
         paged.decode(q[rows], k_use, v_use, bt_c[rows], lens[rows], w.scale, **args)
         kv_bytes += int(lens[rows].sum()) * per_tok
         done += n
+        total += n
     dt = time.perf_counter() - t0
     return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {done} of {w.num_seqs} requests ({w.name}), one pass: copy/write "
-                      f"for those requests then fp64 decode, {dt:.2f} s",
-            "tokens_per_s": done / dt, "seconds": dt}
+            "sample": f"{total} request decodes ({total / w.num_seqs:.2f} passes over the "
+                      f"{w.num_seqs} requests of {w.name}, in chunks of "
+                      f"{max(1, w.num_seqs // 8)}): copy/write for those requests then fp64 "
+                      f"decode, {dt:.2f} s",
+            "tokens_per_s": total / dt, "seconds": dt}
 
 
 def measured_traffic(workload: str, part: int, stream_kv: bool):
