@@ -208,6 +208,77 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
+// consume_tile_rows for RG groups of 16 rows that read the same tile (same
+// arithmetic per row): every group's score MFMAs are issued first, the V
+// masking is done once, and one branch covers the rescale of all groups, so
+// the matrix work of one group overlaps the softmax of another.
+template <int RG>
+__device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile& t,
+                                                    const bf16x8 (&qv)[RG][4], float scale_log2,
+                                                    int lane, const int (&row_valid)[RG],
+                                                    int v_valid, bool masked) {
+    f32x4 s[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int u = 0; u < RG; ++u)
+            s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[u][k], s[u], 0, 0, 0);
+    const int tok_base = 4 * (lane >> 4);
+    if (v_valid < FBS) {   // (wave-uniform) values past the history may be stale bytes
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok_base + i >= v_valid) t.v[j][i] = 0;
+    }
+    float sc[RG][4], mx[RG];
+    bool raise[RG];
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[u][i] = s[u][i] * scale_log2;
+        if (masked) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (tok_base + i >= row_valid[u]) sc[u][i] = -INFINITY;
+        }
+        mx[u] = max_across_rows(fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+        raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
+        any = any || raise[u];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) != 0) {   // wave-uniform
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            const float alpha = raise[u] ? fast_exp2(st[u].m - mx[u]) : 1.f;
+            st[u].m = raise[u] ? mx[u] : st[u].m;
+            st[u].l *= alpha;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) st[u].acc[j] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+        const bool dead = st[u].m == -INFINITY;
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[u][i] - st[u].m);
+        st[u].l += (p[0] + p[1]) + (p[2] + p[3]);
+        const unsigned p01 = pack_bf16x2(p[0], p[1]);
+        const unsigned p23 = pack_bf16x2(p[2], p[3]);
+        s16x4 pb;
+        pb[0] = static_cast<short>(p01 & 0xffff);
+        pb[1] = static_cast<short>(p01 >> 16);
+        pb[2] = static_cast<short>(p23 & 0xffff);
+        pb[3] = static_cast<short>(p23 >> 16);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            st[u].acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st[u].acc[j], 0, 0, 0);
+    }
+}
+
 // One block of 16 tokens seen alike by every row: `valid` of its tokens are
 // visible (16 except in the last block of a request).
 __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf16x8 (&qv)[4],
