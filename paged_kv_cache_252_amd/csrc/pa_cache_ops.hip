@@ -13,41 +13,135 @@ namespace pa {
 namespace {
 
 // ---- write: [KG] "Follow One Token Address" read backwards -----------------
-// One workgroup per new token.  K rows go out as 16-byte chunks of x
-// consecutive dims (the K layout keeps them contiguous); V is dim-major, so
-// each element is stored on its own.
+// One workgroup per (16 consecutive new tokens, KV head, 256-byte slab of the
+// head's dims).  Tokens whose slots follow one another inside one aligned
+// window of 16 positions of a tile (a prompt or a chunk written in order) form
+// a segment, written by the workgroup that holds its first token, so a
+// workgroup covers at most 31 tokens.  Their rows are staged in LDS with every
+// load in flight at once (the slot loads and these are the only waits); then K
+// goes out as 16-byte chunks of x consecutive dims, position-fastest (a
+// segment's chunk is one contiguous run), and V as 16-byte runs of x
+// consecutive positions of one dim row; a run only partly inside the segment
+// is stored element by element.  A lone token (a decode step) is a segment of
+// one.
 template <typename E>
 __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
                                                        E* __restrict__ v_cache,
                                                        const E* __restrict__ k_new,
                                                        const E* __restrict__ v_new,
                                                        const int64_t* __restrict__ slots,
-                                                       int64_t num_slots, int64_t blk_stride,
-                                                       int block_size, int num_kv_heads,
+                                                       int num_tokens, int64_t num_slots,
+                                                       int64_t blk_stride, int block_size,
                                                        int head_dim) {
     constexpr int X = 16 / sizeof(E);
-    const int t = blockIdx.x;
-    const int64_t slot = slots[t];
-    if (slot < 0 || slot >= num_slots) return;
-    const int64_t b = slot / block_size;
-    const int o = static_cast<int>(slot - b * block_size);
-    const int chunks = head_dim / X;
-    const int64_t tile = static_cast<int64_t>(head_dim) * block_size;
-    const int64_t row = static_cast<int64_t>(t) * num_kv_heads * head_dim;
-
-    // K: (head, chunk) pairs, 16 bytes each.
-    for (int i = threadIdx.x; i < num_kv_heads * chunks; i += blockDim.x) {
-        const int h = i / chunks;
-        const int c = i - h * chunks;
-        const uint4 v = *reinterpret_cast<const uint4*>(k_new + row + h * head_dim + c * X);
-        E* dst = k_cache + b * blk_stride + h * tile + k_elem(o, c * X, block_size, head_dim, X);
-        *reinterpret_cast<uint4*>(dst) = v;
+    constexpr int Q = 16 / X;                  // runs of X positions per 16-position window
+    constexpr int SLAB = 256 / sizeof(E);      // most dims per workgroup
+    constexpr int LD = SLAB + X;               // LDS row, padded by 16 bytes
+    constexpr int ROWS = 32;
+    __shared__ int64_t sl[33];                 // tokens t0 - 1 .. t0 + 31: slot (-1: none),
+    __shared__ int64_t sb[33];                 // block,
+    __shared__ int so[33];                     // offset in the block
+    __shared__ int seg[16];                    // length of the segment starting at t0 + i, or 0
+    __shared__ __align__(16) E ks[ROWS * LD];
+    __shared__ __align__(16) E vs[ROWS * LD];
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * 16;
+    const int h = blockIdx.y;
+    const int num_kv_heads = gridDim.y;
+    const int se = head_dim < SLAB ? head_dim : SLAB;    // dims of this slab
+    const int dof = blockIdx.z * se;                      // its first dim
+    const int cs = se / X;                                // its 16-byte chunks per row
+    const int tt = tile_tokens(block_size);
+    for (int i = threadIdx.x; i < 33; i += blockDim.x) {
+        const int64_t t = t0 - 1 + i;
+        int64_t v = (t >= 0 && t < num_tokens) ? slots[t] : -1;
+        v = (v >= 0 && v < num_slots) ? v : -1;
+        const int64_t b = v >= 0 ? v / block_size : 0;
+        sl[i] = v;
+        sb[i] = b;
+        so[i] = static_cast<int>(v - b * block_size);
     }
-    // V: (head, dim) elements.
-    for (int i = threadIdx.x; i < num_kv_heads * head_dim; i += blockDim.x) {
-        const int h = i / head_dim;
-        const int d = i - h * head_dim;
-        v_cache[b * blk_stride + h * tile + v_elem(o, d, block_size, head_dim)] = v_new[row + i];
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        const int i = threadIdx.x;
+        const int64_t s = sl[i + 1];
+        const int p = so[i + 1] % tt;          // position inside the tile
+        int k = 0;
+        if (s >= 0 && !(p % 16 != 0 && sl[i] == s - 1)) {   // else: none, or a continuation
+            k = 1;                             // up to the next window start: i + k <= 31
+            while (p + k < tt && (p + k) % 16 != 0 && sl[i + 1 + k] == s + k) ++k;
+        }
+        seg[i] = k;
+    }
+    __syncthreads();
+    int jmin = 16, jmax = 0;                   // rows t0 + jmin .. t0 + jmax - 1 are needed
+    for (int i = 0; i < 16; ++i) {
+        if (seg[i] == 0) continue;
+        jmin = i < jmin ? i : jmin;
+        jmax = i + seg[i] > jmax ? i + seg[i] : jmax;
+    }
+    if (jmin >= jmax) return;                  // uniform: nothing starts here
+    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+    const int64_t col0 = static_cast<int64_t>(h) * head_dim + dof;
+    const int units = (jmax - jmin) * cs;      // <= 31 * 16 < 2 * 256
+    uint4 kr[2], vr[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = threadIdx.x + it * 256;
+        if (u < units) {
+            const int r = u / cs, c = u - (u / cs) * cs;
+            const int64_t src = (t0 + jmin + r) * row_stride + col0 + c * X;
+            kr[it] = *reinterpret_cast<const uint4*>(k_new + src);
+            vr[it] = *reinterpret_cast<const uint4*>(v_new + src);
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int u = threadIdx.x + it * 256;
+        if (u < units) {
+            const int r = u / cs, c = u - (u / cs) * cs;
+            *reinterpret_cast<uint4*>(ks + r * LD + c * X) = kr[it];
+            *reinterpret_cast<uint4*>(vs + r * LD + c * X) = vr[it];
+        }
+    }
+    __syncthreads();
+    const int64_t head_region = static_cast<int64_t>(head_dim) * block_size;
+    const bool vec_ok = tt % X == 0;           // a dim row keeps 16-byte alignment
+    for (int j = jmin; j < 16; ++j) {
+        const int k = seg[j];
+        if (k == 0) continue;
+        const int o = so[j + 1];
+        const int p = o % tt;
+        const int i0 = p % 16;                 // the segment holds window positions [i0, i0 + k)
+        const int w0 = p - i0;                 // the window's first position in the tile
+        const int64_t base = sb[j + 1] * blk_stride + h * head_region +
+                             static_cast<int64_t>(o - p) * head_dim;   // the tile
+        const int r0 = j - jmin - i0;          // LDS row of window position 0
+        for (int idx = threadIdx.x; idx < 16 * cs; idx += blockDim.x) {
+            const int i = idx & 15;
+            const int c = idx >> 4;
+            if (i < i0 || i >= i0 + k) continue;
+            *reinterpret_cast<uint4*>(k_cache + base +
+                                      (static_cast<int64_t>(dof / X + c) * tt + w0 + i) * X) =
+                *reinterpret_cast<const uint4*>(ks + (r0 + i) * LD + c * X);
+        }
+        for (int idx = threadIdx.x; idx < Q * se; idx += blockDim.x) {
+            const int q = idx % Q;
+            const int dd = idx / Q;
+            const int first = q * X;           // window positions first .. first + X - 1
+            if (first + X <= i0 || first >= i0 + k) continue;
+            E* dst = v_cache + base + static_cast<int64_t>(dof + dd) * tt + w0 + first;
+            if (vec_ok && first >= i0 && first + X <= i0 + k) {
+                E e[X];
+#pragma unroll
+                for (int x = 0; x < X; ++x) e[x] = vs[(r0 + first + x) * LD + dd];
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(e);
+            } else {
+                for (int x = 0; x < X; ++x) {
+                    const int i = first + x;
+                    if (i >= i0 && i < i0 + k) dst[x] = vs[(r0 + i) * LD + dd];
+                }
+            }
+        }
     }
 }
 
@@ -189,17 +283,20 @@ int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, cons
                     hipStream_t stream) {
     if (num_tokens == 0) return PA_OK;
     const int64_t num_slots = c->num_blocks * c->block_size;
+    const int slab = 256 / elem_bytes(c->dtype);
+    const dim3 grid((num_tokens + 15) / 16, c->num_kv_heads,
+                    c->head_dim > slab ? c->head_dim / slab : 1);
     if (c->dtype == PA_BF16) {
-        hipLaunchKernelGGL(write_kv_kernel<uint16_t>, dim3(num_tokens), dim3(256), 0, stream,
+        hipLaunchKernelGGL(write_kv_kernel<uint16_t>, grid, dim3(256), 0, stream,
                            static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
                            static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                           slots, num_slots, block_stride(c), c->block_size, c->num_kv_heads,
+                           slots, num_tokens, num_slots, block_stride(c), c->block_size,
                            c->head_dim);
     } else {
-        hipLaunchKernelGGL(write_kv_kernel<uint32_t>, dim3(num_tokens), dim3(256), 0, stream,
+        hipLaunchKernelGGL(write_kv_kernel<uint32_t>, grid, dim3(256), 0, stream,
                            static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache),
                            static_cast<const uint32_t*>(k_new), static_cast<const uint32_t*>(v_new),
-                           slots, num_slots, block_stride(c), c->block_size, c->num_kv_heads,
+                           slots, num_tokens, num_slots, block_stride(c), c->block_size,
                            c->head_dim);
     }
     return check_launch("write_kv");
