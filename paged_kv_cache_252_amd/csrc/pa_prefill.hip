@@ -3,7 +3,10 @@
 // checked at once.  Built from the MFMA tile of the decode kernels
 // (pa_tile.h); the split-K merge is decode's (launch_merge).
 
+#include <float.h>
+
 #include "pa_tile.h"
+
 
 namespace pa {
 namespace {
@@ -28,7 +31,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int64_t num_blocks, int64_t blk_stride, int total_q, int num_q_heads, int group,
     int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
-    float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
+    float scale_log2, unsigned q_sign, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
     // W waves of a workgroup take W consecutive query tiles of one request and
     // KV head: they read the same blocks at about the same time, so most of
@@ -90,10 +93,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
             q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            bf16x8 v = qp[4 * s4 + quad];
-            qv[u][s4] = row_ok[u] ? v : bf16x8{};
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = __builtin_bit_cast(u32x4, qp[4 * s4 + quad]) ^ q_sign;   // sign of the scale
+            qv[u][s4] = row_ok[u] ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
         }
-        st[u].m = -INFINITY;
+        st[u].m = kNoMaxLog2;
         st[u].l = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -123,9 +127,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
             consume_tile_groups<RG>(st, t, qv, scale_log2, lane, rv, v_valid, masked);
         };
         // two tiles in flight; past the end the prefetch repeats the last tile.
-        // (No scheduling barriers here, unlike decode: this loop is bound by
-        // issue, not memory, and the compiler's interleaving of one tile's
-        // loads and score MFMAs with the other's softmax measured 6% faster.)
+        // (No scheduling barriers here, unlike decode: the compiler's
+        // interleaving of one tile's loads and score MFMAs with the other's
+        // softmax measured 6% faster.  A third tile in flight, or issuing the
+        // next tile's score MFMAs ahead of this tile's softmax, measured no
+        // faster.)
         Tile ta, tb;
         load_blk(ta, 0);
         for (int b = 0; b < nblk; b += 2) {
@@ -180,6 +186,11 @@ template <int RG>
 int launch_prefill_rg(const PrefillArgs& p) {
     const DecodeArgs& a = p.d;
     constexpr int W = PA_PREFILL_WAVES;
+    // the tile consumer takes a positive scale: a negative one flips the sign
+    // of q instead (exact in bf16), zero becomes the least normal float
+    // (every score then rounds to 0 in the exponent, as with scale 0)
+    const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
+    const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
@@ -188,7 +199,7 @@ int launch_prefill_rg(const PrefillArgs& p) {
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts,
-                       a.scale * kLog2e, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       sl2, q_sign, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        p.ws_len);
     return check_launch("prefill");
 }

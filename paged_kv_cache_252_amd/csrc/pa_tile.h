@@ -141,9 +141,12 @@ __device__ __forceinline__ f32x4 fma4(f32x4 a, float w, f32x4 c) {
                  __builtin_fmaf(a[2], w, c[2]), __builtin_fmaf(a[3], w, c[3])};
 }
 
+// Two floats to bf16 (round to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-    return static_cast<unsigned>(float_to_bf16_bits(lo)) |
-           (static_cast<unsigned>(float_to_bf16_bits(hi)) << 16);
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // One block of 16 tokens for rows with their own visibility.  row_valid:
@@ -196,28 +199,52 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    const unsigned p01 = pack_bf16x2(p[0], p[1]);
-    const unsigned p23 = pack_bf16x2(p[2], p[3]);
-    s16x4 pb;
-    pb[0] = static_cast<short>(p01 & 0xffff);
-    pb[1] = static_cast<short>(p01 >> 16);
-    pb[2] = static_cast<short>(p23 & 0xffff);
-    pb[3] = static_cast<short>(p23 >> 16);
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    const s16x4 pb = __builtin_bit_cast(s16x4, pp);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
+// Maximum of floats on the VALU without the quieting of signalling NaNs that
+// fmaxf needs in IEEE mode (inputs here are MFMA sums or -inf, never NaN).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float vmax_across_rows(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float y = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const unsigned w = __float_as_uint(y);
+    auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Reference maximum of a row that has seen no score yet: finite, so that
+// exp2(score * scale - m) needs no special case (a masked score is -inf and
+// gives 0; any visible score raises the maximum past it).
+constexpr float kNoMaxLog2 = -1e30f;
+
 // consume_tile_rows for RG groups of 16 rows that read the same tile (same
 // arithmetic per row): every group's score MFMAs are issued first, the V
 // masking is done once, and one branch covers the rescale of all groups, so
-// the matrix work of one group overlaps the softmax of another.
+// the matrix work of one group overlaps the softmax of another (a score
+// step, tile_scores, and the rest, tile_softmax_pv).  The scale is folded
+// into the exponent: `scale_log2` must be positive (a
+// negative scale is applied by negating q, a zero one replaced by the least
+// normal float), the row maximum is taken over raw scores and scaled once,
+// and p = exp2(fma(s, scale_log2, -m)); rows start at m = kNoMaxLog2.
 template <int RG>
-__device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile& t,
-                                                    const bf16x8 (&qv)[RG][4], float scale_log2,
-                                                    int lane, const int (&row_valid)[RG],
-                                                    int v_valid, bool masked) {
-    f32x4 s[RG];
+__device__ __forceinline__ void tile_scores(f32x4 (&s)[RG], const Tile& t,
+                                            const bf16x8 (&qv)[RG][4]) {
 #pragma unroll
     for (int u = 0; u < RG; ++u) s[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -225,6 +252,13 @@ __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile
 #pragma unroll
         for (int u = 0; u < RG; ++u)
             s[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[u][k], s[u], 0, 0, 0);
+}
+
+template <int RG>
+__device__ __forceinline__ void tile_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&s)[RG], Tile& t,
+                                                float scale_log2, int lane,
+                                                const int (&row_valid)[RG], int v_valid,
+                                                bool masked) {
     const int tok_base = 4 * (lane >> 4);
     if (v_valid < FBS) {   // (wave-uniform) values past the history may be stale bytes
 #pragma unroll
@@ -233,19 +267,17 @@ __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile
             for (int i = 0; i < 4; ++i)
                 if (tok_base + i >= v_valid) t.v[j][i] = 0;
     }
-    float sc[RG][4], mx[RG];
+    float mx[RG];
     bool raise[RG];
     bool any = false;
 #pragma unroll
     for (int u = 0; u < RG; ++u) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[u][i] = s[u][i] * scale_log2;
         if (masked) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (tok_base + i >= row_valid[u]) sc[u][i] = -INFINITY;
+                if (tok_base + i >= row_valid[u]) s[u][i] = -INFINITY;
         }
-        mx[u] = max_across_rows(fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
+        mx[u] = vmax_across_rows(vmax3(s[u][0], s[u][1], vmax(s[u][2], s[u][3]))) * scale_log2;
         raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
         any = any || raise[u];
     }
@@ -261,22 +293,28 @@ __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile
     }
 #pragma unroll
     for (int u = 0; u < RG; ++u) {
-        const bool dead = st[u].m == -INFINITY;
+        const float nm = -st[u].m;
         float p[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[u][i] - st[u].m);
+        for (int i = 0; i < 4; ++i) p[i] = fast_exp2(__builtin_fmaf(s[u][i], scale_log2, nm));
         st[u].l += (p[0] + p[1]) + (p[2] + p[3]);
-        const unsigned p01 = pack_bf16x2(p[0], p[1]);
-        const unsigned p23 = pack_bf16x2(p[2], p[3]);
-        s16x4 pb;
-        pb[0] = static_cast<short>(p01 & 0xffff);
-        pb[1] = static_cast<short>(p01 >> 16);
-        pb[2] = static_cast<short>(p23 & 0xffff);
-        pb[3] = static_cast<short>(p23 >> 16);
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        const s16x4 pb = __builtin_bit_cast(s16x4, pp);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             st[u].acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st[u].acc[j], 0, 0, 0);
     }
+}
+
+template <int RG>
+__device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile& t,
+                                                    const bf16x8 (&qv)[RG][4], float scale_log2,
+                                                    int lane, const int (&row_valid)[RG],
+                                                    int v_valid, bool masked) {
+    f32x4 s[RG];
+    tile_scores<RG>(s, t, qv);
+    tile_softmax_pv<RG>(st, s, t, scale_log2, lane, row_valid, v_valid, masked);
 }
 
 // One block of 16 tokens seen alike by every row: `valid` of its tokens are

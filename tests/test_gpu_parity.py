@@ -720,6 +720,23 @@ def test_prefill_matches_oracle(group, part):
     assert_close(w, out, _oracle_prefill(w), f"prefill g={group}")
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.9])
+def test_prefill_scale_sign(scale):
+    """A negative, zero or large softmax scale (the kernel folds the scale into
+    the exponent and takes the row maximum over unscaled scores, flipping q for
+    a negative scale) against the oracle."""
+    say(f"prefill scale={scale}")
+    lens = [5, 16, 40, 100, 33]
+    w = inputs.paged_random("pfs", len(lens), 0, 100, 8, 2, num_blocks=64, seed=66,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_query_chunks(w, [5, 16, 9, 40, 33])
+    w.scale = scale
+    for part in (0, 16):
+        out = _run_prefill(w, partition_tokens=part)
+        assert_close(w, out, _oracle_prefill(w), f"prefill scale={scale} part={part}")
+
+
 def test_prefill_one_token_equals_decode():
     """A one-token chunk per request is a decode: pa_prefill and pa_decode agree
     with each other (to rounding: prefill raises its running maximum lazily)
