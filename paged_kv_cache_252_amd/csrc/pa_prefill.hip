@@ -7,7 +7,6 @@
 
 #include "pa_tile.h"
 
-
 namespace pa {
 namespace {
 
@@ -23,7 +22,8 @@ namespace {
 // h * g + r % g.  All rows read the same physical blocks, so each tile is
 // loaded once and consumed by every group, masked row by row (RG groups per
 // load cut the tile reads from L2 RG times); the partitions and their merge
-// are those of decode, per query row.
+// are those of decode, per query row.  This kernel keeps the tiles in
+// registers (short chunks); prefill_lds_kernel below stages them in LDS.
 template <bool NT, int RG, int W>
 __global__ __launch_bounds__(64 * W) void prefill_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
@@ -176,25 +176,221 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same work with the tiles staged in LDS: a workgroup of four waves takes
+// 4 * RG * 16/g consecutive query tokens of one request and KV head; each tile
+// is copied from memory to LDS once per workgroup by the waves together (1 KiB
+// of K and 1 KiB of V each, global_load_lds: no registers on the way), S - 1
+// tiles ahead of the one being consumed, and every wave reads its MFMA
+// operands from LDS.  One barrier per tile: after it, the tile is in LDS and
+// every wave is done with the previous one, whose stage is then refilled.
+
+// 16 bytes per lane from gptr to LDS at lds_base + lane * 16 (lds_base
+// wave-uniform; that lane layout was checked on the device).  In asm so that
+// the compiler does not wait for every LDS copy before each LDS read; the
+// loop waits itself, by count.  M0 is set here and used by nothing else in
+// these kernels.
+__device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_base) : "memory");
+}
+
+// LDS stages: S - 1 tiles in flight while one is consumed (measured on the
+// chunked-prefill workload: 3, 4 and 6 stages 216-217 us, 8 stages 236 us,
+// the LDS then limiting the workgroups per CU)
+constexpr int kPrefillStages = 4;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops outstanding
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int RG, int S>
+__global__ __launch_bounds__(256) void prefill_lds_kernel(
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int64_t num_blocks, int64_t blk_stride, int total_q, int num_q_heads, int group,
+    int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
+    float scale_log2, unsigned q_sign, __bf16* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
+    constexpr int W = 4;
+    __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
+    const int h = blockIdx.x;
+    const int seq = blockIdx.y / tiles_per_seq;
+    const int wgt = blockIdx.y - seq * tiles_per_seq;
+    const int part = blockIdx.z;
+    const int wave = static_cast<int>(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row = lane & 15;
+    const int quad = lane >> 4;
+    auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+    const int qs = clampi(q_start[seq], 0, total_q);
+    const int n = clampi(q_start[seq + 1], qs, total_q) - qs;
+    const int tpg = FG / group;
+    const int j0w = wgt * W * RG * tpg;          // the workgroup's first query token
+    if (j0w >= n) return;                        // (whole workgroup)
+    const int j0 = j0w + wave * RG * tpg;        // this wave's
+    const bool active = j0 < n;
+    const int L = clampi(context_lens[seq], 0, len_clamp);
+    const int hq = h * group + row % group;
+    int qi[RG], lim[RG];
+    bool row_ok[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+        const int j = j0 + u * tpg + row / group;
+        row_ok[u] = j < n;
+        qi[u] = qs + (row_ok[u] ? j : j0w);
+        lim[u] = row_ok[u] ? clampi(L - n + j + 1, 0, L) : 0;
+    }
+    const int lim_min = clampi(L - n + j0 + 1, 0, L);
+    const int lim_max = active ? clampi(L - n + min(j0 + RG * tpg, n), 0, L) : 0;
+    const int wg_lim_max = clampi(L - n + min(j0w + W * RG * tpg, n), 0, L);
+
+#pragma unroll
+    for (int u = 0; u < RG; ++u)
+        if (max_parts > 1 && part == 0 && h == 0 && row_ok[u] && row % group == 0 && quad == 0)
+            ws_len[qi[u]] = lim[u];
+    auto out_row = [&](int u) {
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
+    };
+    auto zero_rows = [&]() {
+#pragma unroll
+        for (int u = 0; u < RG; ++u)
+            if (part == 0 && row_ok[u] && lim[u] == 0) {
+                uint2* o = out_row(u);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+            }
+    };
+    const int tok0 = part * part_tokens;
+    if (tok0 >= wg_lim_max) {                    // (whole workgroup)
+        zero_rows();
+        return;
+    }
+    const int tok1 = min(wg_lim_max, tok0 + part_tokens);
+
+    bf16x8 qv[RG][4];
+    SoftmaxState st[RG];
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 v = __builtin_bit_cast(u32x4, qp[4 * s4 + quad]) ^ q_sign;
+            qv[u][s4] = row_ok[u] ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
+        }
+        st[u].m = kNoMaxLog2;
+        st[u].l = 0.f;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const int blk0 = tok0 / FBS;
+    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;
+    const int32_t* tab = block_tables + static_cast<int64_t>(seq) * max_blocks_per_seq + blk0;
+    // the partition's table entries, kTbl at a time, in LDS: the copies need
+    // them without a scalar-load wait in the loop
+    constexpr int kTbl = 256;
+    __shared__ int tbl[kTbl];
+    auto load_tbl = [&](int t0) {   // entries t0 .. t0 + kTbl - 1 (those < nblk)
+        for (int i = threadIdx.x; i < kTbl && t0 + i < nblk; i += 256)
+            tbl[i] = clamp_block(tab[t0 + i], num_blocks);
+        __syncthreads();
+    };
+    load_tbl(0);
+    const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) __bf16*)(&ring[0][0])));
+    // tile t (past the end: the last one again, so every thread issues the same
+    // number of copies per tile) into stage t % S; wave w copies bytes
+    // [w KiB, (w+1) KiB) of the K tile and of the V tile
+    auto issue = [&](int t) {
+        const int tc = t < nblk ? t : nblk - 1;
+        const int64_t o = static_cast<int64_t>(tbl[tc % kTbl]) * blk_stride +
+                          static_cast<int64_t>(h) * FTILE + wave * 512 + lane * 8;
+        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2 + wave * 1024);
+        lds_copy16(k_cache + o, __builtin_amdgcn_readfirstlane(sb));
+        lds_copy16(v_cache + o, __builtin_amdgcn_readfirstlane(sb + FTILE * 2));
+    };
+#pragma unroll
+    for (int t = 0; t < S - 1; ++t) issue(t);
+    for (int b = 0; b < nblk; ++b) {
+        wait_vmcnt<2 * (S - 2)>();               // this thread's copies of tile b have landed
+        __builtin_amdgcn_s_barrier();            // everyone's; and tile b - 1 is consumed
+        const int t_next = b + S - 1;            // refilling tile b - 1's stage
+        if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare)
+        issue(t_next);
+        const int start = tok0 + FBS * b;
+        if (start < lim_max) {                   // (wave-uniform) something of it is visible here
+            const __bf16* stage = &ring[b % S][0];
+            Tile t;
+            const bf16x8* kp = reinterpret_cast<const bf16x8*>(stage) + lane;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
+            const s16x4* vp = reinterpret_cast<const s16x4*>(stage + FTILE) + row * 4 + quad;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t.v[j] = vp[64 * j];
+            const int v_valid = clampi(lim_max - start, 0, FBS);
+            const bool masked = start + FBS > lim_min;
+            int rv[RG];
+#pragma unroll
+            for (int u = 0; u < RG; ++u) rv[u] = clampi(lim[u] - start, 0, FBS);
+            consume_tile_groups<RG>(st, t, qv, scale_log2, lane, rv, v_valid, masked);
+        }
+    }
+    wait_vmcnt<0>();                             // no copy may land after the workgroup ends
+    if (!active) return;
+
+#pragma unroll
+    for (int u = 0; u < RG; ++u) {
+        const float lsum = sum_across_rows(st[u].l);
+        if (!row_ok[u]) continue;
+        if (tok0 >= lim[u]) {
+            if (part == 0 && lim[u] == 0) {
+                uint2* o = out_row(u);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+            }
+            continue;
+        }
+        const int my_nparts = (lim[u] + part_tokens - 1) / part_tokens;
+        if (my_nparts == 1) {
+            const float inv = 1.f / lsum;
+            uint2* o = out_row(u);
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+                o[4 * jj + quad] = make_uint2(pack_bf16x2(st[u].acc[jj][0] * inv, st[u].acc[jj][1] * inv),
+                                              pack_bf16x2(st[u].acc[jj][2] * inv, st[u].acc[jj][3] * inv));
+            continue;
+        }
+        const int64_t pidx = (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * max_parts + part;
+        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st[u].acc[jj];
+        if (quad == 0) {
+            ws_m[pidx] = st[u].m;
+            ws_l[pidx] = lsum;
+        }
+    }
+}
+
 }  // namespace
 
-#ifndef PA_PREFILL_WAVES
-#define PA_PREFILL_WAVES 2
-#endif
 
-template <int RG>
-int launch_prefill_rg(const PrefillArgs& p) {
+namespace {
+
+// Short chunks (fewer than 2 * 16/g query tokens): one row group per wave,
+// tiles in registers, two waves per workgroup.
+int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
-    constexpr int W = PA_PREFILL_WAVES;
-    // the tile consumer takes a positive scale: a negative one flips the sign
-    // of q instead (exact in bf16), zero becomes the least normal float
-    // (every score then rounds to 0 in the exponent, as with scale 0)
-    const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
-    const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-    const int per = W * RG * (FG / a.group);
+    constexpr int W = 2;
+    const int per = W * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_kernel<false, RG, W>), grid, dim3(64 * W), 0, a.stream,
+    hipLaunchKernelGGL((prefill_kernel<false, 1, W>), grid, dim3(64 * W), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
@@ -204,13 +400,40 @@ int launch_prefill_rg(const PrefillArgs& p) {
     return check_launch("prefill");
 }
 
+// Longer chunks: two row groups per wave, four waves per workgroup sharing
+// each tile through LDS.
+int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
+    const DecodeArgs& a = p.d;
+    constexpr int RG = 2;
+    const int per = 4 * RG * (FG / a.group);
+    const int tiles = (p.max_q_len + per - 1) / per;
+    dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
+    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages>), grid, dim3(256), 0, a.stream,
+                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
+                       static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
+                       a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
+                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts,
+                       sl2, q_sign, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       p.ws_len);
+    return check_launch("prefill");
+}
+
+}  // namespace
+
 int launch_prefill(const PrefillArgs& p) {
     const DecodeArgs& a = p.d;
     if (a.num_seqs == 0 || p.max_q_len == 0) return PA_OK;
+    // the tile consumer takes a positive scale: a negative one flips the sign
+    // of q instead (exact in bf16), zero becomes the least normal float
+    // (every score then rounds to 0 in the exponent, as with scale 0)
+    const float sl2 = fmaxf(fabsf(a.scale) * kLog2e, FLT_MIN);
+    const unsigned q_sign = a.scale < 0.f ? 0x80008000u : 0u;
     // two row groups per wave once a chunk fills them: half the tile reads
-    // (measured on the chunked-prefill workload: 1 group 431 us, 2 groups
-    // 273 us, 4 groups 368 us -- 332 VGPRs leave one wave per SIMD)
-    const int st = p.max_q_len >= 2 * (FG / a.group) ? launch_prefill_rg<2>(p) : launch_prefill_rg<1>(p);
+    // (measured on the chunked-prefill workload with tiles in registers: 1
+    // group 431 us, 2 groups 273 us, 4 groups 368 us -- 332 VGPRs leave one
+    // wave per SIMD; staging the tiles in LDS then took it to 217 us)
+    const int st = p.max_q_len >= 2 * (FG / a.group) ? launch_prefill_lds(p, sl2, q_sign)
+                                                     : launch_prefill_short(p, sl2, q_sign);
     if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
     return launch_merge(p.ws_len, p.total_q, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
                         a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
