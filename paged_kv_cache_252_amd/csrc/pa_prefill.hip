@@ -177,12 +177,11 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// The same work with the tiles staged in LDS: a workgroup of four waves takes
-// 4 * RG * 16/g consecutive query tokens of one request and KV head; each tile
-// is copied from memory to LDS once per workgroup by the waves together (1 KiB
-// of K and 1 KiB of V each, global_load_lds: no registers on the way), S - 1
-// tiles ahead of the one being consumed, and every wave reads its MFMA
-// operands from LDS.  One barrier per tile: after it, the tile is in LDS and
+// The same work with the tiles staged in LDS: a workgroup of W waves takes
+// W * RG * 16/g consecutive query tokens of one request and KV head; each tile
+// is copied from memory to LDS once per workgroup by the waves together (8 / W
+// KiB each, global_load_lds: no registers on the way), S - 1 tiles ahead of
+// the one being consumed, and every wave reads its MFMA operands from LDS.  One barrier per tile: after it, the tile is in LDS and
 // every wave is done with the previous one, whose stage is then refilled.
 
 // 16 bytes per lane from gptr to LDS at lds_base + lane * 16 (lds_base
@@ -195,10 +194,12 @@ __device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds_base) 
                  :: "v"(gptr), "s"(lds_base) : "memory");
 }
 
-// LDS stages: S - 1 tiles in flight while one is consumed (measured on the
-// chunked-prefill workload: 3, 4 and 6 stages 216-217 us, 8 stages 236 us,
-// the LDS then limiting the workgroups per CU)
+// LDS stages: S - 1 tiles in flight while one is consumed; waves per
+// workgroup sharing them.  Measured on the chunked-prefill workload: 4 waves
+// with 3, 4 or 6 stages 216-217 us, 8 stages 236 us (the LDS then limits the
+// workgroups per CU); 2 waves 228-242 us, 8 waves 291 us.
 constexpr int kPrefillStages = 4;
+constexpr int kPrefillLdsWaves = 4;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops outstanding
@@ -206,8 +207,8 @@ __device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops 
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int RG, int S>
-__global__ __launch_bounds__(256) void prefill_lds_kernel(
+template <int RG, int S, int W>
+__global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -215,7 +216,8 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(
     int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
     float scale_log2, unsigned q_sign, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
-    constexpr int W = 4;
+    static_assert(W == 2 || W == 4 || W == 8, "a tile is 8 KiB: 8 / W copies of 1 KiB per wave");
+    constexpr int kCopies = 8 / W;
     __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
     const int h = blockIdx.x;
     const int seq = blockIdx.y / tiles_per_seq;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(
     constexpr int kTbl = 256;
     __shared__ int tbl[kTbl];
     auto load_tbl = [&](int t0) {   // entries t0 .. t0 + kTbl - 1 (those < nblk)
-        for (int i = threadIdx.x; i < kTbl && t0 + i < nblk; i += 256)
+        for (int i = threadIdx.x; i < kTbl && t0 + i < nblk; i += 64 * W)
             tbl[i] = clamp_block(tab[t0 + i], num_blocks);
         __syncthreads();
     };
@@ -305,20 +307,24 @@ __global__ __launch_bounds__(256) void prefill_lds_kernel(
     const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) __bf16*)(&ring[0][0])));
     // tile t (past the end: the last one again, so every thread issues the same
-    // number of copies per tile) into stage t % S; wave w copies bytes
-    // [w KiB, (w+1) KiB) of the K tile and of the V tile
+    // number of copies per tile) into stage t % S; the stage's 8 KiB are K
+    // then V, and wave w copies KiB w * kCopies .. (w + 1) * kCopies - 1
     auto issue = [&](int t) {
         const int tc = t < nblk ? t : nblk - 1;
         const int64_t o = static_cast<int64_t>(tbl[tc % kTbl]) * blk_stride +
-                          static_cast<int64_t>(h) * FTILE + wave * 512 + lane * 8;
-        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2 + wave * 1024);
-        lds_copy16(k_cache + o, __builtin_amdgcn_readfirstlane(sb));
-        lds_copy16(v_cache + o, __builtin_amdgcn_readfirstlane(sb + FTILE * 2));
+                          static_cast<int64_t>(h) * FTILE + lane * 8;
+        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+            const int kib = wave * kCopies + c;            // 0..3 K, 4..7 V
+            const __bf16* src = (kib < 4 ? k_cache : v_cache) + o + (kib & 3) * 512;
+            lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
+        }
     };
 #pragma unroll
     for (int t = 0; t < S - 1; ++t) issue(t);
     for (int b = 0; b < nblk; ++b) {
-        wait_vmcnt<2 * (S - 2)>();               // this thread's copies of tile b have landed
+        wait_vmcnt<kCopies * (S - 2)>();         // this thread's copies of tile b have landed
         __builtin_amdgcn_s_barrier();            // everyone's; and tile b - 1 is consumed
         const int t_next = b + S - 1;            // refilling tile b - 1's stage
         if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare)
@@ -400,15 +406,16 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
     return check_launch("prefill");
 }
 
-// Longer chunks: two row groups per wave, four waves per workgroup sharing
-// each tile through LDS.
+// Longer chunks: two row groups per wave, kPrefillLdsWaves waves per
+// workgroup sharing each tile through LDS.
 int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
     constexpr int RG = 2;
-    const int per = 4 * RG * (FG / a.group);
+    constexpr int W = kPrefillLdsWaves;
+    const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages>), grid, dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages, W>), grid, dim3(64 * W), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
