@@ -798,6 +798,21 @@ def test_prefill_full_size_sampled():
                 assert np.max(np.abs(got - ref)) <= BF16_TOL, (i, j)
 
 
+def test_prefill_long_history_one_partition():
+    """A history of more than 16,384 positions walked in one partition (the
+    kernel holds the partition's table entries in LDS 1,024 at a time and
+    refills them on the way) against the oracle, with and without the split."""
+    say("prefill long history")
+    lens = [20011, 300]
+    w = inputs.paged_random("pfl", len(lens), 0, max(lens), 8, 2, num_blocks=1400, seed=67,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_query_chunks(w, [40, 17])
+    want = _oracle_prefill(w)
+    for part in (1 << 15, 4096):
+        assert_close(w, _run_prefill(w, partition_tokens=part), want, f"prefill long part={part}")
+
+
 def test_prefill_validate_rejects_bad_offsets(monkeypatch):
     say("prefill PA_VALIDATE")
     monkeypatch.setenv("PA_VALIDATE", "1")
