@@ -859,6 +859,77 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
     for (int i = 0; i < 4; ++i) store_f32(o + i, tot[i] * inv);
 }
 
+// The same merge for at most kMaxWgParts partitions, bf16 output, head_dim
+// 128: 32 lanes per (request, query head), eight of them per workgroup, and
+// each lane loads all of its row's partitions at once (one memory round trip).
+// The arithmetic is the formula above for that case -- global max first, then
+// fused multiply-adds in partition order -- so the bits are the same as from
+// reduce_kernel or the in-workgroup merge of the decode kernel.
+constexpr int kSmallMergeRows = kMergeThreads / (FD / 4);   // rows per workgroup
+
+__global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
+    const int32_t* __restrict__ context_lens, int64_t rows, int num_q_heads, int len_clamp,
+    int part_tokens, int max_parts, const float* __restrict__ ws_acc,
+    const float* __restrict__ ws_m, const float* __restrict__ ws_l, uint16_t* __restrict__ out) {
+    constexpr int C = FD / 4;                  // float4 chunks per row
+    const int c = threadIdx.x % C;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kSmallMergeRows + threadIdx.x / C;
+    if (row >= rows) return;
+    const int64_t seq = row / num_q_heads;
+    int L = context_lens[seq];
+    L = L < 0 ? 0 : (L > len_clamp ? len_clamp : L);
+    int nparts = (L + part_tokens - 1) / part_tokens;
+    if (nparts <= 1) return;   // written directly by the partition kernel
+    nparts = nparts < kMaxWgParts ? nparts : kMaxWgParts;
+    const int64_t base = row * max_parts;
+    float m[kMaxWgParts], l[kMaxWgParts];
+    f32x4 acc[kMaxWgParts];
+#pragma unroll
+    for (int p = 0; p < kMaxWgParts; ++p) {
+        if (p < nparts) {
+            m[p] = ws_m[base + p];
+            l[p] = ws_l[base + p];
+            acc[p] = reinterpret_cast<const f32x4*>(ws_acc + (base + p) * FD)[c];
+        }
+    }
+    float M = m[0];
+#pragma unroll
+    for (int p = 1; p < kMaxWgParts; ++p)
+        if (p < nparts) M = fmaxf(M, m[p]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float dtot = 0.f;
+#pragma unroll
+    for (int p = 0; p < kMaxWgParts; ++p) {
+        if (p < nparts) {
+            const float w = fast_exp2(m[p] - M);
+            tot = fma4(acc[p], w, tot);
+            dtot = __builtin_fmaf(l[p], w, dtot);
+        }
+    }
+    const float inv = 1.f / dtot;
+    uint2* o = reinterpret_cast<uint2*>(out + row * FD) + c;
+    *o = make_uint2(pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv));
+}
+
+// The split-K merge of bf16, head_dim-128 partials of `rows` rows
+// (request-major, num_q_heads per request).
+int merge_bf16(const int32_t* lens, int64_t rows, int num_q_heads, int len_clamp, int part_tokens,
+               int max_parts, const float* ws_acc, const float* ws_m, const float* ws_l, void* out,
+               hipStream_t stream) {
+    if (rows == 0) return PA_OK;
+    if (max_parts <= kMaxWgParts) {
+        const int64_t wgs = (rows + kSmallMergeRows - 1) / kSmallMergeRows;
+        hipLaunchKernelGGL(reduce_small_kernel, dim3(static_cast<unsigned>(wgs)), dim3(kMergeThreads), 0,
+                           stream, lens, rows, num_q_heads, len_clamp, part_tokens, max_parts, ws_acc,
+                           ws_m, ws_l, static_cast<uint16_t*>(out));
+        return check_launch("decode merge");
+    }
+    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(num_q_heads, static_cast<unsigned>(rows / num_q_heads)),
+                       dim3(kMergeThreads), 0, stream, lens, num_q_heads, len_clamp, part_tokens,
+                       max_parts, ws_acc, ws_m, ws_l, static_cast<uint16_t*>(out));
+    return check_launch("decode merge");
+}
+
 template <typename T, int D>
 int launch_generic(const DecodeArgs& a) {
     dim3 grid(a.num_q_heads, a.num_seqs, a.max_parts);
@@ -917,10 +988,8 @@ int launch_fast(const DecodeArgs& a) {
                        a.num_kv_heads, a.cow_src);
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
-    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads),
-                       0, a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
-                       a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
-    return check_launch("decode reduce");
+    return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                      a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
 template <int MAXR, bool NT, bool APPEND>
@@ -938,10 +1007,8 @@ int launch_grouped(const DecodeArgs& a, int members) {
                        a.num_kv_heads, a.cow_src);
     int st = check_launch("decode (grouped)");
     if (st != PA_OK || a.max_parts <= 1) return st;
-    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads),
-                       0, a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
-                       a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
-    return check_launch("decode reduce");
+    return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                      a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
 template <int BS>
@@ -964,11 +1031,9 @@ int launch_grouped_r(const DecodeArgs& a) {
 int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t len_clamp,
                  int32_t part_tokens, int32_t max_parts, const float* ws_acc, const float* ws_m,
                  const float* ws_l, void* out, hipStream_t stream) {
-    if (rows == 0) return PA_OK;
-    hipLaunchKernelGGL((reduce_kernel<uint16_t, 128>), dim3(num_q_heads, rows), dim3(kMergeThreads), 0,
-                       stream, lens, num_q_heads, len_clamp, part_tokens, max_parts, ws_acc, ws_m, ws_l,
-                       static_cast<uint16_t*>(out));
-    return check_launch("merge");
+    // rows here are query rows, each with its own visible length in lens
+    return merge_bf16(lens, static_cast<int64_t>(rows) * num_q_heads, num_q_heads, len_clamp, part_tokens,
+                      max_parts, ws_acc, ws_m, ws_l, out, stream);
 }
 
 int launch_decode(const DecodeArgs& a_in) {
