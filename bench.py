@@ -43,7 +43,7 @@ WORKLOADS = {
     "gqa": dict(make=inputs.gqa, replicas=8,
                 desc="GQA decode: 32 requests, context U[512,4096], 32 q / 8 KV heads, "
                      "head_dim 128, block 16, bf16, blocks shuffled in a 65536-block pool"),
-    "prefix": dict(make=inputs.shared_prefix, replicas=4,
+    "prefix": dict(make=inputs.shared_prefix, replicas=4, runs=True,
                    desc="shared prefix: 256 requests, first 2048 tokens in the same 128 blocks, "
                         "private suffix U[64,512], 32 q / 8 KV heads, head_dim 128, block 16, bf16"),
     "long": dict(make=inputs.long_context, replicas=1,
@@ -367,6 +367,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-runs", action="store_true",
+                    help="shared prefix: no cooperative shared partitions (PA_DECODE_PREFIX_RUNS off)")
     ap.add_argument("--no-group", action="store_true",
                     help="decode shared-prefix batches one request per wave")
     ap.add_argument("--stream-kv", choices=("auto", "on", "off"), default="auto",
@@ -408,6 +410,9 @@ def main() -> int:
     # sharers are consecutive requests: decode them together (each shared
     # block is then read once per group) and stream K/V
     group_shared = w.shared_blocks is not None and not args.no_group
+    # one prefix shared by the whole batch: shared partitions decoded once per
+    # chunk of requests (PA_DECODE_PREFIX_RUNS)
+    prefix_runs = group_shared and cfg.get("runs", False) and not args.no_runs
     stream_kv = {"on": True, "off": False}.get(args.stream_kv,
                                                 w.shared_blocks is None or group_shared)
     log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
@@ -431,7 +436,8 @@ def main() -> int:
         # append of its new token at position L-1, and decode (pa_decode_step)
         ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src, tables[r],
                         w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
-                        partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared)
+                        partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared,
+                        prefix_runs=prefix_runs)
 
     for i in range(args.warmup):
         step(i % reps)
@@ -463,7 +469,7 @@ def main() -> int:
         r = i % reps
         ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
                    out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv,
-                   group_shared=group_shared)
+                   group_shared=group_shared, prefix_runs=prefix_runs)
     ev1.record(stream)
     ev1.synchronize()
     dec_us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
@@ -488,7 +494,7 @@ def main() -> int:
         "config": {"workload": cfg["desc"], "name": args.workload, "requests": w.num_seqs,
                    "max_context_len": max_len, "total_context_tokens": int(w.context_lens.sum()),
                    "replicas": reps, "partition_tokens": part, "stream_kv": stream_kv,
-                   "group_shared": group_shared,
+                   "group_shared": group_shared, "prefix_runs": prefix_runs,
                    "kv_layout": "one buffer [block][K|V], block_stride 2 blocks"},
         "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
         "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),

@@ -124,6 +124,16 @@ typedef struct {
                                       the ungrouped ones: every request still sees its
                                       tiles in logical order with the same partitions and
                                       the same arithmetic. */
+#define PA_DECODE_PREFIX_RUNS 4u   /* long runs of consecutive requests share their leading
+                                      blocks (one prefix, many requests).  A partition that
+                                      all 4 * 16/(Hq/Hkv) requests of a chunk share is decoded
+                                      for all of them at once by four waves that copy each
+                                      tile to LDS once; the other partitions are decoded one
+                                      request per wave in the same launch.  Output bits equal
+                                      one request per wave.  Used on the fast path with
+                                      16 % (Hq/Hkv) == 0 and at least two partitions, except
+                                      in pa_decode_step with copy-on-write sources; elsewhere
+                                      ignored (PA_DECODE_GROUP_SHARED then applies if set). */
 #define PA_DECODE_STREAM_KV 1u  /* read K/V with non-temporal loads, which keeps them from
                                    displacing other cache contents.  A cache hint only:
                                    results are identical.  Measured on MI355X: +6..13% when
@@ -269,7 +279,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *   partition_tokens  0 = automatic; otherwise a multiple of block_size in
  *                 [block_size, 1024] (the fast path also needs a multiple of 16)
  *   flags         0 or an OR of PA_DECODE_STREAM_KV (a cache hint; results are the
- *                 same) and PA_DECODE_GROUP_SHARED
+ *                 same), PA_DECODE_GROUP_SHARED and PA_DECODE_PREFIX_RUNS
  */
 int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
               const void* q, const int32_t* block_tables, const int32_t* context_lens,

@@ -683,6 +683,281 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
 }
 
 // ============================================================================
+// Runs of requests with a common prefix: cooperative shared partitions
+// ============================================================================
+//
+// For a batch in which long runs of consecutive requests share their leading
+// blocks ([ZQ] answer and TL;DR: one prefix, many requests).  A workgroup of
+// four waves is (KV head, chunk of M = 4 * 16/g consecutive requests,
+// partition, slot).  It first checks whether the partition is shared by the
+// whole chunk: every member's history extends past the partition's end and
+// names the same physical blocks there.
+//   * Shared: slot 0 decodes the partition for all M members at once.  Each
+//     tile is copied from memory to LDS once (2 KiB per wave, global_load_lds,
+//     S - 1 tiles ahead) and every wave consumes it for its 16 rows (16/g
+//     members x g heads).  The other slots exit.
+//   * Otherwise: wave w of slot s decodes member 4 s + w alone, as the fast
+//     path does (one wave per request, KV head and partition).
+// Both kinds of workgroup run in the same launch, so the shared partitions'
+// matrix work proceeds while the private suffixes stream from HBM.  The
+// arithmetic per row is the fast path's (same tiles in the same order, same
+// tile consumer), so the bits equal one request per wave; the partials go to
+// the usual merge.  A shared partition never holds a member's newest
+// position (the member's history extends past it), so the append, when
+// asked for, is always done by the per-member waves.
+constexpr int kCascadeStages = 4;
+
+template <bool NT, bool APPEND>
+__global__ __launch_bounds__(256) void decode_cascade_kernel(
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
+    int num_seqs, int num_q_heads, int group, int max_blocks_per_seq, int len_clamp,
+    int part_tokens, int max_parts, float scale_log2, __bf16* __restrict__ out,
+    float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
+    const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new, int num_kv_heads) {
+    constexpr int S = kCascadeStages;
+    constexpr int kCopies = 2;                       // KiB of each 8 KiB tile per wave
+    __shared__ __align__(16) __bf16 ring[S][2 * FTILE];
+    __shared__ int tbl[64];
+    __shared__ int not_shared;
+    const int h = blockIdx.x;
+    const int chunk = blockIdx.y;
+    const int per = FG / group;                      // members per wave in a shared partition
+    const int slot = blockIdx.z / max_parts;         // slot-major: slot 0 is dispatched first
+    const int part = blockIdx.z - slot * max_parts;
+    const int wave = static_cast<int>(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row = lane & 15;
+    const int quad = lane >> 4;
+    const int M = 4 * per;
+    const int seq0 = chunk * M;
+    const int nmem = min(M, num_seqs - seq0);
+    const int tok0 = part * part_tokens;
+    const int tok1 = tok0 + part_tokens;
+    const int blk0 = tok0 / FBS;
+    const int nblk = part_tokens / FBS;              // tiles of a whole partition, <= 64
+    auto clampL = [&](int L) { return L < 0 ? 0 : (L > len_clamp ? len_clamp : L); };
+
+    // Is the partition shared by the whole chunk?
+    if (threadIdx.x == 0) not_shared = nmem < 2 || blk0 + nblk > max_blocks_per_seq;
+    __syncthreads();
+    if (!not_shared) {
+        const int32_t* tab0 = block_tables + static_cast<int64_t>(seq0) * max_blocks_per_seq + blk0;
+        for (int i = threadIdx.x; i < nmem * nblk; i += 256) {
+            const int m = i / nblk;
+            const int j = i - m * nblk;
+            bool bad = tab0[static_cast<int64_t>(m) * max_blocks_per_seq + j] != tab0[j];
+            if (j == 0) bad = bad || clampL(context_lens[seq0 + m]) <= tok1;
+            if (bad) not_shared = 1;                 // (every writer writes 1)
+        }
+    }
+    __syncthreads();
+    const bool shared = not_shared == 0;
+
+    if (shared) {
+        if (slot != 0) return;                       // (whole workgroup)
+        const int mem = wave * per + row / group;
+        const bool row_ok = mem < nmem;
+        const int seq = seq0 + (row_ok ? mem : 0);
+        const int hq = h * group + row % group;
+        bf16x8 qv[4];
+        {
+            const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+                q + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                bf16x8 v = qp[4 * s4 + quad];
+                qv[s4] = row_ok ? v : bf16x8{};
+            }
+        }
+        SoftmaxState st;
+        st.m = -INFINITY;
+        st.l = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (threadIdx.x < nblk)
+            tbl[threadIdx.x] = clamp_block(
+                block_tables[static_cast<int64_t>(seq0) * max_blocks_per_seq + blk0 + threadIdx.x],
+                num_blocks);
+        __syncthreads();
+        const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(
+            (__attribute__((address_space(3))) __bf16*)(&ring[0][0])));
+        // tile t (past the end: the last one again, so every thread issues the
+        // same number of copies per tile) into stage t % S: K then V, wave w
+        // copying KiB 2w and 2w + 1
+        auto issue = [&](int t) {
+            const int tc = t < nblk ? t : nblk - 1;
+            const int64_t o = static_cast<int64_t>(tbl[tc]) * blk_stride +
+                              static_cast<int64_t>(h) * FTILE + lane * 8;
+            const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
+#pragma unroll
+            for (int c = 0; c < kCopies; ++c) {
+                const int kib = wave * kCopies + c;  // 0..3 K, 4..7 V
+                const __bf16* src = (kib < 4 ? k_cache : v_cache) + o + (kib & 3) * 512;
+                lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < S - 1; ++t) issue(t);
+        for (int b = 0; b < nblk; ++b) {
+            wait_vmcnt<kCopies * (S - 2)>();         // this thread's copies of tile b have landed
+            __builtin_amdgcn_s_barrier();            // everyone's; and tile b - 1 is consumed
+            issue(b + S - 1);                        // into tile b - 1's stage
+            const __bf16* stage = &ring[b % S][0];
+            Tile t;
+            const bf16x8* kp = reinterpret_cast<const bf16x8*>(stage) + lane;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
+            const s16x4* vp = reinterpret_cast<const s16x4*>(stage + FTILE) + row * 4 + quad;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t.v[j] = vp[64 * j];
+            consume_tile(st, t, qv, scale_log2, lane, FBS);
+        }
+        wait_vmcnt<0>();                             // no copy may land after the workgroup ends
+        const float lsum = sum_across_rows(st.l);
+        if (!row_ok) return;
+        // every member's history extends past this partition: a partial
+        const int64_t pidx = (static_cast<int64_t>(seq) * num_q_heads + hq) * max_parts + part;
+        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
+        if (quad == 0) {
+            ws_m[pidx] = st.m;
+            ws_l[pidx] = lsum;
+        }
+        return;
+    }
+
+    // One member per wave, as the fast path (block size 16).
+    const int m = slot * 4 + wave;
+    if (m >= nmem) return;
+    const int seq = seq0 + m;
+    const int L = clampL(context_lens[seq]);
+    const int hq = h * group + row;
+    const bool row_ok = row < group;
+    auto out_row = [&]() {
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+    };
+    if (tok0 >= L) {
+        if (L == 0 && part == 0 && row_ok) {         // empty history: zero output
+            uint2* o = out_row();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+        }
+        return;
+    }
+    const int mtok1 = min(L, tok1);
+    const int mblk = (mtok1 - tok0 + FBS - 1) / FBS;
+    const int last_valid = mtok1 - (tok0 + (mblk - 1) * FBS);
+    const int nparts = (L + part_tokens - 1) / part_tokens;
+    int my_phys = 0;
+    if (lane < mblk)
+        my_phys = clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
+                              num_blocks);
+    auto entry_off = [&](int e) {
+        return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, e < mblk ? e : mblk - 1)) * blk_stride;
+    };
+
+    // Appending (the wave of the last partition): the four lanes of row o
+    // hold the token's 16 key chunks, the 16 lanes of quad o/4 its 128 value
+    // dims; they store them to the cache and into the loaded tile.
+    const bool append_here = APPEND && part == nparts - 1;
+    const int o_new = (L - 1) % FBS;
+    bf16x8 fk[4];
+    short fv[8];
+    if constexpr (APPEND) {
+        if (append_here) {
+            const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * FD;
+            const bf16x8* kn = reinterpret_cast<const bf16x8*>(k_new + nrow);
+            const short* vn = reinterpret_cast<const short*>(v_new + nrow);
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) fk[s4] = kn[4 * s4 + quad];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) fv[j] = vn[16 * j + row];
+            const int64_t toff = entry_off(mblk - 1) + static_cast<int64_t>(h) * FTILE;
+            if (row == o_new) {
+                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff);
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * FBS + o_new] = fk[s4];
+            }
+            if (quad == o_new / 4) {
+                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + toff);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * FBS + o_new] = fv[j];
+            }
+        }
+    }
+
+    bf16x8 qv[4];
+    {
+        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+            q + (static_cast<int64_t>(seq) * num_q_heads + (row_ok ? hq : 0)) * FD);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            bf16x8 v = qp[4 * s4 + quad];
+            qv[s4] = row_ok ? v : bf16x8{};
+        }
+    }
+    SoftmaxState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
+    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
+    // two tiles in flight; loads are unconditional (past the end they repeat
+    // the last tile), as on the fast path
+    Tile buf[2];
+    auto load_t = [&](Tile& t, int jj) {
+        const int64_t o = entry_off(jj);
+        load_tile<NT>(t, k_head + o, v_head + o, lane);
+    };
+    load_t(buf[0], 0);
+    for (int j0 = 0; j0 < mblk; j0 += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int j = j0 + u;
+            load_t(buf[u ^ 1], j + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (APPEND) {
+                if (append_here && j == mblk - 1) {
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4)
+                        if (row == o_new) buf[u].k[s4] = fk[s4];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
+                }
+            }
+            if (j < mblk) consume_tile(st, buf[u], qv, scale_log2, lane, j == mblk - 1 ? last_valid : FBS);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    const float lsum = sum_across_rows(st.l);
+    if (!row_ok) return;
+    if (nparts == 1) {
+        const float inv = 1.f / lsum;
+        uint2* o = out_row();
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
+                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
+        return;
+    }
+    const int64_t pidx = (static_cast<int64_t>(seq) * num_q_heads + hq) * max_parts + part;
+    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
+    if (quad == 0) {
+        ws_m[pidx] = st.m;
+        ws_l[pidx] = lsum;
+    }
+}
+
+// ============================================================================
 // Generic path
 // ============================================================================
 
@@ -1011,6 +1286,26 @@ int launch_grouped(const DecodeArgs& a, int members) {
                       a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
+template <bool NT, bool APPEND>
+int launch_cascade(const DecodeArgs& a) {
+    const int per = FG / a.group;
+    const int chunks = (a.num_seqs + 4 * per - 1) / (4 * per);
+    dim3 grid(a.num_kv_heads, chunks, a.max_parts * per);
+    const float sl2 = a.scale * kLog2e;
+    hipLaunchKernelGGL((decode_cascade_kernel<NT, APPEND>), grid, dim3(256), 0, a.stream,
+                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
+                       static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
+                       a.num_blocks, a.block_stride, a.num_seqs, a.num_q_heads, a.group,
+                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
+                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                       static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                       a.num_kv_heads);
+    int st = check_launch("decode (prefix runs)");
+    if (st != PA_OK) return st;
+    return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                      a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
+}
+
 template <int BS>
 int launch_fast_bs(const DecodeArgs& a, bool nt) {
     if (a.k_new) return nt ? launch_fast<true, true, BS>(a) : launch_fast<false, true, BS>(a);
@@ -1049,6 +1344,12 @@ int launch_decode(const DecodeArgs& a_in) {
         a.cow_src = nullptr;
     }
     const bool nt = (a.flags & PA_DECODE_STREAM_KV) != 0;
+    if ((a.flags & PA_DECODE_PREFIX_RUNS) && a.cow_src == nullptr && fast_path_ok(&c, a.group) &&
+        FG % a.group == 0 && a.part_tokens % FBS == 0 && a.part_tokens <= 64 * FBS && a.max_parts >= 2 &&
+        static_cast<int64_t>(a.max_parts) * (FG / a.group) <= 65535) {
+        if (a.k_new) return nt ? launch_cascade<true, true>(a) : launch_cascade<false, true>(a);
+        return nt ? launch_cascade<true, false>(a) : launch_cascade<false, false>(a);
+    }
     const int64_t grouped_z = static_cast<int64_t>(a.max_parts) * (FG / a.group);
     if (fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0 && (a.flags & PA_DECODE_GROUP_SHARED) &&
         a.group <= FG / 2 && grouped_z <= 65535) {

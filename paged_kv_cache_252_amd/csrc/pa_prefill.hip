@@ -184,28 +184,12 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 // the one being consumed, and every wave reads its MFMA operands from LDS.  One barrier per tile: after it, the tile is in LDS and
 // every wave is done with the previous one, whose stage is then refilled.
 
-// 16 bytes per lane from gptr to LDS at lds_base + lane * 16 (lds_base
-// wave-uniform; that lane layout was checked on the device).  In asm so that
-// the compiler does not wait for every LDS copy before each LDS read; the
-// loop waits itself, by count.  M0 is set here and used by nothing else in
-// these kernels.
-__device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(gptr), "s"(lds_base) : "memory");
-}
-
 // LDS stages: S - 1 tiles in flight while one is consumed; waves per
 // workgroup sharing them.  Measured on the chunked-prefill workload: 4 waves
 // with 3, 4 or 6 stages 216-217 us, 8 stages 236 us (the LDS then limits the
 // workgroups per CU); 2 waves 228-242 us, 8 waves 291 us.
 constexpr int kPrefillStages = 4;
 constexpr int kPrefillLdsWaves = 4;
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops outstanding
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int RG, int S, int W>
 __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(

@@ -324,5 +324,21 @@ __device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf
     consume_tile_rows(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
 }
 
+// 16 bytes per lane from gptr to LDS at lds_base + lane * 16 (lds_base
+// wave-uniform; that lane layout was checked on the device).  In asm so that
+// the compiler does not wait for every LDS copy before each LDS read; the
+// loop waits itself, by count.  M0 is set here and used by nothing else in
+// these kernels.
+__device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gptr), "s"(lds_base) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops outstanding
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace
 }  // namespace pa

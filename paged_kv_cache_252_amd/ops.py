@@ -30,6 +30,7 @@ HEADERS = [os.path.join(os.path.dirname(HERE), "include", h) for h in ("pa.h", "
 PA_F32, PA_BF16 = 0, 1
 PA_DECODE_STREAM_KV = 1
 PA_DECODE_GROUP_SHARED = 2
+PA_DECODE_PREFIX_RUNS = 4
 _DTYPES = {"f32": (PA_F32, torch.float32), "bf16": (PA_BF16, torch.bfloat16)}
 
 
@@ -337,13 +338,15 @@ def _decode_args(spec, q, k_cache, v_cache, block_tables, context_lens, max_cont
     return dev, s, hq, out, workspace, ws_bytes
 
 
-def _flags(stream_kv: bool, group_shared: bool) -> int:
-    return (PA_DECODE_STREAM_KV if stream_kv else 0) | (PA_DECODE_GROUP_SHARED if group_shared else 0)
+def _flags(stream_kv: bool, group_shared: bool, prefix_runs: bool = False) -> int:
+    return ((PA_DECODE_STREAM_KV if stream_kv else 0) | (PA_DECODE_GROUP_SHARED if group_shared else 0)
+            | (PA_DECODE_PREFIX_RUNS if prefix_runs else 0))
 
 
 def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
            max_context_len: int, scale: float, out=None, workspace=None,
-           partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False):
+           partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False,
+           prefix_runs: bool = False):
     """``pa_decode``: attention of one query per request over its paged history.
 
     ``q`` is [num_seqs, Hq, head_dim]; returns ``out`` of the same shape and
@@ -351,7 +354,10 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
     when not given.  ``stream_kv`` sets ``PA_DECODE_STREAM_KV``: a cache hint
     for batches in which no block is read by two requests.  ``group_shared``
     sets ``PA_DECODE_GROUP_SHARED``: consecutive requests that share leading
-    blocks are decoded together and read those blocks once.
+    blocks are decoded together and read those blocks once.  ``prefix_runs``
+    sets ``PA_DECODE_PREFIX_RUNS``: for long runs of requests with a common
+    prefix, partitions a whole chunk of requests shares are decoded once for
+    all of them.
     """
     dev, s, hq, out, workspace, ws_bytes = _decode_args(
         spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, workspace,
@@ -361,7 +367,7 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
                                         _ptr(block_tables), _ptr(context_lens), s, hq,
                                         block_tables.shape[1], max_context_len, float(scale),
                                         _ptr(out), _ptr(workspace), ws_bytes,
-                                        partition_tokens, _flags(stream_kv, group_shared),
+                                        partition_tokens, _flags(stream_kv, group_shared, prefix_runs),
                                         _stream(dev)))
     return out
 
@@ -369,7 +375,7 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
 def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tables,
                   context_lens, max_context_len: int, scale: float, out=None, workspace=None,
                   partition_tokens: int = 0, stream_kv: bool = False,
-                  group_shared: bool = False):
+                  group_shared: bool = False, prefix_runs: bool = False):
     """``pa_decode_append``: append each request's token at position L-1, then decode.
 
     ``k_new``/``v_new`` are [num_seqs, Hkv, head_dim]; the caches are written.
@@ -387,13 +393,14 @@ def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tabl
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q),
         _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1], max_context_len,
         float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
-        _flags(stream_kv, group_shared), _stream(dev)))
+        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
     return out
 
 
 def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, block_tables,
                 context_lens, max_context_len: int, scale: float, out=None, workspace=None,
-                partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False):
+                partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False,
+                prefix_runs: bool = False):
     """``pa_decode_step``: copy-on-write of each request's last block from
     ``cow_src[i]`` (int32 [num_seqs], -1 = none), then append + decode."""
     dev, s, hq, out, workspace, ws_bytes = _decode_args(
@@ -413,7 +420,7 @@ def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, blo
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
         _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
         max_context_len, float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
-        _flags(stream_kv, group_shared), _stream(dev)))
+        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
     return out
 
 

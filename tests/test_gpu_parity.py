@@ -471,6 +471,55 @@ def test_grouped_prefix_append(group, part):
     assert_close(w, fused, oracle_decode(w), f"grouped append g={group}")
 
 
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("part", [0, 64])
+def test_prefix_runs_bit_identical(group, part):
+    """PA_DECODE_PREFIX_RUNS: partitions that a whole chunk of requests shares
+    are decoded cooperatively, the rest one request per wave, in one launch.
+    The same bits as one request per wave for decode and decode_append, with
+    a request in the run that shares nothing and one with no history."""
+    say(f"prefix runs g={group} part={part}")
+    hkv = 2
+    w = inputs.shared_prefix(num_seqs=80, prefix_len=256, suffix_lo=1, suffix_hi=70,
+                             num_blocks=2200, num_q_heads=hkv * group, num_kv_heads=hkv,
+                             device=DEV)
+    used = set(w.referenced_blocks().tolist())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    for j in range(16):   # request 9: the same bytes in blocks of its own
+        nb = free.pop()
+        w.k_cache[nb] = w.k_cache[int(w.shared_blocks[j])]
+        w.v_cache[nb] = w.v_cache[int(w.shared_blocks[j])]
+        w.block_tables[9, j] = nb
+    len20 = int(w.context_lens[20])
+    w.context_lens[20] = 0
+    poison_tails(w)
+    spec = ops.CacheSpec.of(w)
+    base = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                      w.max_context_len, w.scale, partition_tokens=part)
+    for stream_kv, grouped in ((True, False), (False, True)):
+        runs = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                          w.max_context_len, w.scale, partition_tokens=part, stream_kv=stream_kv,
+                          group_shared=grouped, prefix_runs=True)
+        assert same_bits(runs, base), (stream_kv, grouped)
+    assert_close(w, runs, oracle_decode(w), f"prefix runs g={group}")
+    w.context_lens[20] = len20   # every request appends one token, in a block of its own
+    inputs.add_step_tokens(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                     w.max_context_len, w.scale, partition_tokens=part)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                              w.context_lens, w.max_context_len, w.scale, partition_tokens=part,
+                              stream_kv=True, prefix_runs=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+    assert same_bits(fused, sep)
+
+
 def test_grouped_fanout_step():
     """Fan-out branches decoded four per wave: copy, grouped append+decode."""
     say("grouped fan-out step")
