@@ -706,9 +706,12 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
 // position (the member's history extends past it), so the append, when
 // asked for, is always done by the per-member waves.
 constexpr int kCascadeStages = 4;
+// Three waves per SIMD: the append variant would take 172 VGPRs (two waves);
+// held to 168 it spills 24 bytes per lane and runs the shared-prefix step
+// 2-3 % faster.
 
 template <bool NT, bool APPEND>
-__global__ __launch_bounds__(256) void decode_cascade_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_cascade_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
