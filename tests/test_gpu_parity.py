@@ -971,7 +971,7 @@ def _step_both_ways(w, spec, pairs, cow_src, **kw):
     return ref, got
 
 
-@pytest.mark.parametrize("grouped", [False, True])
+@pytest.mark.parametrize("grouped", [False, True, "runs"])
 @pytest.mark.parametrize("stream_kv", [False, True])
 @pytest.mark.parametrize("part", [0, 64])
 def test_decode_step_fanout(grouped, stream_kv, part):
@@ -984,8 +984,11 @@ def test_decode_step_fanout(grouped, stream_kv, part):
     spec = ops.CacheSpec.of(w)
     cow_src = _cow_src_of(w)
     assert int((cow_src >= 0).sum()) == w.cow_pairs.shape[0]
+    # ("runs": PA_DECODE_PREFIX_RUNS as well, which copy-on-write sources turn off
+    # in pa_decode_step and which finds no chunk-wide sharing in pa_decode_append)
     ref, got = _step_both_ways(w, spec, w.cow_pairs, cow_src, partition_tokens=part,
-                               stream_kv=stream_kv, group_shared=grouped)
+                               stream_kv=stream_kv, group_shared=bool(grouped),
+                               prefix_runs=grouped == "runs")
     assert same_bits(got, ref)
     assert_close(w, got, oracle_decode(w), "decode_step fan-out")
 
