@@ -30,6 +30,11 @@
 // their scores and zero for their values (never by multiplying by zero, so
 // stale NaN bytes in a block's tail cannot leak).
 //
+// Shared blocks (same tile consumer, same bits): the grouped path serves up
+// to 16/g consecutive requests per wave and loads a block they all name once;
+// the prefix-runs path decodes a partition that a whole chunk of requests
+// shares once for the chunk, four waves reading each tile through LDS.
+//
 // Generic path (fp32 or bf16, other head_dim / block_size): one wave per
 // (request, query head, partition), one token per step, lanes over dims.
 #include "pa_tile.h"
