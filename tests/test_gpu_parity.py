@@ -635,6 +635,12 @@ def test_full_size_sampled(name):
         assert np.array_equal(slots.cpu().numpy(), want_slots)
     say(f"full-size {name}: decode (auto partition)")
     out = run_decode(w)
+    # the flags the benchmark decodes this workload with: the same bits
+    flags = {"gqa": dict(stream_kv=True), "long": dict(stream_kv=True),
+             "prefix": dict(stream_kv=True, group_shared=True, prefix_runs=True),
+             "fanout": dict(stream_kv=True, group_shared=True)}[name]
+    say(f"full-size {name}: decode with {sorted(flags)}")
+    assert same_bits(run_decode(w, **flags), out)
     torch.cuda.synchronize()
     out_np = to_np(out)
     assert not np.isnan(paged.to_f64(out_np, w.dtype)).any()
