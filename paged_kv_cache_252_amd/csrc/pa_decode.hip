@@ -60,7 +60,15 @@ constexpr size_t kMaxWgLds = 32768;
 // workgroup (wave w = partition w, at most kMaxWgParts of them) and are
 // merged through LDS after a workgroup barrier, instead of by the merge
 // kernel.  Waves without a partition wait at the barrier.
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS>
+//
+// PERSIST (with at most 64 requests): the grid is (KV head, Z) and wave z of
+// a head takes items z, z + Z, z + 2Z, ... of the list of (request,
+// partition) pairs of all requests, request-major, built from the lengths in
+// the wave.  The host sizes Z so that every wave of the grid is resident at
+// once: with more items than that, a one-wave-per-item grid would leave its
+// last items running as a tail on a mostly idle device.  Each item is
+// computed exactly as in the plain grid, so the bits are the same.
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST>
 __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
@@ -68,17 +76,19 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
     int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src) {
+    const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
+    int num_seqs) {
     // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
     // dealt to the XCDs round-robin, so each XCD sees every partition index
     // and the same heads for all requests (a shared prefix's head slice then
     // stays in one XCD's L2).
     const int h = blockIdx.x;
-    const int seq = blockIdx.y;
-    const int part = WGM ? static_cast<int>(threadIdx.x >> 6) : static_cast<int>(blockIdx.z);
     const int lane = threadIdx.x & 63;
     const int row = lane & 15;
     const int quad = lane >> 4;
+
+  // one (request, partition) item
+  auto body = [&](const int seq, const int part) {
 
     int L = context_lens[seq];
     L = L < 0 ? 0 : (L > len_clamp ? len_clamp : L);
@@ -309,6 +319,43 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
     if (quad == 0) {
         ws_m[pidx] = st.m;
         ws_l[pidx] = lsum;
+    }
+  };
+
+    if constexpr (PERSIST) {
+        static_assert(!WGM, "persistent waves merge through the merge kernel");
+        int np = 0;                                  // lane i: request i's partitions
+        if (lane < num_seqs) {
+            int Li = context_lens[lane];
+            Li = Li < 0 ? 0 : (Li > len_clamp ? len_clamp : Li);
+            np = (Li + part_tokens - 1) / part_tokens;
+        }
+        int incl = np;                               // inclusive prefix sum over lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off);
+            if (lane >= off) incl += v;
+        }
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        for (int it = static_cast<int>(blockIdx.y); it < total; it += static_cast<int>(gridDim.y)) {
+            const int seq = static_cast<int>(__builtin_ctzll(__ballot(lane < num_seqs && incl > it)));
+            body(seq, it - (__builtin_amdgcn_readlane(incl, seq) - __builtin_amdgcn_readlane(np, seq)));
+        }
+        if (blockIdx.y == 0) {                       // empty histories: zero output
+            uint64_t zm = __ballot(lane < num_seqs && np == 0);
+            while (zm != 0) {
+                const int seq = static_cast<int>(__builtin_ctzll(zm));
+                zm &= zm - 1;
+                if (row < group) {
+                    uint2* o = reinterpret_cast<uint2*>(
+                        out + (static_cast<int64_t>(seq) * num_q_heads + h * group + row) * FD);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+                }
+            }
+        }
+    } else {
+        body(static_cast<int>(blockIdx.y), WGM ? static_cast<int>(threadIdx.x >> 6) : static_cast<int>(blockIdx.z));
     }
 }
 
@@ -1243,13 +1290,22 @@ int launch_generic_d(const DecodeArgs& a) {
     }
 }
 
+// One-wave workgroups of `kernel` that one CU keeps resident at once (from the
+// kernel's registers), or 0 if the runtime cannot say.
+int workgroups_per_cu(const void* kernel) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess || per_cu <= 0)
+        return 0;
+    return per_cu;
+}
+
 template <bool NT, bool APPEND, int BS>
 int launch_fast(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
     const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (FD + 4) * sizeof(float);
     if (a.max_parts >= 2 && a.max_parts <= kMaxWgParts && wg_lds <= kMaxWgLds) {
         // partitions of a request are the waves of one workgroup, merged in LDS
-        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true, BS>),
+        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true, BS, false>),
                            dim3(a.num_kv_heads, a.num_seqs, 1), dim3(64 * a.max_parts), wg_lds,
                            a.stream, static_cast<const __bf16*>(a.k_cache),
                            static_cast<const __bf16*>(a.v_cache), static_cast<const __bf16*>(a.q),
@@ -1257,18 +1313,29 @@ int launch_fast(const DecodeArgs& a) {
                            a.num_q_heads, a.group, a.max_blocks_per_seq, a.len_clamp, a.part_tokens,
                            a.max_parts, sl2, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                            static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                           a.num_kv_heads, a.cow_src);
+                           a.num_kv_heads, a.cow_src, a.num_seqs);
         return check_launch("decode (fast, workgroup merge)");
     }
-    dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-    hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS>), grid, dim3(64), 0, a.stream,
+    // One wave per (KV head, request, partition), unless that grid holds more
+    // waves than the device keeps resident: then as many persistent waves per
+    // head as fit, each taking every Z-th item (at most 64 requests).
+    const int64_t upper = static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.max_parts;
+    static const int per_cu = workgroups_per_cu(reinterpret_cast<const void*>(
+        &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, true>));
+    const int64_t resident = static_cast<int64_t>(per_cu) * device_cu_count();
+    const bool persist = a.num_seqs <= 64 && resident >= a.num_kv_heads && upper > resident;
+    const dim3 grid = persist ? dim3(a.num_kv_heads, static_cast<unsigned>(std::min<int64_t>(resident / a.num_kv_heads, 65535)), 1)
+                              : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
+    auto kernel = persist ? &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, true>
+                          : &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, false>;
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_q_heads, a.group,
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
                        static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                       a.num_kv_heads, a.cow_src);
+                       a.num_kv_heads, a.cow_src, a.num_seqs);
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
     return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,

@@ -215,6 +215,39 @@ def test_fast_path_groups_and_partitions(group, part):
     assert same_bits(out, streamed)              # a cache hint: the same bits
 
 
+@pytest.mark.parametrize("part", [16, 32])
+def test_fast_path_persistent_waves(part):
+    """More partitions than resident waves: persistent waves walk the
+    (request, partition) list.  Same bits as the grouped kernel (its own
+    grid, the same partitions and arithmetic), close to the oracle, with a
+    request of no history; decode_append too."""
+    say(f"persistent waves part={part}")
+    w = inputs.paged_random("pw", 8, 1, 2200, 32, 8, num_blocks=1400, seed=75, device=DEV)
+    w.context_lens[3] = 0
+    poison_tails(w)
+    spec = ops.CacheSpec.of(w)
+    out = run_decode(w, partition_tokens=part)
+    ref_bits = run_decode(w, partition_tokens=part, group_shared=True)
+    assert same_bits(out, ref_bits)
+    assert_close(w, out, oracle_decode(w), f"persistent part={part}")
+    w.context_lens[3] = 7
+    inputs.add_step_tokens(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = ops.decode(spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                     w.max_context_len, w.scale, partition_tokens=part, group_shared=True)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                              w.context_lens, w.max_context_len, w.scale, partition_tokens=part,
+                              stream_kv=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+    assert same_bits(fused, sep)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_separate_dense_pools(dtype):
     """K and V in two dense buffers (block stride 0) instead of one combined buffer."""
