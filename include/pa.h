@@ -84,7 +84,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4   /* 4: PA_DECODE_PREFIX_RUNS */
 
 typedef enum {
     PA_F32 = 0,   /* IEEE binary32 */

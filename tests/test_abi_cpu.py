@@ -29,7 +29,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ops.abi_version() == 3
+    assert ops.abi_version() == 4
     assert ops.status_string(0) == "PA_OK"
     assert ops.status_string(5) == "PA_ERR_UNSUPPORTED"
     assert ops.status_string(8) == "PA_ERR_VALIDATE"
