@@ -53,42 +53,50 @@ constexpr size_t kMaxWgLds = 32768;
 // Fast path
 // ============================================================================
 
-// APPEND: the call also appends each request's newest token (position L-1):
-// the wave of the request's last partition stores k_new/v_new into the cache
-// and uses them in place of whatever its load of that slot returned.
-// WGM: the partitions of one (request, KV head) are the waves of one
-// workgroup (wave w = partition w, at most kMaxWgParts of them) and are
-// merged through LDS after a workgroup barrier, instead of by the merge
-// kernel.  Waves without a partition wait at the barrier.
-//
-// PERSIST (with at most 64 requests): the grid is (KV head, Z) and wave z of
-// a head takes items z, z + Z, z + 2Z, ... of the list of (request,
-// partition) pairs of all requests, request-major, built from the lengths in
-// the wave.  The host sizes Z so that every wave of the grid is resident at
-// once: with more items than that, a one-wave-per-item grid would leave its
-// last items running as a tail on a mostly idle device.  Each item is
-// computed exactly as in the plain grid, so the bits are the same.
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST>
-__global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
-    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
-    const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
-    int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
-    int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
-    int num_seqs) {
-    // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
-    // dealt to the XCDs round-robin, so each XCD sees every partition index
-    // and the same heads for all requests (a shared prefix's head slice then
-    // stays in one XCD's L2).
-    const int h = blockIdx.x;
+// The arguments of one decode launch on the fast path.
+struct FastArgs {
+    const __bf16* __restrict__ k_cache;
+    const __bf16* __restrict__ v_cache;
+    const __bf16* __restrict__ q;
+    const int32_t* __restrict__ block_tables;
+    const int32_t* __restrict__ context_lens;
+    int64_t num_blocks, blk_stride;
+    int num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts;
+    float scale_log2;
+    __bf16* __restrict__ out;
+    float* __restrict__ ws_acc;
+    float* __restrict__ ws_m;
+    float* __restrict__ ws_l;
+    const __bf16* __restrict__ k_new;
+    const __bf16* __restrict__ v_new;
+    int num_kv_heads;
+    const int32_t* __restrict__ cow_src;
+};
+
+// One wave's item of the fast path: partition `part` of request `seq` for KV
+// head h (the grid and the flags are described at decode_fast_kernel).
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS>
+__device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const int seq, const int part) {
+    const __bf16* __restrict__ k_cache = a.k_cache;
+    const __bf16* __restrict__ v_cache = a.v_cache;
+    const __bf16* __restrict__ q = a.q;
+    const int32_t* __restrict__ block_tables = a.block_tables;
+    const int32_t* __restrict__ context_lens = a.context_lens;
+    const int64_t num_blocks = a.num_blocks, blk_stride = a.blk_stride;
+    const int num_q_heads = a.num_q_heads, group = a.group, max_blocks_per_seq = a.max_blocks_per_seq;
+    const int len_clamp = a.len_clamp, part_tokens = a.part_tokens, max_parts = a.max_parts;
+    const float scale_log2 = a.scale_log2;
+    __bf16* __restrict__ out = a.out;
+    float* __restrict__ ws_acc = a.ws_acc;
+    float* __restrict__ ws_m = a.ws_m;
+    float* __restrict__ ws_l = a.ws_l;
+    const __bf16* __restrict__ k_new = a.k_new;
+    const __bf16* __restrict__ v_new = a.v_new;
+    const int num_kv_heads = a.num_kv_heads;
+    const int32_t* __restrict__ cow_src = a.cow_src;
     const int lane = threadIdx.x & 63;
     const int row = lane & 15;
     const int quad = lane >> 4;
-
-  // one (request, partition) item
-  auto body = [&](const int seq, const int part) {
 
     int L = context_lens[seq];
     L = L < 0 ? 0 : (L > len_clamp ? len_clamp : L);
@@ -320,6 +328,48 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
         ws_m[pidx] = st.m;
         ws_l[pidx] = lsum;
     }
+}
+
+// APPEND: the call also appends each request's newest token (position L-1):
+// the wave of the request's last partition stores k_new/v_new into the cache
+// and uses them in place of whatever its load of that slot returned.
+// WGM: the partitions of one (request, KV head) are the waves of one
+// workgroup (wave w = partition w, at most kMaxWgParts of them) and are
+// merged through LDS after a workgroup barrier, instead of by the merge
+// kernel.  Waves without a partition wait at the barrier.
+//
+// PERSIST (with at most 64 requests): the grid is (KV head, Z) and wave z of
+// a head takes items z, z + Z, z + 2Z, ... of the list of (request,
+// partition) pairs of all requests, request-major, built from the lengths in
+// the wave.  The host sizes Z so that every wave of the grid is resident at
+// once: with more items than that, a one-wave-per-item grid would leave its
+// last items running as a tail on a mostly idle device.  Each item is
+// computed exactly as in the plain grid, so the bits are the same.
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST>
+__global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
+    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
+    const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
+    int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
+    int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
+    int num_seqs) {
+    // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
+    // dealt to the XCDs round-robin, so each XCD sees every partition index
+    // and the same heads for all requests (a shared prefix's head slice then
+    // stays in one XCD's L2).
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int row = lane & 15;
+    const int quad = lane >> 4;
+
+  // one (request, partition) item
+  const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
+                    num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
+                    scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src};
+  auto body = [&](const int seq, const int part) {
+      fast_item<NBUF, NT, APPEND, WGM, BS>(fa, h, seq, part);
   };
 
     if constexpr (PERSIST) {
@@ -884,132 +934,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         return;
     }
 
-    // One member per wave, as the fast path (block size 16).
+    // One member per wave, as the fast path does (one wave per request, KV
+    // head and partition, block size 16; no copy-on-write here).
     const int m = slot * 4 + wave;
     if (m >= nmem) return;
-    const int seq = seq0 + m;
-    const int L = clampL(context_lens[seq]);
-    const int hq = h * group + row;
-    const bool row_ok = row < group;
-    auto out_row = [&]() {
-        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
-    };
-    if (tok0 >= L) {
-        if (L == 0 && part == 0 && row_ok) {         // empty history: zero output
-            uint2* o = out_row();
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
-        }
-        return;
-    }
-    const int mtok1 = min(L, tok1);
-    const int mblk = (mtok1 - tok0 + FBS - 1) / FBS;
-    const int last_valid = mtok1 - (tok0 + (mblk - 1) * FBS);
-    const int nparts = (L + part_tokens - 1) / part_tokens;
-    int my_phys = 0;
-    if (lane < mblk)
-        my_phys = clamp_block(block_tables[static_cast<int64_t>(seq) * max_blocks_per_seq + blk0 + lane],
-                              num_blocks);
-    auto entry_off = [&](int e) {
-        return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, e < mblk ? e : mblk - 1)) * blk_stride;
-    };
-
-    // Appending (the wave of the last partition): the four lanes of row o
-    // hold the token's 16 key chunks, the 16 lanes of quad o/4 its 128 value
-    // dims; they store them to the cache and into the loaded tile.
-    const bool append_here = APPEND && part == nparts - 1;
-    const int o_new = (L - 1) % FBS;
-    bf16x8 fk[4];
-    short fv[8];
-    if constexpr (APPEND) {
-        if (append_here) {
-            const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * FD;
-            const bf16x8* kn = reinterpret_cast<const bf16x8*>(k_new + nrow);
-            const short* vn = reinterpret_cast<const short*>(v_new + nrow);
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) fk[s4] = kn[4 * s4 + quad];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) fv[j] = vn[16 * j + row];
-            const int64_t toff = entry_off(mblk - 1) + static_cast<int64_t>(h) * FTILE;
-            if (row == o_new) {
-                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + toff);
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * FBS + o_new] = fk[s4];
-            }
-            if (quad == o_new / 4) {
-                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + toff);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * FBS + o_new] = fv[j];
-            }
-        }
-    }
-
-    bf16x8 qv[4];
-    {
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            q + (static_cast<int64_t>(seq) * num_q_heads + (row_ok ? hq : 0)) * FD);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-            bf16x8 v = qp[4 * s4 + quad];
-            qv[s4] = row_ok ? v : bf16x8{};
-        }
-    }
-    SoftmaxState st;
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * FTILE;
-    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * FTILE;
-    // two tiles in flight; loads are unconditional (past the end they repeat
-    // the last tile), as on the fast path
-    Tile buf[2];
-    auto load_t = [&](Tile& t, int jj) {
-        const int64_t o = entry_off(jj);
-        load_tile<NT>(t, k_head + o, v_head + o, lane);
-    };
-    load_t(buf[0], 0);
-    for (int j0 = 0; j0 < mblk; j0 += 2) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = j0 + u;
-            load_t(buf[u ^ 1], j + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (APPEND) {
-                if (append_here && j == mblk - 1) {
-#pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
-                        if (row == o_new) buf[u].k[s4] = fk[s4];
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
-                }
-            }
-            if (j < mblk) consume_tile(st, buf[u], qv, scale_log2, lane, j == mblk - 1 ? last_valid : FBS);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    const float lsum = sum_across_rows(st.l);
-    if (!row_ok) return;
-    if (nparts == 1) {
-        const float inv = 1.f / lsum;
-        uint2* o = out_row();
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
-                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
-        return;
-    }
-    const int64_t pidx = (static_cast<int64_t>(seq) * num_q_heads + hq) * max_parts + part;
-    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
-    if (quad == 0) {
-        ws_m[pidx] = st.m;
-        ws_l[pidx] = lsum;
-    }
+    const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
+                      num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
+                      scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, nullptr};
+    fast_item<PA_FAST_NBUF, NT, APPEND, false, FBS>(fa, h, seq0 + m, part);
 }
 
 // ============================================================================
