@@ -51,6 +51,19 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
     const int dof = blockIdx.z * se;                      // its first dim
     const int cs = se / X;                                // its 16-byte chunks per row
     const int tt = tile_tokens(block_size);
+    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
+    const int64_t col0 = static_cast<int64_t>(h) * head_dim + dof;
+    // The window's own rows t0 .. t0 + 15 go out now, beside the slot loads:
+    // a chunk's slots are almost always its rows' (only rows of segments
+    // that run past the window, t0 + 16 .. t0 + 30, wait for the slots).
+    uint4 kp = {0u, 0u, 0u, 0u}, vp = {0u, 0u, 0u, 0u};
+    const int pr = threadIdx.x / cs, pc = threadIdx.x - (threadIdx.x / cs) * cs;
+    const bool pre = threadIdx.x < 16 * cs && t0 + pr < num_tokens;
+    if (pre) {
+        const int64_t src = (t0 + pr) * row_stride + col0 + pc * X;
+        kp = *reinterpret_cast<const uint4*>(k_new + src);
+        vp = *reinterpret_cast<const uint4*>(v_new + src);
+    }
     for (int i = threadIdx.x; i < 33; i += blockDim.x) {
         const int64_t t = t0 - 1 + i;
         int64_t v = (t >= 0 && t < num_tokens) ? slots[t] : -1;
@@ -80,28 +93,19 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
         jmax = i + seg[i] > jmax ? i + seg[i] : jmax;
     }
     if (jmin >= jmax) return;                  // uniform: nothing starts here
-    const int64_t row_stride = static_cast<int64_t>(num_kv_heads) * head_dim;
-    const int64_t col0 = static_cast<int64_t>(h) * head_dim + dof;
-    const int units = (jmax - jmin) * cs;      // <= 31 * 16 < 2 * 256
-    uint4 kr[2], vr[2];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int u = threadIdx.x + it * 256;
-        if (u < units) {
-            const int r = u / cs, c = u - (u / cs) * cs;
-            const int64_t src = (t0 + jmin + r) * row_stride + col0 + c * X;
-            kr[it] = *reinterpret_cast<const uint4*>(k_new + src);
-            vr[it] = *reinterpret_cast<const uint4*>(v_new + src);
-        }
+    // LDS row r holds token t0 + r: the prefetched rows, then rows 16 ..
+    // jmax - 1 of segments that run past the window
+    if (pre) {
+        *reinterpret_cast<uint4*>(ks + pr * LD + pc * X) = kp;
+        *reinterpret_cast<uint4*>(vs + pr * LD + pc * X) = vp;
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int u = threadIdx.x + it * 256;
-        if (u < units) {
-            const int r = u / cs, c = u - (u / cs) * cs;
-            *reinterpret_cast<uint4*>(ks + r * LD + c * X) = kr[it];
-            *reinterpret_cast<uint4*>(vs + r * LD + c * X) = vr[it];
-        }
+    const int extra = jmax > 16 ? (jmax - 16) * cs : 0;   // <= 15 * 16 < 256
+    if (static_cast<int>(threadIdx.x) < extra) {
+        const int r = 16 + static_cast<int>(threadIdx.x) / cs;
+        const int c = static_cast<int>(threadIdx.x) - (static_cast<int>(threadIdx.x) / cs) * cs;
+        const int64_t src = (t0 + r) * row_stride + col0 + c * X;
+        *reinterpret_cast<uint4*>(ks + r * LD + c * X) = *reinterpret_cast<const uint4*>(k_new + src);
+        *reinterpret_cast<uint4*>(vs + r * LD + c * X) = *reinterpret_cast<const uint4*>(v_new + src);
     }
     __syncthreads();
     const int64_t head_region = static_cast<int64_t>(head_dim) * block_size;
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256) void write_kv_kernel(E* __restrict__ k_cache,
         const int w0 = p - i0;                 // the window's first position in the tile
         const int64_t base = sb[j + 1] * blk_stride + h * head_region +
                              static_cast<int64_t>(o - p) * head_dim;   // the tile
-        const int r0 = j - jmin - i0;          // LDS row of window position 0
+        const int r0 = j - i0;                 // LDS row of window position 0
         for (int idx = threadIdx.x; idx < 16 * cs; idx += blockDim.x) {
             const int i = idx & 15;
             const int c = idx >> 4;
