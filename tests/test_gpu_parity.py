@@ -15,6 +15,8 @@ from ``oracle``.  Each GPU step prints the case it runs first.
 
 import os
 
+import random
+
 import numpy as np
 import pytest
 import torch
@@ -551,6 +553,50 @@ def test_prefix_runs_bit_identical(group, part):
     torch.cuda.synchronize()
     assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
     assert same_bits(fused, sep)
+
+
+def test_random_cross_path():
+    """Seeded random shapes (KV heads, group size, batch, shared prefix, suffix
+    lengths, partition size, an empty history): the plain, grouped,
+    prefix-runs and streaming decode paths give the same bits, close to the
+    oracle; their appends leave the same cache bytes and output bits."""
+    rnd = random.Random(11)
+    for case in range(24):
+        hkv = rnd.choice([1, 2, 4])
+        g = rnd.choice([1, 2, 4, 8, 16])
+        s = rnd.randint(1, 90)
+        prefix = rnd.choice([16, 64, 128, 256, 512])
+        shi = rnd.randint(1, 300)
+        part = rnd.choice([0, 16, 32, 64, 128, 256])
+        say(f"random case {case}: hkv={hkv} g={g} S={s} prefix={prefix} suffix<={shi} part={part}")
+        nb = prefix // 16 + s * ((shi + 15) // 16 + 1) + 64
+        w = inputs.shared_prefix(num_seqs=s, prefix_len=prefix, suffix_lo=1, suffix_hi=shi,
+                                 num_blocks=nb, num_q_heads=hkv * g, num_kv_heads=hkv,
+                                 device=DEV, seed=2000 + case)
+        if s > 3 and rnd.random() < 0.5:
+            w.context_lens[rnd.randrange(s)] = 0
+        poison_tails(w)
+        spec = ops.CacheSpec.of(w)
+        args = (spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
+                w.max_context_len, w.scale)
+        base = ops.decode(*args, partition_tokens=part)
+        for kw in (dict(group_shared=True), dict(prefix_runs=True),
+                   dict(prefix_runs=True, group_shared=True, stream_kv=True), dict(stream_kv=True)):
+            assert same_bits(ops.decode(*args, partition_tokens=part, **kw), base), (case, kw)
+        assert_close(w, base, oracle_decode(w), f"random case {case}")
+        inputs.add_step_tokens(w)
+        k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+        res = []
+        for kw in ({}, dict(group_shared=True), dict(prefix_runs=True, stream_kv=True)):
+            w.k_cache.copy_(k0)
+            w.v_cache.copy_(v0)
+            o = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v,
+                                  w.block_tables, w.context_lens, w.max_context_len, w.scale,
+                                  partition_tokens=part, **kw)
+            torch.cuda.synchronize()
+            res.append((o.clone(), bits(w.k_cache).clone(), bits(w.v_cache).clone()))
+        for o, kc, vc in res[1:]:
+            assert same_bits(o, res[0][0]) and torch.equal(kc, res[0][1]) and torch.equal(vc, res[0][2]), case
 
 
 def test_grouped_fanout_step():
