@@ -293,15 +293,20 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
     // tile t (past the end: the last one again, so every thread issues the same
     // number of copies per tile) into stage t % S; the stage's 8 KiB are K
     // then V, and wave w copies KiB w * kCopies .. (w + 1) * kCopies - 1
+    // V stage layout: 16-byte chunk c of the tile sits at chunk c ^ ((c >> 4) & 1)
+    // (the two chunks of a dim swap for dims 8..15 of every 16), so the 8-byte
+    // reads of rows r and r + 8, 256 bytes apart, fall in different LDS banks.
+    const int v_swz_lane = lane ^ ((lane >> 4) & 1);
     auto issue = [&](int t) {
         const int tc = t < nblk ? t : nblk - 1;
         const int64_t o = static_cast<int64_t>(tbl[tc % kTbl]) * blk_stride +
-                          static_cast<int64_t>(h) * FTILE + lane * 8;
+                          static_cast<int64_t>(h) * FTILE;
         const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
             const int kib = wave * kCopies + c;            // 0..3 K, 4..7 V
-            const __bf16* src = (kib < 4 ? k_cache : v_cache) + o + (kib & 3) * 512;
+            const __bf16* src = kib < 4 ? k_cache + o + (kib & 3) * 512 + lane * 8
+                                          : v_cache + o + (kib & 3) * 512 + v_swz_lane * 8;
             lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
         }
     };
@@ -320,7 +325,8 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
             const bf16x8* kp = reinterpret_cast<const bf16x8*>(stage) + lane;
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
-            const s16x4* vp = reinterpret_cast<const s16x4*>(stage + FTILE) + row * 4 + quad;
+            const s16x4* vp = reinterpret_cast<const s16x4*>(stage + FTILE) +
+                              2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
 #pragma unroll
             for (int j = 0; j < 8; ++j) t.v[j] = vp[64 * j];
             const int v_valid = clampi(lim_max - start, 0, FBS);
