@@ -73,6 +73,35 @@ struct FastArgs {
     const int32_t* __restrict__ cow_src;
 };
 
+// Merge of the partitions 0..nparts-1 of one query row whose partial states
+// sit in LDS at base + p * pstride (acc[FD], then m and l), with the merge
+// kernel's formula: global maximum first, then fused multiply-adds in
+// partition order, one division.  Lane quad writes dims 32*quad..+31 of the
+// bf16 output row o.
+__device__ __forceinline__ void merge_lds_row(const float* base, int pstride, int nparts, int quad,
+                                              uint2* o) {
+    float M = base[FD];
+    for (int p = 1; p < nparts; ++p) M = fmaxf(M, base[p * pstride + FD]);
+    float den = 0.f;
+    f32x4 num[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < nparts; ++p) {
+        const float* src = base + p * pstride;
+        const float w = fast_exp2(src[FD] - M);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            num[k] = fma4(*reinterpret_cast<const f32x4*>(src + 32 * quad + 4 * k), w, num[k]);
+        den = __builtin_fmaf(src[FD + 1], w, den);
+    }
+    const float inv = 1.f / den;
+    uint2* ob = o + 8 * quad;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        ob[k] = make_uint2(pack_bf16x2(num[k][0] * inv, num[k][1] * inv),
+                           pack_bf16x2(num[k][2] * inv, num[k][3] * inv));
+}
+
 // One wave's item of the fast path: partition `part` of request `seq` for KV
 // head h (the grid and the flags are described at decode_fast_kernel).
 template <int NBUF, bool NT, bool APPEND, bool WGM, int BS>
@@ -283,26 +312,7 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
             // merge partitions 0..nparts-1 in order (the merge kernel's formula:
             // global max first, then fused multiply-adds in partition order);
             // lane: row, dims 32*quad..+31
-            float M = wg_part[row * RS + FD];
-            for (int p = 1; p < nparts; ++p) M = fmaxf(M, wg_part[(p * group + row) * RS + FD]);
-            float den = 0.f;
-            f32x4 num[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-            for (int p = 0; p < nparts; ++p) {
-                const float* src = wg_part + (p * group + row) * RS;
-                const float w = fast_exp2(src[FD] - M);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    num[k] = fma4(*reinterpret_cast<const f32x4*>(src + 32 * quad + 4 * k), w, num[k]);
-                den = __builtin_fmaf(src[FD + 1], w, den);
-            }
-            const float inv = 1.f / den;
-            uint2* ob = o + 8 * quad;
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                ob[k] = make_uint2(pack_bf16x2(num[k][0] * inv, num[k][1] * inv),
-                                   pack_bf16x2(num[k][2] * inv, num[k][3] * inv));
+            merge_lds_row(wg_part + row * RS, group * RS, nparts, quad, o);
             return;
         }
         // a single partition: wave 0 holds the whole result (falls through)
@@ -433,8 +443,8 @@ constexpr int kShared = -1;
 // stored by the wave that handles the member's last block and substituted
 // into that tile; the token is staged in LDS because one wave may append for
 // several members.
-template <int MAXR, bool NT, bool APPEND>
-__global__ __launch_bounds__(64) void decode_grouped_kernel(
+template <int MAXR, bool NT, bool APPEND, bool WGM>
+__global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -447,10 +457,13 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
     const int grp = blockIdx.y;
     // z = r_wave * max_parts + part: the waves that do the work of grouped
     // partitions (r_wave 0) are dispatched before the ones that only work in
-    // per-member partitions and otherwise exit at once.
-    const int r_wave = blockIdx.z / max_parts;   // this wave's member in per-member mode
-    const int part = blockIdx.z - r_wave * max_parts;
-    const int lane = threadIdx.x;
+    // per-member partitions and otherwise exit at once.  WGM: z = r_wave and
+    // the partitions are the waves of the workgroup.
+    const int r_wave = WGM ? static_cast<int>(blockIdx.z)
+                           : static_cast<int>(blockIdx.z) / max_parts;   // member in per-member mode
+    const int part = WGM ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))
+                         : static_cast<int>(blockIdx.z) - r_wave * max_parts;
+    const int lane = WGM ? static_cast<int>(threadIdx.x & 63) : static_cast<int>(threadIdx.x);
     const int row = lane & 15;
     const int quad = lane >> 4;
 
@@ -476,13 +489,15 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
     };
-    if (tok0 >= Lmax) {
+    // (WGM: a wave past the longest member's history keeps going with no
+    // tiles, to meet the workgroup's barriers; it has no tasks and no rows.)
+    if (!WGM && tok0 >= Lmax) {
         if (part == 0 && r_wave == 0 && row_ok && my_L == 0) write_zero_row();
         return;
     }
-    const int tok1 = min(Lmax, tok0 + part_tokens);
+    const int tok1 = max(tok0, min(Lmax, tok0 + part_tokens));
     const int blk0 = tok0 / FBS;
-    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64
+    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // 1..64 (WGM: 0..64)
 
     // Appending: the token of each member this wave handles whose newest
     // position lies in this partition goes to the cache and to LDS, from
@@ -555,8 +570,22 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
 #pragma unroll
     for (int r = 0; r < MAXR; ++r)
         if (r < nmem) longest = max(longest, static_cast<int>(__popcll(__ballot(phys[r] >= 0))));
-    const bool grouped = 2 * tasks_here <= 3 * longest;
-    if (grouped ? r_wave != 0 : r_wave >= nmem) return;
+    bool grouped = 2 * tasks_here <= 3 * longest;
+    // WGM: if every partition of the group that has tokens takes the same mode,
+    // one workgroup holds all partitions of each row it serves and merges them
+    // in LDS (uniform); otherwise each wave goes its own way and writes its
+    // partials for the merge kernel, as without WGM.
+    bool uniform = false;
+    if constexpr (WGM) {
+        __shared__ int wg_mode[kMaxWgParts];   // 0: no tokens, 1: grouped, 2: per member
+        if (lane == 0) wg_mode[part] = nblk == 0 ? 0 : (grouped ? 1 : 2);
+        __syncthreads();
+        int seen = 0;
+        for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) seen |= 1 << wg_mode[w];
+        uniform = (seen & 6) != 6;
+        if (uniform) grouped = (seen & 4) == 0;
+    }
+    if (grouped ? r_wave != 0 : r_wave >= nmem) return;   // (uniform: the whole workgroup)
     const bool mine = row_ok && (grouped || my_mem == r_wave);
 
     auto is_shared = [&](int j) { return ((shared_mask >> j) & 1ull) != 0; };
@@ -759,12 +788,36 @@ __global__ __launch_bounds__(64) void decode_grouped_kernel(
     if constexpr (APPEND) store_new_tokens();
 
     const float lsum = sum_across_rows(st.l);
+    const int my_nparts = (my_L + part_tokens - 1) / part_tokens;
+    if (WGM && uniform) {
+        // LDS: [partition][row][acc 128 | m | l | pad 2]; wave 0 merges and
+        // marks the row as done for the merge kernel (l of partition 0 < 0)
+        extern __shared__ float wg_part[];
+        constexpr int RS = FD + 4;
+        if (mine && tok0 < my_L && my_nparts > 1) {
+            float* dst = wg_part + (part * FG + row) * RS;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<f32x4*>(dst + 16 * jj + 4 * quad) = st.acc[jj];
+            if (quad == 0) {
+                dst[FD] = st.m;
+                dst[FD + 1] = lsum;
+            }
+        }
+        __syncthreads();
+        if (part != 0 || !mine) return;
+        if (my_L > 0 && my_nparts > 1) {
+            merge_lds_row(wg_part + row * RS, FG * RS, my_nparts, quad,
+                          reinterpret_cast<uint2*>(out + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD));
+            if (quad == 0) ws_l[(static_cast<int64_t>(my_seq) * num_q_heads + hq) * max_parts] = -1.f;
+            return;
+        }
+        // an empty history or a single partition: wave 0 writes it below
+    }
     if (!mine) return;
     if (tok0 >= my_L) {                       // this row has no tokens in this partition
         if (part == 0 && my_L == 0) write_zero_row();
         return;
     }
-    const int my_nparts = (my_L + part_tokens - 1) / part_tokens;
     if (my_nparts == 1) {
         const float inv = 1.f / lsum;
         uint2* o = reinterpret_cast<uint2*>(out + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD);
@@ -1135,6 +1188,9 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
 // reduce_kernel or the in-workgroup merge of the decode kernel.
 constexpr int kSmallMergeRows = kMergeThreads / (FD / 4);   // rows per workgroup
 
+// SKIP_DONE: rows whose partition-0 l is negative were merged already (by
+// the grouped kernel's workgroups that held all of their partitions).
+template <bool SKIP_DONE>
 __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     const int32_t* __restrict__ context_lens, int64_t rows, int num_q_heads, int len_clamp,
     int part_tokens, int max_parts, const float* __restrict__ ws_acc,
@@ -1150,6 +1206,7 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     if (nparts <= 1) return;   // written directly by the partition kernel
     nparts = nparts < kMaxWgParts ? nparts : kMaxWgParts;
     const int64_t base = row * max_parts;
+    if (SKIP_DONE && ws_l[base] < 0.f) return;
     float m[kMaxWgParts], l[kMaxWgParts];
     f32x4 acc[kMaxWgParts];
 #pragma unroll
@@ -1181,13 +1238,16 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
 
 // The split-K merge of bf16, head_dim-128 partials of `rows` rows
 // (request-major, num_q_heads per request).
+// (skip_done: rows marked as merged are left alone; at most kMaxWgParts
+// partitions.)
 int merge_bf16(const int32_t* lens, int64_t rows, int num_q_heads, int len_clamp, int part_tokens,
                int max_parts, const float* ws_acc, const float* ws_m, const float* ws_l, void* out,
-               hipStream_t stream) {
+               hipStream_t stream, bool skip_done = false) {
     if (rows == 0) return PA_OK;
     if (max_parts <= kMaxWgParts) {
         const int64_t wgs = (rows + kSmallMergeRows - 1) / kSmallMergeRows;
-        hipLaunchKernelGGL(reduce_small_kernel, dim3(static_cast<unsigned>(wgs)), dim3(kMergeThreads), 0,
+        hipLaunchKernelGGL(skip_done ? reduce_small_kernel<true> : reduce_small_kernel<false>,
+                           dim3(static_cast<unsigned>(wgs)), dim3(kMergeThreads), 0,
                            stream, lens, rows, num_q_heads, len_clamp, part_tokens, max_parts, ws_acc,
                            ws_m, ws_l, static_cast<uint16_t*>(out));
         return check_launch("decode merge");
@@ -1283,9 +1343,28 @@ int launch_fast(const DecodeArgs& a) {
 template <int MAXR, bool NT, bool APPEND>
 int launch_grouped(const DecodeArgs& a, int members) {
     const int groups = (a.num_seqs + members - 1) / members;
-    dim3 grid(a.num_kv_heads, groups, a.max_parts * members);
     const float sl2 = a.scale * kLog2e;
-    hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT, APPEND>), grid, dim3(64), 0, a.stream,
+    const size_t wg_lds = static_cast<size_t>(a.max_parts) * FG * (FD + 4) * sizeof(float);
+    if (a.max_parts >= 2 && a.max_parts <= kMaxWgParts && wg_lds <= kMaxWgLds) {
+        // the partitions of a group are the waves of one workgroup, merged in LDS
+        hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT, APPEND, true>),
+                           dim3(a.num_kv_heads, groups, members), dim3(64 * a.max_parts), wg_lds, a.stream,
+                           static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
+                           static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
+                           a.num_blocks, a.block_stride, a.num_seqs, a.num_q_heads, a.group, members,
+                           a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
+                           static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
+                           static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                           a.num_kv_heads, a.cow_src);
+        const int st = check_launch("decode (grouped, workgroup merge)");
+        if (st != PA_OK) return st;
+        // groups whose partitions took different modes are merged here
+        return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                          a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream,
+                          true);
+    }
+    dim3 grid(a.num_kv_heads, groups, a.max_parts * members);
+    hipLaunchKernelGGL((decode_grouped_kernel<MAXR, NT, APPEND, false>), grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, a.num_seqs, a.num_q_heads, a.group, members,

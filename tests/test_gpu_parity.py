@@ -441,7 +441,7 @@ def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-@pytest.mark.parametrize("part", [0, 16, 64])
+@pytest.mark.parametrize("part", [0, 16, 64, 128])
 def test_grouped_decode_bit_identical(group, part):
     """PA_DECODE_GROUP_SHARED gives the same bits as one request per wave, on a
     batch mixing shared prefixes, private suffixes, unshared requests, L = 0
@@ -471,6 +471,35 @@ def test_grouped_decode_bit_identical(group, part):
                              stream_kv=stream_kv, group_shared=True)
         assert same_bits(grouped, base)
     assert_close(w, grouped, ref, f"grouped g={group}")
+
+
+@pytest.mark.parametrize("fill", [-1.0, 0.0, float("nan")])
+def test_grouped_workgroup_merge_workspace(fill):
+    """Grouped decode with at most three partitions: a group whose partitions
+    all take one mode (all shared-walk, or all one member per wave) is merged
+    inside its workgroup and marks its rows done for the merge kernel, the
+    rest go through the merge kernel.  Whatever the workspace held before
+    (here -1.0, 0.0 or NaN everywhere, then the previous batch's partials and
+    marks), the bits equal one request per wave."""
+    say(f"grouped workgroup merge, workspace filled with {fill}")
+    hkv, group = 2, 4
+    ws = None
+    for prefix, part in ((224, 128), (64, 64), (64, 128), (224, 64), (224, 128)):
+        w = inputs.shared_prefix(num_seqs=14, prefix_len=prefix, suffix_lo=1, suffix_hi=15 if prefix == 224 else 90,
+                                 num_blocks=400, num_q_heads=hkv * group, num_kv_heads=hkv, device=DEV)
+        w.context_lens[6] = 0
+        poison_tails(w)
+        spec = ops.CacheSpec.of(w)
+        args = (spec, w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.max_context_len, w.scale)
+        base = ops.decode(*args, partition_tokens=part)
+        need = ops.decode_workspace(spec, w.q.shape[0], w.q.shape[1], w.max_context_len, part, DEV)
+        assert need is not None
+        if ws is None or ws.numel() < need.numel():
+            ws = torch.empty(max(need.numel(), 1 << 20), dtype=torch.uint8, device=DEV)
+            ws.view(torch.float32).fill_(fill)
+        got = ops.decode(*args, partition_tokens=part, group_shared=True, workspace=ws)
+        assert same_bits(got, base), (prefix, part)
+        assert_close(w, got, oracle_decode(w), f"grouped wg merge prefix={prefix} part={part}")
 
 
 @pytest.mark.parametrize("group", [1, 4])
@@ -1058,11 +1087,12 @@ def _step_both_ways(w, spec, pairs, cow_src, **kw):
 
 @pytest.mark.parametrize("grouped", [False, True, "runs"])
 @pytest.mark.parametrize("stream_kv", [False, True])
-@pytest.mark.parametrize("part", [0, 64])
+@pytest.mark.parametrize("part", [0, 64, 128])
 def test_decode_step_fanout(grouped, stream_kv, part):
     """The fan-out step with its copies folded in equals copy + append +
     decode: the same pool bytes (NaN-poisoned free blocks included) and the
-    same output bits."""
+    same output bits.  (Grouped, part 128: at most three partitions, merged
+    inside the workgroup; part 64: up to five, merged by the merge kernel.)"""
     say(f"decode_step fan-out grouped={grouped} stream={stream_kv} part={part}")
     w = inputs.fanout(num_prompts=9, branches=4, prompt_lo=20, prompt_hi=300, num_blocks=500,
                       device=DEV)
