@@ -1200,13 +1200,15 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     const int64_t row = static_cast<int64_t>(blockIdx.x) * kSmallMergeRows + threadIdx.x / C;
     if (row >= rows) return;
     const int64_t seq = row / num_q_heads;
+    const int64_t base = row * max_parts;
     int L = context_lens[seq];
+    // (the mark is loaded beside the length, not after it: one round trip)
+    const float l0 = SKIP_DONE ? ws_l[base] : 0.f;
     L = L < 0 ? 0 : (L > len_clamp ? len_clamp : L);
     int nparts = (L + part_tokens - 1) / part_tokens;
-    if (nparts <= 1) return;   // written directly by the partition kernel
+    // one partition: written directly by the partition kernel
+    if ((nparts <= 1) | (SKIP_DONE && l0 < 0.f)) return;
     nparts = nparts < kMaxWgParts ? nparts : kMaxWgParts;
-    const int64_t base = row * max_parts;
-    if (SKIP_DONE && ws_l[base] < 0.f) return;
     float m[kMaxWgParts], l[kMaxWgParts];
     f32x4 acc[kMaxWgParts];
 #pragma unroll
