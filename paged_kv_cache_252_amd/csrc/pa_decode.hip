@@ -443,6 +443,14 @@ constexpr int kShared = -1;
 // stored by the wave that handles the member's last block and substituted
 // into that tile; the token is staged in LDS because one wave may append for
 // several members.
+// WGM (at most three partitions): the partitions of a group are the waves of
+// one workgroup per member slot (z = r_wave).  After each wave has decided
+// its partition's mode, the waves compare: if every partition with tokens took
+// the same mode, the workgroup that serves a row holds all of that row's
+// partitions, merges them in LDS with the merge kernel's formula and stores
+// -1 as the row's partition-0 l in the workspace; the merge kernel launched
+// after it skips rows marked so.  Otherwise every wave writes its partials
+// and the merge kernel merges them, as without WGM.  Same bits either way.
 template <int MAXR, bool NT, bool APPEND, bool WGM>
 __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
