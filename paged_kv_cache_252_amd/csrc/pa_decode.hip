@@ -1189,12 +1189,15 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_kernel(
 }
 
 // The same merge for at most kMaxWgParts partitions, bf16 output, head_dim
-// 128: 32 lanes per (request, query head), eight of them per workgroup, and
+// 128: 8 lanes per (request, query head), each with four 16-byte chunks of
+// the row (lane c: chunks c, c+8, c+16, c+24), 32 rows per workgroup, and
 // each lane loads all of its row's partitions at once (one memory round trip).
 // The arithmetic is the formula above for that case -- global max first, then
 // fused multiply-adds in partition order -- so the bits are the same as from
 // reduce_kernel or the in-workgroup merge of the decode kernel.
-constexpr int kSmallMergeRows = kMergeThreads / (FD / 4);   // rows per workgroup
+constexpr int kMergeChunks = 4;                               // float4 chunks per lane
+constexpr int kMergeLanes = FD / 4 / kMergeChunks;            // lanes per row
+constexpr int kSmallMergeRows = kMergeThreads / kMergeLanes;   // rows per workgroup
 
 // SKIP_DONE: rows whose partition-0 l is negative were merged already (by
 // the grouped kernel's workgroups that held all of their partitions).
@@ -1203,9 +1206,8 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     const int32_t* __restrict__ context_lens, int64_t rows, int num_q_heads, int len_clamp,
     int part_tokens, int max_parts, const float* __restrict__ ws_acc,
     const float* __restrict__ ws_m, const float* __restrict__ ws_l, uint16_t* __restrict__ out) {
-    constexpr int C = FD / 4;                  // float4 chunks per row
-    const int c = threadIdx.x % C;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * kSmallMergeRows + threadIdx.x / C;
+    const int c = threadIdx.x % kMergeLanes;   // chunks c + kMergeLanes * i of the row
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * kSmallMergeRows + threadIdx.x / kMergeLanes;
     if (row >= rows) return;
     const int64_t seq = row / num_q_heads;
     const int64_t base = row * max_parts;
@@ -1218,32 +1220,40 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     if ((nparts <= 1) | (SKIP_DONE && l0 < 0.f)) return;
     nparts = nparts < kMaxWgParts ? nparts : kMaxWgParts;
     float m[kMaxWgParts], l[kMaxWgParts];
-    f32x4 acc[kMaxWgParts];
+    f32x4 acc[kMaxWgParts][kMergeChunks];
 #pragma unroll
     for (int p = 0; p < kMaxWgParts; ++p) {
         if (p < nparts) {
             m[p] = ws_m[base + p];
             l[p] = ws_l[base + p];
-            acc[p] = reinterpret_cast<const f32x4*>(ws_acc + (base + p) * FD)[c];
+#pragma unroll
+            for (int i = 0; i < kMergeChunks; ++i)
+                acc[p][i] = reinterpret_cast<const f32x4*>(ws_acc + (base + p) * FD)[c + kMergeLanes * i];
         }
     }
     float M = m[0];
 #pragma unroll
     for (int p = 1; p < kMaxWgParts; ++p)
         if (p < nparts) M = fmaxf(M, m[p]);
-    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    f32x4 tot[kMergeChunks];
+#pragma unroll
+    for (int i = 0; i < kMergeChunks; ++i) tot[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dtot = 0.f;
 #pragma unroll
     for (int p = 0; p < kMaxWgParts; ++p) {
         if (p < nparts) {
             const float w = fast_exp2(m[p] - M);
-            tot = fma4(acc[p], w, tot);
+#pragma unroll
+            for (int i = 0; i < kMergeChunks; ++i) tot[i] = fma4(acc[p][i], w, tot[i]);
             dtot = __builtin_fmaf(l[p], w, dtot);
         }
     }
     const float inv = 1.f / dtot;
     uint2* o = reinterpret_cast<uint2*>(out + row * FD) + c;
-    *o = make_uint2(pack_bf16x2(tot[0] * inv, tot[1] * inv), pack_bf16x2(tot[2] * inv, tot[3] * inv));
+#pragma unroll
+    for (int i = 0; i < kMergeChunks; ++i)
+        o[kMergeLanes * i] = make_uint2(pack_bf16x2(tot[i][0] * inv, tot[i][1] * inv),
+                                        pack_bf16x2(tot[i][2] * inv, tot[i][3] * inv));
 }
 
 // The split-K merge of bf16, head_dim-128 partials of `rows` rows
