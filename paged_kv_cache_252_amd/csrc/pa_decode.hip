@@ -1216,7 +1216,8 @@ __global__ __launch_bounds__(kMergeThreads) void reduce_small_kernel(
     const float l0 = SKIP_DONE ? ws_l[base] : 0.f;
     L = L < 0 ? 0 : (L > len_clamp ? len_clamp : L);
     int nparts = (L + part_tokens - 1) / part_tokens;
-    // one partition: written directly by the partition kernel
+    // one partition: written directly by the partition kernel; a marked row:
+    // merged by the partition kernel's workgroup
     if ((nparts <= 1) | (SKIP_DONE && l0 < 0.f)) return;
     nparts = nparts < kMaxWgParts ? nparts : kMaxWgParts;
     float m[kMaxWgParts], l[kMaxWgParts];
