@@ -251,10 +251,10 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *     s_t = scale * <q[i][hq], K_i[t][h]>          for t = 0 .. L-1
  *     out[i][hq] = sum_t softmax(s)_t * V_i[t][h]
  * where K_i[t], V_i[t] are found through block_tables[i] as in
- * pa_slot_mapping ([KG] "Follow One Token Address": after lookup the newest
- * query scores the keys, applies its visibility rule and mixes the values;
- * "The Contiguous Allocation Problem": the attention formula is unchanged by
- * paging).  The query sees positions [0, L): the cache holds the current
+ * pa_slot_mapping ([KG] "Follow One Token Address", closing sentence: the
+ * table only locates keys and values, the decode attention over them is the
+ * usual one; "The Contiguous Allocation Problem": paging changes placement,
+ * not the attention formula).  The query sees positions [0, L): the cache holds the current
  * token's K/V (written by pa_write_kv) and nothing later.  L = 0 gives a
  * zero output.  Positions at or past L are never read into the result, so
  * stale or NaN bytes there do not matter.

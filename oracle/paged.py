@@ -10,13 +10,13 @@ What is computed, and where it comes from:
 * History gather.  [KG] "The Block Table Is the Map" and "Batching Becomes
   More Flexible": the kernel reads the request's block table and gathers the
   history in logical token order, whatever the physical numbering.
-* Attention.  [KG] "Follow One Token Address" (closing sentence: after lookup
-  the newest query scores the right keys, applies its visibility rule and
-  mixes the matching values) and "The Contiguous Allocation Problem" (paging
-  is about placement, not a change of the attention formula).  Read as
-  scaled dot-product softmax attention of one decode query over the first
-  ``L`` cached positions, with grouped query heads mapped to KV head
-  ``hq // (Hq / Hkv)``.
+* Attention.  [KG] "Follow One Token Address" (closing sentence: the table
+  only locates the cached keys and values; once found they are used by the
+  usual decode attention of the newest token, with its visibility rule) and
+  "The Contiguous Allocation Problem" (paging is about placement, not a
+  change of the attention formula).  Read as scaled dot-product softmax
+  attention of one decode query over the first ``L`` cached positions, with
+  grouped query heads mapped to KV head ``hq // (Hq / Hkv)``.
 * KV-write scatter.  The new token's K/V land at ``slot = physical *
   block_size + offset`` ([KG] "Follow One Token Address"); the library
   receives that flat slot per token.
@@ -25,12 +25,17 @@ What is computed, and where it comes from:
   block; only that block is copied ([ZQ] "Most common mistake").
 
 The in-block layout is the library's documented contract (the pages leave it
-to the implementation, [KG] "Split the Cache Into Fixed Blocks").  With
-``x = 16 / element_bytes`` (8 for bf16, 4 for fp32) the element for
-(block b, kv head h, offset t, dim d) sits at
+to the implementation, [KG] "Split the Cache Into Fixed Blocks").  Each pool
+(K or V) reaches the oracle as a dense ``[num_blocks][Hkv * block_size * D]``
+array (how the library spaces blocks in device memory, its block stride, is
+no concern here).  Positions of a block sit in tiles of ``T`` positions
+(``T = 16`` when the block size is a multiple of 16, else the whole block).
+With ``x = 16 / element_bytes`` (8 for bf16, 4 for fp32), tile ``u = t // T``
+and place ``p = t % T``, the element for (block b, kv head h, position t,
+dim d) is, inside the pool array,
 
-    K: (((b * Hkv + h) * (D / x) + d / x) * block_size + t) * x + d % x
-    V: ((b * Hkv + h) * D + d) * block_size + t
+    K: ((((b * Hkv + h) * (block_size / T) + u) * (D / x) + d / x) * T + p) * x + d % x
+    V: (((b * Hkv + h) * (block_size / T) + u) * D + d) * T + p
 
 The oracle reads it through numpy reshapes/transposes, not through those
 scalar formulas (tests pin the two against each other).
@@ -60,7 +65,9 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     bits = np.asarray(bits)
     if bits.dtype != np.uint16:
         raise TypeError("bf16 data must be given as uint16 bit patterns")
-    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    wide = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    with np.errstate(invalid="ignore"):     # signalling-NaN patterns widen to NaN quietly
+        return wide.astype(np.float64)
 
 
 def to_f64(values: np.ndarray, dtype: str) -> np.ndarray:
@@ -88,15 +95,15 @@ def translate(position: int, block_table, block_size: int):
     the table entry for the logical block names the physical block.  The flat
     slot index of the token is ``physical * block_size + offset``.
     """
-    position = int(position)
-    block_size = int(block_size)
-    if block_size <= 0:
+    pos, size = int(position), int(block_size)
+    if size <= 0:
         raise ValueError("block_size must be positive")
-    if position < 0:
+    if pos < 0:
         raise ValueError("position must be non-negative")
-    logical_block, offset = divmod(position, block_size)
-    physical_block = int(block_table[logical_block])
-    return logical_block, offset, physical_block, physical_block * block_size + offset
+    quotient = pos // size                  # which entry of the table
+    remainder = pos - quotient * size       # where inside that block
+    entry = int(block_table[quotient])
+    return quotient, remainder, entry, entry * size + remainder
 
 
 def slot_mapping(block_tables, seq_ids, positions, block_size: int) -> np.ndarray:

@@ -297,7 +297,8 @@ def check_visibility(seed=16):
 
 
 def check_gather_order(seed=17):
-    """Gathered history follows logical order through the table, not physical order."""
+    """The gathered history is ordered by table entry index (logical position);
+    the physical block numbers, scrambled here, play no part in the order."""
     w = inputs.tiny(seed=seed)
     kp, vp = to_np(w.k_cache), to_np(w.v_cache)
     bt = to_np(w.block_tables)
@@ -646,6 +647,68 @@ def check_prefill_rows_are_decodes(seed=42):
     assert not early[:2].any() and early[2].any()
 
 
+# ---- value decoding ([KG] "Split the Cache Into Fixed Blocks": the bytes of a
+# block depend on the element type; bf16 is the upper half of a binary32) ------
+
+def _binary32_upper_half(bits16):
+    """Value of a bf16 pattern assembled from its fields by integer arithmetic:
+    sign bit 15, 8 exponent bits 14..7 (bias 127), 7 fraction bits 6..0 --
+    the top 16 bits of an IEEE 754 binary32.  No float reinterpretation."""
+    sign = -1.0 if bits16 >> 15 else 1.0
+    exponent = (bits16 >> 7) & 0xFF
+    fraction = bits16 & 0x7F
+    if exponent == 0xFF:
+        return sign * math.inf if fraction == 0 else math.nan
+    if exponent == 0:                       # subnormal: fraction * 2^(1 - 127 - 7)
+        return sign * math.ldexp(fraction, -133)
+    return sign * math.ldexp(0x80 | fraction, exponent - 127 - 7)
+
+
+def check_bf16_widening():
+    """bf16 bit patterns widen to the binary32 values they are the top half of."""
+    fixed = {0x3F80: 1.0, 0xBF80: -1.0, 0x4049: 3.140625, 0x0001: 2.0 ** -133,
+             0x0080: 2.0 ** -126, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0x4000: 2.0,
+             0x3E80: 0.25, 0xC2F7: -123.5, 0x0000: 0.0, 0x8000: -0.0,
+             0x7F80: math.inf, 0xFF80: -math.inf}
+    got = paged.bf16_bits_to_f64(np.array(list(fixed), dtype=np.uint16))
+    for (b, want), g in zip(fixed.items(), got.tolist()):
+        assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), (hex(b), g)
+    for b in (0x7FC0, 0xFFC0, 0x7F81, 0xFFFF):
+        assert math.isnan(paged.bf16_bits_to_f64(np.array([b], dtype=np.uint16))[0]), hex(b)
+    # every one of the 65,536 patterns against the field-by-field decode
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    wide = paged.bf16_bits_to_f64(allbits)
+    assert wide.dtype == np.float64 and wide.shape == (1 << 16,)
+    for b, g in enumerate(wide.tolist()):
+        want = _binary32_upper_half(b)
+        if math.isnan(want):
+            assert math.isnan(g), hex(b)
+        else:
+            assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), (hex(b), g)
+    # fp32 storage widens without change
+    f = np.array([1.5, -0.0, 3.4e38, 1e-45], dtype=np.float32)
+    assert paged.to_f64(f, "f32").tolist() == [float(x) for x in f.tolist()]
+
+
+def check_decode_one_head_is_decode_slice(seed=43):
+    """Decoding one (request, KV head) gives exactly the matching rows of the
+    batched decode, for every request and KV head (g = 1, 2 and 4; bf16 and
+    fp32; empty, one-block and ragged histories)."""
+    for dtype, hq, hkv, bs in (("bf16", 8, 2, 16), ("f32", 4, 4, 4), ("bf16", 6, 3, 4)):
+        w = _rand_workload(seed, dtype=dtype, num_seqs=5, len_lo=0, len_hi=37, hq=hq, hkv=hkv,
+                           bs=bs, num_blocks=64)
+        lens = to_np(w.context_lens).copy()
+        lens[1], lens[3] = 0, bs                     # an empty and a one-block history
+        full = oracle_decode(w, context_lens=torch.as_tensor(lens))
+        q, kp, vp, bt = to_np(w.q), to_np(w.k_cache), to_np(w.v_cache), to_np(w.block_tables)
+        g = w.group
+        for i in range(w.num_seqs):
+            for h in range(w.num_kv_heads):
+                one = paged.decode_one_head(q[i, h * g:(h + 1) * g], kp, vp, bt[i], int(lens[i]),
+                                            h, w.scale, **oracle_args(w))
+                assert np.array_equal(one, full[i, h * g:(h + 1) * g]), (dtype, i, h)
+
+
 ALL_CHECKS = [
     check_worked_address, check_fixed_blocks_16, check_block_growth, check_tail_waste_bound,
     check_layout_contract, check_sdpa_identity_tables, check_closed_forms,
@@ -655,4 +718,5 @@ ALL_CHECKS = [
     check_prefix_admission, check_prefix_partial_block_private, check_prefix_eviction,
     check_prefix_in_use_not_evicted, check_prefix_decode_registration,
     check_prefix_collision_safe, check_prefill_causal_sdpa, check_prefill_rows_are_decodes,
+    check_bf16_widening, check_decode_one_head_is_decode_slice,
 ]

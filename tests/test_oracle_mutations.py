@@ -207,6 +207,25 @@ def _admit_registers_partial(self, tokens):
     return seq, hits
 
 
+def _bf16_as_half(bits):
+    return np.asarray(bits).view(np.float16).astype(np.float64)
+
+
+def _bf16_drops_sign(bits):
+    bits = np.asarray(bits)
+    return ((bits & np.uint16(0x7FFF)).astype(np.uint32) << np.uint32(16)).view(
+        np.float32).astype(np.float64)
+
+
+_orig_one_head = paged.decode_one_head
+
+
+def _one_head_drops_newest(q_group, k_pool, v_pool, block_table, context_len, kv_head, scale,
+                           num_kv_heads, block_size, head_dim, dtype):
+    return _orig_one_head(q_group, k_pool, v_pool, block_table, max(int(context_len) - 1, 0),
+                          kv_head, scale, num_kv_heads, block_size, head_dim, dtype)
+
+
 _orig_admit = opc.PrefixCachePool.admit
 _orig_prefill = paged.prefill
 
@@ -273,6 +292,9 @@ MUTATIONS = {
     "prefill_positions_from_start": (paged, "prefill", _prefill_positions_from_start),
     "prefill_excludes_own_token": (paged, "prefill", _prefill_excludes_self),
     "prefill_sees_future": (paged, "prefill", _prefill_no_causal_mask),
+    "bf16_read_as_half": (paged, "bf16_bits_to_f64", _bf16_as_half),
+    "bf16_drops_sign": (paged, "bf16_bits_to_f64", _bf16_drops_sign),
+    "one_head_drops_newest_token": (paged, "decode_one_head", _one_head_drops_newest),
 }
 
 
