@@ -1,6 +1,7 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout|prefill]
+                    [--extra prefix,long,fanout,prefill|none]
 
 A step is one pass of the whole hot path over one batch of synthetic
 requests: ``pa_decode_step``, which makes each request's copy-on-write copy
@@ -11,11 +12,14 @@ at disjoint physical blocks, so the 256 MB Infinity Cache cannot hold the
 working set between steps (every replica holds the same bytes, so every
 replica gives bit-identical outputs; the benchmark checks that).
 
-Prints one JSON line.  ``value`` is KV GB/s: algorithmic bytes of a step
-(distinct KV bytes read by decode + q/out/table/length bytes + the KV write
-and copy bytes) per second.  ``roofline`` is for the decode call, timed on
-its own with HIP events on the stream it runs on.  ``cpu_baseline`` times
-the CPU oracle on the same workload (first requests until ~10 s of work).
+Prints one JSON line for the headline workload (``--workload``, GQA decode
+by default).  ``value`` is KV GB/s: algorithmic bytes of a step (distinct
+KV bytes read by decode + q/out/table/length bytes + the KV write and copy
+bytes) per second.  ``roofline`` is for the decode call, timed on its own
+with HIP events on the stream it runs on.  ``cpu_baseline`` times the CPU
+oracle on the same workload (first requests until ~10 s of work).  The
+same line carries ``workloads``: every other workload (``--extra``),
+measured the same way in the same run, each with a shorter oracle sample.
 """
 
 from __future__ import annotations
@@ -103,18 +107,25 @@ def step_extra_bytes(w) -> int:
     return write + copy
 
 
+def host(t):
+    """A host numpy copy of a tensor; bf16 as its raw uint16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def host_cores() -> dict:
+    """The host cores this process may run on, and the BLAS threads numpy uses."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - reporting only
+        blas = None
+    return {"cores": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
 def cpu_baseline(w, budget_s: float = 10.0) -> dict:
     """The CPU oracle as it stands, on the first requests of the workload."""
     from oracle import paged
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - reporting only
-        threads = 1
-
-    def host(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     bt = host(w.block_tables)
     lens = host(w.context_lens)
@@ -153,7 +164,7 @@ def cpu_baseline(w, budget_s: float = 10.0) -> dict:
         done += n
         total += n
     dt = time.perf_counter() - t0
-    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", **host_cores(), "kind": "oracle",
             "sample": f"{total} request decodes ({total / w.num_seqs:.2f} passes over the "
                       f"{w.num_seqs} requests of {w.name}, in chunks of "
                       f"{max(1, w.num_seqs // 8)}): copy/write for those requests then fp64 "
@@ -204,15 +215,6 @@ def prefill_flops(w) -> int:
 def cpu_baseline_prefill(w, budget_s: float = 10.0) -> dict:
     """The CPU oracle's prefill on the first query rows of the first request."""
     from oracle import paged
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - reporting only
-        threads = 1
-
-    def host(t):
-        t = t.detach().cpu().contiguous()
-        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
     bt = host(w.block_tables[:1])
     L = int(w.context_lens[0])
@@ -235,20 +237,140 @@ def cpu_baseline_prefill(w, budget_s: float = 10.0) -> dict:
         flops += 4 * w.head_dim * w.num_q_heads * sum(L - n + j + 1 for j in range(done, done + k))
         done += k
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **host_cores(), "kind": "oracle",
             "sample": f"first {done} of {n} query rows of request 0 (context {L}), fp64, {dt:.2f} s",
             "seconds": dt}
 
 
-def run_prefill(args, dev, copy_gbs) -> int:
-    """``--workload prefill``: a step writes each request's new chunk of K/V
-    (pa_write_kv) and runs pa_prefill for the chunk's queries."""
+def launch_flags(name: str, w, no_group: bool = False, no_runs: bool = False,
+                 stream: str = "auto") -> dict:
+    """The decode flags a workload is timed with.
+
+    Sharers are consecutive requests: decode them together (each shared block
+    is then read once per group) and stream K/V.  One prefix shared by the
+    whole batch: shared partitions decoded once per chunk of requests.
+    """
+    group_shared = w.shared_blocks is not None and not no_group
+    prefix_runs = group_shared and WORKLOADS[name].get("runs", False) and not no_runs
+    stream_kv = {"on": True, "off": False}.get(stream, w.shared_blocks is None or group_shared)
+    return dict(stream_kv=stream_kv, group_shared=group_shared, prefix_runs=prefix_runs)
+
+
+def cow_sources(w, table):
+    """Per request, the source block of the copy-on-write copy into the block
+    that holds its newest position (-1 = none), from the workload's pairs;
+    None when the workload has no pairs."""
+    if w.cow_pairs is None:
+        return None
+    by_dst = {int(d): int(s_) for s_, d in w.cow_pairs.cpu().numpy()}
+    bt, lens = table.cpu().numpy(), w.context_lens.cpu().numpy()
+    src = [by_dst.get(int(bt[i, (int(lens[i]) - 1) // w.block_size]), -1) if int(lens[i]) else -1
+           for i in range(w.num_seqs)]
+    if sum(x >= 0 for x in src) != w.cow_pairs.shape[0]:
+        raise ValueError("copy-on-write pairs do not map one per request")
+    return torch.as_tensor(src, dtype=torch.int32, device=w.q.device)
+
+
+def time_calls(fn, iters: int, reps: int, dev) -> float:
+    """Mean microseconds of ``fn(r)`` over ``iters`` back-to-back calls (r
+    cycling over the replicas), from HIP events on the stream the library
+    launches on (torch's current stream)."""
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(iters):
+        fn(i % reps)
+    ev1.record(stream)
+    ev1.synchronize()
+    return ev0.elapsed_time(ev1) * 1e3 / iters
+
+
+def time_steps(fn, steps: int, reps: int) -> float:
+    """Milliseconds per step by the host clock, synchronised on both sides."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i % reps)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def measure_decode(name: str, args, dev, replicas: int, partition: int, cpu_budget: float,
+                   no_group=False, no_runs=False, stream="auto") -> dict:
+    """Generate one decode workload, time its step and its decode call."""
+    cfg = WORKLOADS[name]
+    log(f"generating {name}")
+    w = cfg["make"](device=dev, poison=False)
+    if w.new_k is None:
+        inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    reps = replicas or cfg["replicas"]
+    tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
+    # every request appends one token at its last position, L-1
+    assert torch.equal(w.new_pos, w.context_lens - 1) and torch.equal(
+        w.new_seq, torch.arange(w.num_seqs, dtype=torch.int32, device=dev))
+    max_len = w.max_context_len
+    part = partition or ops.decode_partition_tokens(spec, w.num_seqs, w.num_q_heads, max_len)
+    ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(w.q) for _ in tables]
+    flags = launch_flags(name, w, no_group, no_runs, stream)
+    log(f"{name}: {w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
+        f"workspace {ws_bytes} B, {reps} replicas, flags {flags}")
+    if reps > 1 and w.cow_pairs is not None:
+        raise ValueError("copy-on-write workloads run with one replica")
+    cow_src = cow_sources(w, tables[0])
+
+    def step(r: int) -> None:
+        # one call: each request's copy-on-write copy (fan-out only), the
+        # append of its new token at position L-1, and decode (pa_decode_step)
+        ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src, tables[r],
+                        w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
+                        partition_tokens=part, **flags)
+
+    def decode(r: int) -> None:
+        ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
+                   out=outs[r], workspace=workspace, partition_tokens=part, **flags)
+
+    for i in range(args.warmup):
+        step(i % reps)
+    # every replica holds the same bytes: outputs must agree bit for bit
+    for r in range(reps):
+        step(r)
+    torch.cuda.synchronize()
+    for r in range(1, reps):
+        if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
+            raise RuntimeError(f"{name}: replica outputs differ")
+    log(f"{name}: timing {args.steps} steps")
+    ms = time_steps(step, args.steps, reps)
+    # the dominant kernel: decode alone, HIP events on the stream it runs on
+    dec_us = time_calls(decode, args.kernel_iters, reps, dev)
+    # the step once more by HIP events (its kernel time without host gaps)
+    step_us = time_calls(step, args.kernel_iters, reps, dev)
+    db = decode_bytes(w)
+    extra = step_extra_bytes(w)
+    res = {
+        "name": name, "desc": cfg["desc"], "w": w, "reps": reps, "part": part, "flags": flags,
+        "ms_per_step": ms, "decode_us": dec_us, "step_event_us": step_us, "bytes": db,
+        "step_bytes": db["unique"] + extra, "step_bytes_logical": db["logical"] + extra,
+        "traffic": measured_traffic(name, part, flags["stream_kv"]),
+    }
+    if cpu_budget > 0:
+        log(f"{name}: timing the CPU oracle ({cpu_budget:.0f} s budget)")
+        res["cpu_baseline"] = cpu_baseline(w, cpu_budget)
+    del outs, workspace, tables
+    return res
+
+
+def measure_prefill(args, dev, replicas: int, partition: int, cpu_budget: float) -> dict:
+    """A prefill step writes each request's new chunk of K/V (pa_write_kv) and
+    runs pa_prefill for the chunk's queries."""
     cfg = WORKLOADS["prefill"]
     log("generating prefill")
     w = cfg["make"](device=dev, poison=False)
     spec = ops.CacheSpec.of(w)
-    reps = args.replicas or cfg["replicas"]
+    reps = replicas or cfg["replicas"]
     tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
     max_len = w.max_context_len
     qs = w.q_start.cpu().numpy()
@@ -266,13 +388,13 @@ def run_prefill(args, dev, copy_gbs) -> int:
     gen.manual_seed(77)
     k_new = torch.randn((total_q, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(w.k_cache.dtype)
     v_new = torch.randn((total_q, w.num_kv_heads, w.head_dim), generator=gen, device=dev).to(w.k_cache.dtype)
-    part = args.partition
+    part = partition
     need = ops.prefill_workspace_bytes(spec, w.num_seqs, total_q, w.max_q_len, w.num_q_heads,
                                        max_len, part)
     workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(w.q_chunk) for _ in tables]
-    log(f"{w.num_seqs} requests, {total_q} query rows, max len {max_len}, workspace {need} B, "
-        f"{reps} replicas")
+    log(f"prefill: {w.num_seqs} requests, {total_q} query rows, max len {max_len}, "
+        f"workspace {need} B, {reps} replicas")
 
     def attend(r):
         ops.prefill(spec, w.q_chunk, w.q_start, w.k_cache, w.v_cache, tables[r], w.context_lens,
@@ -290,53 +412,121 @@ def run_prefill(args, dev, copy_gbs) -> int:
     torch.cuda.synchronize()
     for r in range(1, reps):
         if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
-            log("replica outputs differ")
-            return 1
-    log(f"timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % reps)
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.kernel_iters):
-        attend(i % reps)
-    ev1.record(stream)
-    ev1.synchronize()
-    us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
+            raise RuntimeError("prefill: replica outputs differ")
+    log(f"prefill: timing {args.steps} steps")
+    ms = time_steps(step, args.steps, reps)
+    us = time_calls(attend, args.kernel_iters, reps, dev)
     flops = prefill_flops(w)
     db = decode_bytes(w)
     e = 2
     qo = 2 * total_q * w.num_q_heads * w.head_dim * e
     write = 2 * 2 * total_q * w.num_kv_heads * w.head_dim * e + 8 * total_q
-    step_bytes = db["kv_unique"] + qo + write
-    tflops = flops / (us * 1e-6) / 1e12
+    res = {"name": "prefill", "desc": cfg["desc"], "w": w, "reps": reps, "part": part,
+           "ms_per_step": ms, "prefill_us": us, "flops": flops, "kv_unique": db["kv_unique"],
+           "step_bytes": db["kv_unique"] + qo + write, "total_q": total_q}
+    if cpu_budget > 0:
+        log(f"prefill: timing the CPU oracle ({cpu_budget:.0f} s budget)")
+        res["cpu_baseline"] = cpu_baseline_prefill(w, cpu_budget)
+    del outs, workspace, tables
+    return res
+
+
+def decode_line(r: dict, args, copy_gbs) -> dict:
+    """The JSON line of a decode workload measured by ``measure_decode``."""
+    w, db, ms = r["w"], r["bytes"], r["ms_per_step"]
+    value = r["step_bytes"] / (ms * 1e-3) / 1e9
+    achieved = db["unique"] / (r["decode_us"] * 1e-6) / 1e9
     line = {
         "metric": METRIC,
-        "value": round(step_bytes / (ms * 1e-3) / 1e9, 2),
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": r["desc"], "name": r["name"], "requests": w.num_seqs,
+                   "max_context_len": w.max_context_len,
+                   "total_context_tokens": int(w.context_lens.sum()),
+                   "replicas": r["reps"], "partition_tokens": r["part"], **r["flags"],
+                   "kv_layout": "one buffer [block][K|V], block_stride 2 blocks"},
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
+        "kv_gbs_logical": round(r["step_bytes_logical"] / (ms * 1e-3) / 1e9, 2),
+        "step_event_us": round(r["step_event_us"], 3),
+        "copy_probe_gbs": None if copy_gbs is None else round(copy_gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": r["traffic"], "kernel": "pa_decode",
+                     "bytes_per_launch": db["unique"], "avg_launch_us": round(r["decode_us"], 3)},
+    }
+    if "cpu_baseline" in r:
+        line["cpu_baseline"] = r["cpu_baseline"]
+    return line
+
+
+def prefill_line(r: dict, args, copy_gbs) -> dict:
+    """The JSON line of the prefill workload measured by ``measure_prefill``."""
+    w, ms, us = r["w"], r["ms_per_step"], r["prefill_us"]
+    tflops = r["flops"] / (us * 1e-6) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(r["step_bytes"] / (ms * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": cfg["desc"], "name": "prefill", "requests": w.num_seqs,
-                   "query_rows": total_q, "max_context_len": max_len, "replicas": reps,
-                   "partition_tokens": part},
-        "tokens_per_s": round(total_q / (ms * 1e-3), 1),
+        "config": {"workload": r["desc"], "name": "prefill", "requests": w.num_seqs,
+                   "query_rows": r["total_q"], "max_context_len": w.max_context_len,
+                   "replicas": r["reps"], "partition_tokens": r["part"]},
+        "tokens_per_s": round(r["total_q"] / (ms * 1e-3), 1),
         "copy_probe_gbs": None if copy_gbs is None else round(copy_gbs, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel": "pa_prefill", "flops_per_launch": flops,
-                     "kv_bytes_per_launch": db["kv_unique"], "avg_launch_us": round(us, 3),
-                     "kv_gbs": round(db["kv_unique"] / (us * 1e-6) / 1e9, 2)},
+                     "traffic": None, "kernel": "pa_prefill", "flops_per_launch": r["flops"],
+                     "kv_bytes_per_launch": r["kv_unique"], "avg_launch_us": round(us, 3),
+                     "kv_gbs": round(r["kv_unique"] / (us * 1e-6) / 1e9, 2)},
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline_prefill(w)
-    print(json.dumps(line), flush=True)
-    return 0
+    if "cpu_baseline" in r:
+        line["cpu_baseline"] = r["cpu_baseline"]
+    return line
+
+
+def workload_entry(r: dict) -> dict:
+    """The compact record of one extra workload for the ``workloads`` object."""
+    w, ms = r["w"], r["ms_per_step"]
+    if r["name"] == "prefill":
+        us = r["prefill_us"]
+        tflops = r["flops"] / (us * 1e-6) / 1e12
+        e = {"workload": r["desc"], "prefill_us": round(us, 3), "step_us": round(ms * 1e3, 3),
+             "tflops": round(tflops, 2), "roofline": {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFLOPS,
+                                                      "unit": "TFLOP/s",
+                                                      "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+             "kv_gbs": round(r["kv_unique"] / (us * 1e-6) / 1e9, 2),
+             "query_tokens_per_s": round(r["total_q"] / (ms * 1e-3), 1),
+             "flops_per_launch": r["flops"], "replicas": r["reps"]}
+    else:
+        db, us = r["bytes"], r["decode_us"]
+        uniq = db["unique"] / (us * 1e-6) / 1e9
+        e = {"workload": r["desc"], "requests": w.num_seqs, "decode_us": round(us, 3),
+             "step_us": round(ms * 1e3, 3), "step_event_us": round(r["step_event_us"], 3),
+             "step_over_decode": round(r["step_event_us"] / us, 4),
+             "decode_gbs_unique": round(uniq, 2),
+             "decode_gbs_logical": round(db["logical"] / (us * 1e-6) / 1e9, 2),
+             "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(uniq / HBM_PEAK_GBS, 4), "traffic": r["traffic"]},
+             "step_gbs": round(r["step_bytes"] / (ms * 1e-3) / 1e9, 2),
+             "step_frac": round(r["step_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+             "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
+             "bytes_per_launch": db["unique"], "logical_bytes_per_launch": db["logical"],
+             "partition_tokens": r["part"], "replicas": r["reps"], **r["flags"]}
+    if "cpu_baseline" in r:
+        e["cpu_baseline"] = r["cpu_baseline"]
+    return e
 
 
 def copy_probe(dev, mib: int) -> float:
@@ -363,10 +553,18 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOADS),
+                    help="the headline workload of the JSON line")
+    ap.add_argument("--extra", default="prefix,long,fanout,prefill",
+                    help="comma-separated workloads also measured into the line's 'workloads' "
+                         "object ('none' = only the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")
     ap.add_argument("--partition", type=int, default=0, help="decode partition tokens (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the headline workload")
+    ap.add_argument("--extra-cpu-budget", type=float, default=3.0,
+                    help="seconds of oracle work for each extra workload")
     ap.add_argument("--no-runs", action="store_true",
                     help="shared prefix: no cooperative shared partitions (PA_DECODE_PREFIX_RUNS off)")
     ap.add_argument("--no-group", action="store_true",
@@ -385,130 +583,36 @@ def main() -> int:
         print("bench.py measures one GPU only: the paged decode path here runs on a single "
               "MI355X with no collectives; run it with --gpus 1.", file=sys.stderr, flush=True)
         return 2
+    extra = [] if args.extra in ("", "none") else args.extra.split(",")
+    for e in extra:
+        if e not in WORKLOADS:
+            ap.error(f"unknown workload in --extra: {e}")
+    extra = [e for e in extra if e != args.workload]
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     copy_gbs = copy_probe(dev, args.copy_probe_mib) if args.copy_probe_mib > 0 else None
+    budget = 0.0 if args.no_cpu_baseline else args.cpu_budget
     if args.workload == "prefill":
-        return run_prefill(args, dev, copy_gbs)
-    cfg = WORKLOADS[args.workload]
-    log(f"generating {args.workload}")
-    w = cfg["make"](device=dev, poison=False)
-    if w.new_k is None:
-        inputs.add_step_tokens(w)
-    spec = ops.CacheSpec.of(w)
-    reps = args.replicas or cfg["replicas"]
-    tables = inputs.replicate(w, reps) if reps > 1 else [w.block_tables]
-    # every request appends one token at its last position, L-1
-    assert torch.equal(w.new_pos, w.context_lens - 1) and torch.equal(
-        w.new_seq, torch.arange(w.num_seqs, dtype=torch.int32, device=dev))
-    max_len = w.max_context_len
-    part = args.partition or ops.decode_partition_tokens(spec, w.num_seqs, w.num_q_heads, max_len)
-    ws_bytes = ops.decode_workspace_bytes(spec, w.num_seqs, w.num_q_heads, max_len, part)
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    outs = [torch.empty_like(w.q) for _ in tables]
-    # sharers are consecutive requests: decode them together (each shared
-    # block is then read once per group) and stream K/V
-    group_shared = w.shared_blocks is not None and not args.no_group
-    # one prefix shared by the whole batch: shared partitions decoded once per
-    # chunk of requests (PA_DECODE_PREFIX_RUNS)
-    prefix_runs = group_shared and cfg.get("runs", False) and not args.no_runs
-    stream_kv = {"on": True, "off": False}.get(args.stream_kv,
-                                                w.shared_blocks is None or group_shared)
-    log(f"{w.num_seqs} requests, max len {max_len}, partition {part} tokens, "
-        f"workspace {ws_bytes} B, {reps} replicas")
-
-    cow_src = None
-    if w.cow_pairs is not None:
-        # the step's copy-on-write pairs given per request: the source of the
-        # copy into the block that holds the request's newest position
-        by_dst = {int(d): int(s_) for s_, d in w.cow_pairs.cpu().numpy()}
-        bt0, lens0 = tables[0].cpu().numpy(), w.context_lens.cpu().numpy()
-        src = [by_dst.get(int(bt0[i, (int(lens0[i]) - 1) // w.block_size]), -1)
-               for i in range(w.num_seqs)]
-        if reps > 1 or sum(x >= 0 for x in src) != w.cow_pairs.shape[0]:
-            log("copy-on-write pairs do not map one per request")
-            return 1
-        cow_src = torch.as_tensor(src, dtype=torch.int32, device=dev)
-
-    def step(r: int) -> None:
-        # one call: each request's copy-on-write copy (fan-out only), the
-        # append of its new token at position L-1, and decode (pa_decode_step)
-        ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src, tables[r],
-                        w.context_lens, max_len, w.scale, out=outs[r], workspace=workspace,
-                        partition_tokens=part, stream_kv=stream_kv, group_shared=group_shared,
-                        prefix_runs=prefix_runs)
-
-    for i in range(args.warmup):
-        step(i % reps)
-    torch.cuda.synchronize()
-    # every replica holds the same bytes: outputs must agree bit for bit
-    for r in range(reps):
-        step(r)
-    torch.cuda.synchronize()
-    for r in range(1, reps):
-        if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
-            log("replica outputs differ")
-            return 1
-
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i % reps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-
-    # the dominant kernel: decode alone, HIP events on the stream it runs on
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(args.kernel_iters):
-        r = i % reps
-        ops.decode(spec, w.q, w.k_cache, w.v_cache, tables[r], w.context_lens, max_len, w.scale,
-                   out=outs[r], workspace=workspace, partition_tokens=part, stream_kv=stream_kv,
-                   group_shared=group_shared, prefix_runs=prefix_runs)
-    ev1.record(stream)
-    ev1.synchronize()
-    dec_us = ev0.elapsed_time(ev1) * 1e3 / args.kernel_iters
-
-    db = decode_bytes(w)
-    step_bytes = db["unique"] + step_extra_bytes(w)
-    value = step_bytes / (ms * 1e-3) / 1e9
-    achieved = db["unique"] / (dec_us * 1e-6) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": cfg["desc"], "name": args.workload, "requests": w.num_seqs,
-                   "max_context_len": max_len, "total_context_tokens": int(w.context_lens.sum()),
-                   "replicas": reps, "partition_tokens": part, "stream_kv": stream_kv,
-                   "group_shared": group_shared, "prefix_runs": prefix_runs,
-                   "kv_layout": "one buffer [block][K|V], block_stride 2 blocks"},
-        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(w.num_seqs / (ms * 1e-3), 1),
-        "kv_gbs_logical": round((db["logical"] + step_extra_bytes(w)) / (ms * 1e-3) / 1e9, 2),
-        "copy_probe_gbs": None if copy_gbs is None else round(copy_gbs, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(args.workload, part, stream_kv),
-                     "kernel": "pa_decode", "bytes_per_launch": db["unique"],
-                     "avg_launch_us": round(dec_us, 3)},
-    }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle")
-        line["cpu_baseline"] = cpu_baseline(w)
+        r = measure_prefill(args, dev, args.replicas, args.partition, budget)
+        line = prefill_line(r, args, copy_gbs)
+    else:
+        r = measure_decode(args.workload, args, dev, args.replicas, args.partition, budget,
+                           args.no_group, args.no_runs, args.stream_kv)
+        line = decode_line(r, args, copy_gbs)
+    del r
+    torch.cuda.empty_cache()
+    if extra:
+        line["workloads"] = {}
+        ebudget = 0.0 if args.no_cpu_baseline else args.extra_cpu_budget
+        for name in extra:
+            if name == "prefill":
+                r = measure_prefill(args, dev, 0, 0, ebudget)
+            else:
+                r = measure_decode(name, args, dev, 0, 0, ebudget)
+            line["workloads"][name] = workload_entry(r)
+            del r
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -711,58 +711,61 @@ def test_validate_mode_rejects_bad_indices(monkeypatch):
 
 
 # ----------------------------------------------------------------------------
-# the benchmark workloads at full size: sampled (request, KV head) checks
+# the benchmark workloads at full size, every output row against the oracle
 # ----------------------------------------------------------------------------
 
-def oracle_one_head(w, seq, h, k_cache, v_cache):
-    """Oracle decode of one (request, KV head), from host copies of its blocks only."""
-    L = int(w.context_lens[seq])
-    nb = -(-L // w.block_size)
-    table = w.block_tables[seq, :nb].long()
-    tile = w.block_size * w.head_dim
-    kc = k_cache[table].view(nb, w.num_kv_heads, tile)[:, h].contiguous()
-    vc = v_cache[table].view(nb, w.num_kv_heads, tile)[:, h].contiguous()
-    g = w.group
-    qg = w.q[seq, h * g:(h + 1) * g]
-    return paged.decode_one_head(to_np(qg), to_np(kc), to_np(vc), np.arange(nb), L, 0, w.scale,
-                                 1, w.block_size, w.head_dim, w.dtype)
-
-
 @pytest.mark.parametrize("name", ["gqa", "prefix", "long", "fanout"])
-def test_full_size_sampled(name):
+def test_full_size_step(name):
+    """The benchmark's step at full size, launched as bench.py launches it
+    (pa_decode_step with its flags and automatic partition; the fan-out
+    workload with its copy-on-write sources): the whole pool after the step
+    equals the oracle's copies + writes byte for byte (NaN-poisoned free
+    blocks included), and every (request, query head) row of the output
+    matches the oracle's decode over that pool, one request at a time."""
+    import bench
     say(f"full-size {name}: generate")
     w = inputs.PRESETS[name](device=DEV, poison=True)
+    if w.new_k is None:
+        inputs.add_step_tokens(w)
     spec = ops.CacheSpec.of(w)
-    if name == "fanout":
-        say("full-size fanout: copy + slots + write")
-        ops.copy_blocks(spec, w.k_cache, w.v_cache, w.cow_pairs)
-        slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
-        ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
-        want_slots = paged.slot_mapping(to_np(w.block_tables), to_np(w.new_seq),
-                                        to_np(w.new_pos), w.block_size)
-        assert np.array_equal(slots.cpu().numpy(), want_slots)
-    say(f"full-size {name}: decode (auto partition)")
-    out = run_decode(w)
-    # the flags the benchmark decodes this workload with: the same bits
-    flags = {"gqa": dict(stream_kv=True), "long": dict(stream_kv=True),
-             "prefix": dict(stream_kv=True, group_shared=True, prefix_runs=True),
-             "fanout": dict(stream_kv=True, group_shared=True)}[name]
-    say(f"full-size {name}: decode with {sorted(flags)}")
-    assert same_bits(run_decode(w, **flags), out)
+    flags = bench.launch_flags(name, w)
+    cow_src = bench.cow_sources(w, w.block_tables)
+    kp0, vp0 = to_np(w.k_cache), to_np(w.v_cache)
+    say(f"full-size {name}: pa_decode_step with {flags}")
+    out = ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow_src,
+                          w.block_tables, w.context_lens, w.max_context_len, w.scale, **flags)
     torch.cuda.synchronize()
+    say(f"full-size {name}: oracle copies + writes, whole pool compared")
+    bt, lens = to_np(w.block_tables), to_np(w.context_lens)
+    if w.cow_pairs is not None:
+        assert int((cow_src >= 0).sum()) == w.cow_pairs.shape[0]
+        kp0, vp0 = paged.copy_blocks(kp0, vp0, to_np(w.cow_pairs))
+    slots = paged.slot_mapping(bt, to_np(w.new_seq), to_np(w.new_pos), w.block_size)
+    kp, vp = paged.write_kv(kp0, vp0, to_np(w.new_k), to_np(w.new_v), slots, **oracle_args(w))
+    del kp0, vp0
+    gk, gv = to_np(w.k_cache), to_np(w.v_cache)
+    assert np.array_equal(gk.view(np.uint16), kp.view(np.uint16)), "K pool differs"
+    assert np.array_equal(gv.view(np.uint16), vp.view(np.uint16)), "V pool differs"
+    del gk, gv
+    say(f"full-size {name}: pa_decode (the timed call) and the automatic flags, same bits")
+    again = run_decode(w, **flags)
+    plain = run_decode(w)
+    assert same_bits(again, out) and same_bits(plain, out)
     out_np = to_np(out)
-    assert not np.isnan(paged.to_f64(out_np, w.dtype)).any()
-    rng = np.random.default_rng(70)
-    seqs = sorted(set(rng.integers(0, w.num_seqs, size=3).tolist()) |
-                  {int(torch.argmax(w.context_lens))})
-    for seq in seqs:
-        h = int(rng.integers(0, w.num_kv_heads))
-        ref = oracle_one_head(w, seq, h, w.k_cache, w.v_cache)
-        g = w.group
-        got = paged.to_f64(out_np[seq, h * g:(h + 1) * g], w.dtype)
+    q = to_np(w.q)
+    worst = 0.0
+    for i in range(w.num_seqs):
+        if i % 64 == 0:
+            say(f"full-size {name}: oracle rows of requests {i}..{min(i + 64, w.num_seqs) - 1}")
+        ref = paged.decode(q[i:i + 1], kp, vp, bt[i:i + 1], lens[i:i + 1], w.scale,
+                           **oracle_args(w))
+        got = paged.to_f64(out_np[i:i + 1], w.dtype)
+        assert np.isfinite(got).all(), f"{name} request {i}: non-finite output"
         err = float(np.max(np.abs(got - ref)))
-        assert err <= BF16_TOL, f"{name} seq={seq} h={h}: err {err}"
-    del w, out
+        assert err <= BF16_TOL, f"{name} request {i}: max abs err {err}"
+        worst = max(worst, err)
+    say(f"full-size {name}: {w.num_seqs} requests x {w.num_q_heads} heads, max err {worst:.3e}")
+    del w, out, again, plain
     torch.cuda.empty_cache()
 
 
