@@ -29,7 +29,8 @@
  *    synchronises unless PA_VALIDATE=1 is set in the environment (below).
  *  - The caller owns all memory.  The library allocates no device memory,
  *    keeps no pointer after a call returns and holds no global mutable state
- *    except a thread-local error message.
+ *    except a thread-local error message -- and, for pa_decode_step_noalloc
+ *    only, one static device array per GPU (see there).
  *  - Return value: PA_OK (0) or a pa_status_t error.  On error nothing was
  *    enqueued and pa_last_error() describes the problem.  Device-side
  *    contract violations (a block id outside [0, num_blocks), a context
@@ -344,6 +345,33 @@ int pa_decode_step(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const
                    int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_context_len,
                    float scale, void* out, void* workspace, size_t workspace_bytes,
                    int32_t partition_tokens, uint32_t flags, void* stream);
+
+/*
+ * pa_decode_step_noalloc -- pa_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, results and errors as pa_decode_step, minus workspace and
+ * workspace_bytes.  The split-K partials go to a static device array inside
+ * the library (PA_DECODE_NOALLOC_MAX_BYTES bytes on every GPU the library
+ * runs on, held from module load until the process ends).  The call itself
+ * allocates nothing; its first call on a device looks up that device's
+ * address of the array.
+ *   - A call whose partials need more than PA_DECODE_NOALLOC_MAX_BYTES (what
+ *     pa_decode_workspace_bytes reports for the same shape and partition)
+ *     returns PA_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on one GPU shares that GPU's array, and it keeps the last
+ *     call's contents (the kernels need no cleared memory).  Calls that
+ *     overlap on one GPU (different streams, or threads without ordering)
+ *     race on it: serialise them.
+ */
+#define PA_DECODE_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int pa_decode_step_noalloc(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int32_t* cow_src,
+                           const void* q, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           void* out, int32_t partition_tokens, uint32_t flags, void* stream);
 
 /*
  * pa_prefill -- several new query tokens per request against the paged

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <unordered_set>
 #include <vector>
@@ -211,6 +212,40 @@ int prefill_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t max_q_
     int64_t p = ceil_div(ceil_div(whole, splits), 16) * 16;
     p = std::max<int64_t>(std::min<int64_t>(p, whole), std::min<int64_t>(whole, kMinAutoPartitionTokens));
     *out = static_cast<int32_t>(std::min<int64_t>(p, kMaxPrefillPartitionTokens));
+    return PA_OK;
+}
+
+// Scratch for pa_decode_step_noalloc: the split-K partials live in this
+// file-scope device array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy from module load until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host
+// that name is only a stand-in for the symbol); it passes the device address
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kNoallocScratchBytes = PA_DECODE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call
+// made with that device current.
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PA_ERR_UNSUPPORTED, "device %d outside [0, %d)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
     return PA_OK;
 }
 
@@ -628,6 +663,34 @@ int pa_decode_step(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const
                        block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
                        max_context_len, scale, out, workspace, workspace_bytes, partition_tokens,
                        flags, stream);
+}
+
+int pa_decode_step_noalloc(const pa_cache_desc_t* c, void* k_cache, void* v_cache,
+                           const void* k_new, const void* v_new, const int32_t* cow_src,
+                           const void* q, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                           void* out, int32_t partition_tokens, uint32_t flags, void* stream) {
+    int st = check_desc(c);
+    if (st) return st;
+    if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
+    if (num_seqs > 0 && (!k_new || !v_new))
+        return fail(PA_ERR_NULL, "pa_decode_step_noalloc: k_new and v_new are required");
+    int32_t part = 0;
+    if ((st = resolve_partition(c, num_seqs, num_q_heads, max_context_len, partition_tokens, &part)))
+        return st;
+    const size_t need = workspace_bytes(c, num_seqs, num_q_heads, max_context_len, part);
+    if (need > kNoallocScratchBytes)
+        return fail(PA_ERR_WORKSPACE,
+                    "pa_decode_step_noalloc: this call needs %zu bytes of split-K partials; the "
+                    "static scratch holds %zu (use pa_decode_step with a workspace)",
+                    need, kNoallocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0 && (st = noalloc_scratch(&ws))) return st;
+    return decode_impl("pa_decode_step_noalloc", c, k_cache, v_cache, k_new, v_new, cow_src, q,
+                       block_tables, context_lens, num_seqs, num_q_heads, max_blocks_per_seq,
+                       max_context_len, scale, out, ws, need ? kNoallocScratchBytes : 0,
+                       partition_tokens, flags, stream);
 }
 
 }  // extern "C"

@@ -126,6 +126,9 @@ _SIGNATURES = {
     "pa_decode_step": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _P, _P,
                                       _I32, _I32, _I32, _I32, ctypes.c_float, _P, _P,
                                       ctypes.c_size_t, _I32, ctypes.c_uint32, _P]),
+    "pa_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P,
+                                              _P, _P, _I32, _I32, _I32, _I32, ctypes.c_float, _P,
+                                              _I32, ctypes.c_uint32, _P]),
     "pa_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc), _I32, _I32, _I32,
                                                      _I32, _I32, _I32]),
     "pa_prefill": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _P, _P, _P, _P, _P, _P, _I32, _I32,
@@ -330,6 +333,8 @@ def _decode_args(spec, q, k_cache, v_cache, block_tables, context_lens, max_cont
     _need(out, "out", spec.torch_dtype, dev)
     if out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    if workspace is False:                     # the caller wants none allocated
+        return dev, s, hq, out, None, 0
     if workspace is None:
         workspace = decode_workspace(spec, s, hq, max_context_len, partition_tokens, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -420,6 +425,39 @@ def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, blo
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
         _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
         max_context_len, float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
+        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
+    return out
+
+
+# the static scratch of pa_decode_step_noalloc (PA_DECODE_NOALLOC_MAX_BYTES in pa.h)
+NOALLOC_MAX_BYTES = 64 << 20
+
+
+def decode_step_noalloc(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src,
+                        block_tables, context_lens, max_context_len: int, scale: float, out,
+                        partition_tokens: int = 0, stream_kv: bool = False,
+                        group_shared: bool = False, prefix_runs: bool = False):
+    """``pa_decode_step_noalloc``: ``decode_step`` with the split-K partials
+    in the library's static scratch instead of a workspace.  ``out`` must be
+    given (nothing is allocated here either)."""
+    if out is None:
+        raise ValueError("decode_step_noalloc needs a preallocated out")
+    dev, s, hq, out, _, _ = _decode_args(spec, q, k_cache, v_cache, block_tables, context_lens,
+                                         max_context_len, out, False, partition_tokens)
+    _need(k_new, "k_new", spec.torch_dtype, dev)
+    _need(v_new, "v_new", spec.torch_dtype, dev)
+    if cow_src is not None:
+        _need(cow_src, "cow_src", torch.int32, dev)
+        if cow_src.numel() != s:
+            raise ValueError("cow_src must be [num_seqs]")
+    per = s * spec.num_kv_heads * spec.head_dim
+    if k_new.numel() != per or v_new.numel() != per:
+        raise ValueError("k_new/v_new must be [num_seqs, Hkv, head_dim]")
+    d = spec.desc()
+    _check("pa_decode_step_noalloc", lib().pa_decode_step_noalloc(
+        ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
+        _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
+        max_context_len, float(scale), _ptr(out), partition_tokens,
         _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
     return out
 
