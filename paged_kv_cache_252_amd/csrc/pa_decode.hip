@@ -890,8 +890,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int h = blockIdx.x;
     const int chunk = blockIdx.y;
     const int per = FG / group;                      // members per wave in a shared partition
-    const int slot = blockIdx.z / max_parts;         // slot-major: slot 0 is dispatched first
-    const int part = blockIdx.z - slot * max_parts;
+    // Dispatch order (z is the slowest grid index): first slot 0 of every
+    // partition (the shared work, and members 0..3 of unshared partitions),
+    // then the other slots from the last partition down.  A chunk's prefix
+    // is shared at its start, so the later partitions are the ones whose
+    // other slots have members to decode; the slots of shared partitions
+    // (which exit after the check) come last and no longer hold back the
+    // private waves from the resident set.
+    int slot = 0, part = static_cast<int>(blockIdx.z);
+    if (part >= max_parts) {
+        const int k = part - max_parts;
+        part = max_parts - 1 - k / (per - 1);
+        slot = 1 + k % (per - 1);
+    }
     const int wave = static_cast<int>(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int row = lane & 15;
