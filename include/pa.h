@@ -109,9 +109,11 @@ typedef enum {
 /* Shape of one layer's paged KV cache. */
 typedef struct {
     int64_t num_blocks;    /* physical blocks in each of the K and V buffers, >= 1 */
-    int32_t block_size;    /* token positions per block: 1..256 (16 on the fast path) */
+    int32_t block_size;    /* token positions per block: 1..256 (MFMA decode: 8, 16, 32
+                              or 64; the grouped, prefix-run and prefill kernels: 16) */
     int32_t num_kv_heads;  /* Hkv >= 1 */
-    int32_t head_dim;      /* D: 16, 32, 64, 128 or 256 (128 on the fast path) */
+    int32_t head_dim;      /* D: 16, 32, 64, 128 or 256 (MFMA decode, bf16: 64, 128 or
+                              256; the grouped, prefix-run and prefill kernels: 128) */
     int32_t dtype;         /* pa_dtype_t of K, V, q, out, k_new, v_new */
     int64_t block_stride;  /* elements from block b to block b+1 in k_cache and in v_cache;
                               0 means dense (Hkv * block_size * head_dim) */

@@ -45,9 +45,20 @@ namespace {
 #ifndef PA_FAST_NBUF
 #define PA_FAST_NBUF 2           // tiles in the load ring of the fast path
 #endif
+#ifndef PA_FAST_NBUF_D64
+#define PA_FAST_NBUF_D64 3       // ... at head_dim 64, whose tiles are half as large
+#endif
 
 constexpr int kMaxWgParts = 8;   // partitions merged inside one workgroup
 constexpr size_t kMaxWgLds = 32768;
+
+// Load-ring depth of the fast path at head_dim d.
+constexpr int fast_nbuf(int d) { return d <= 64 ? PA_FAST_NBUF_D64 : PA_FAST_NBUF; }
+
+// Waves of a workgroup-merge workgroup of the fast path at head_dim d: at 256
+// a wave holds twice the tiles and accumulators, more than the 256 registers
+// each of eight waves may have, so its workgroups take at most four.
+constexpr int fast_wg_parts(int d) { return d > FD ? 4 : kMaxWgParts; }
 
 // ============================================================================
 // Fast path
@@ -74,38 +85,42 @@ struct FastArgs {
 };
 
 // Merge of the partitions 0..nparts-1 of one query row whose partial states
-// sit in LDS at base + p * pstride (acc[FD], then m and l), with the merge
+// sit in LDS at base + p * pstride (acc[D], then m and l), with the merge
 // kernel's formula: global maximum first, then fused multiply-adds in
-// partition order, one division.  Lane quad writes dims 32*quad..+31 of the
-// bf16 output row o.
+// partition order, one division.  Lane quad writes dims D/4*quad..+D/4-1 of
+// the bf16 output row o.
+template <int D>
 __device__ __forceinline__ void merge_lds_row(const float* base, int pstride, int nparts, int quad,
                                               uint2* o) {
-    float M = base[FD];
-    for (int p = 1; p < nparts; ++p) M = fmaxf(M, base[p * pstride + FD]);
+    constexpr int K = D / 16;                    // float4 chunks per lane
+    float M = base[D];
+    for (int p = 1; p < nparts; ++p) M = fmaxf(M, base[p * pstride + D]);
     float den = 0.f;
-    f32x4 num[8];
+    f32x4 num[K];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) num[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int p = 0; p < nparts; ++p) {
         const float* src = base + p * pstride;
-        const float w = fast_exp2(src[FD] - M);
+        const float w = fast_exp2(src[D] - M);
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-            num[k] = fma4(*reinterpret_cast<const f32x4*>(src + 32 * quad + 4 * k), w, num[k]);
-        den = __builtin_fmaf(src[FD + 1], w, den);
+        for (int k = 0; k < K; ++k)
+            num[k] = fma4(*reinterpret_cast<const f32x4*>(src + (D / 4) * quad + 4 * k), w, num[k]);
+        den = __builtin_fmaf(src[D + 1], w, den);
     }
     const float inv = 1.f / den;
-    uint2* ob = o + 8 * quad;
+    uint2* ob = o + K * quad;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
+    for (int k = 0; k < K; ++k)
         ob[k] = make_uint2(pack_bf16x2(num[k][0] * inv, num[k][1] * inv),
                            pack_bf16x2(num[k][2] * inv, num[k][3] * inv));
 }
 
 // One wave's item of the fast path: partition `part` of request `seq` for KV
-// head h (the grid and the flags are described at decode_fast_kernel).
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS>
+// head h (the grid and the flags are described at decode_fast_kernel); head_dim D.
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, int D>
 __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const int seq, const int part) {
+    constexpr int KC = D / 32;                        // K chunks (and q chunks) per lane
+    constexpr int VJ = D / 16;                        // V operands / accumulator chunks per lane
     const __bf16* __restrict__ k_cache = a.k_cache;
     const __bf16* __restrict__ v_cache = a.v_cache;
     const __bf16* __restrict__ q = a.q;
@@ -133,14 +148,14 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     const int hq = h * group + row;
     const bool row_ok = row < group;
     auto out_row = [&]() {
-        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * FD);
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * D);
     };
 
     if (!WGM && tok0 >= L) {
         if (L == 0 && part == 0 && row_ok) {   // empty history: zero output
             uint2* o = out_row();
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
         }
         return;
     }
@@ -152,13 +167,13 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     const int last_valid = tok1 - (tok0 + (nblk - 1) * FBS);
     const int blk0 = tok0 / BS;
     const int nent = (tok1 - tok0 + BS - 1) / BS;     // 1..64
-    constexpr int HT = BS * FD;                       // elements of one (block, head) tile
+    constexpr int HT = BS * D;                        // elements of one (block, head) region
 
-    SoftmaxState st;
+    SoftmaxStateT<D> st;
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < VJ; ++j) st.acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     float lsum = 0.f;
 
     if (active) {
@@ -169,14 +184,14 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
                               num_blocks);
 
     // Appending: the last partition holds position L-1 at offset o of its
-    // last block.  The four lanes of row o hold that token's 16 key chunks
+    // last block.  The four lanes of row o hold that token's D/8 key chunks
     // (the same chunk order as the K tile); the 16 lanes of quad o/4 hold its
-    // 128 value dims (dim 16*j + row).  They also store them to the cache.
+    // D value dims (dim 16*j + row).  They also store them to the cache.
     const bool append_here = APPEND && part == nparts - 1;
     const int o_new = (L - 1) % FBS;                  // slot within the last tile
     const int ob_new = (L - 1) % BS;                  // slot within the last block
-    bf16x8 fk[4];
-    short fv[8];
+    bf16x8 fk[KC];
+    short fv[VJ];
     // Copy-on-write folded in (blocks of 16): the last block is read from
     // cow_src[seq] and written back whole, new token included, to the
     // request's own block, so the token needs no store of its own.
@@ -189,39 +204,39 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     }
     if constexpr (APPEND) {
         if (append_here) {
-            const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * FD;
+            const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * D;
             const bf16x8* kn = reinterpret_cast<const bf16x8*>(k_new + nrow);
             const short* vn = reinterpret_cast<const short*>(v_new + nrow);
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) fk[s4] = kn[4 * s4 + quad];
+            for (int s4 = 0; s4 < KC; ++s4) fk[s4] = kn[4 * s4 + quad];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) fv[j] = vn[16 * j + row];
+            for (int j = 0; j < VJ; ++j) fv[j] = vn[16 * j + row];
             const int64_t toff = static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, nent - 1)) *
                                      blk_stride + static_cast<int64_t>(h) * HT;
             // the slot's tile inside the block, and its position in that tile
             constexpr int TT = BS >= 16 ? 16 : BS;
-            const int64_t tile_base = toff + static_cast<int64_t>(ob_new / TT) * TT * FD;
+            const int64_t tile_base = toff + static_cast<int64_t>(ob_new / TT) * TT * D;
             const int pt = ob_new % TT;
             if (cow_phys < 0 && row == o_new) {
                 bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + tile_base);
 #pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) kd[(4 * s4 + quad) * TT + pt] = fk[s4];
+                for (int s4 = 0; s4 < KC; ++s4) kd[(4 * s4 + quad) * TT + pt] = fk[s4];
             }
             if (cow_phys < 0 && quad == o_new / 4) {
                 short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + tile_base);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) vd[(16 * j + row) * TT + pt] = fv[j];
+                for (int j = 0; j < VJ; ++j) vd[(16 * j + row) * TT + pt] = fv[j];
             }
         }
     }
 
     // Query rows of this KV head as the B operand (rows >= group are zero).
-    bf16x8 qv[4];
+    bf16x8 qv[KC];
     {
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            q + (static_cast<int64_t>(seq) * num_q_heads + (row_ok ? hq : 0)) * FD);
+            q + (static_cast<int64_t>(seq) * num_q_heads + (row_ok ? hq : 0)) * D);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KC; ++s) {
             bf16x8 v = qp[4 * s + quad];
             qv[s] = row_ok ? v : bf16x8{};
         }
@@ -237,11 +252,11 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     // scheduling barriers keep each tile's loads issued ahead of the previous
     // tile's arithmetic; without them the compiler sinks loads next to their
     // first use and every block waits a full memory latency.
-    Tile buf[NBUF];
+    TileT<D> buf[NBUF];
     auto entry_off = [&](int e) {
         return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, e < nent ? e : nent - 1)) * blk_stride;
     };
-    auto load_t = [&](Tile& t, int jj) {     // tile jj (clamped to the last)
+    auto load_t = [&](TileT<D>& t, int jj) {   // tile jj (clamped to the last)
         const int jc = jj < nblk ? jj : nblk - 1;
         if constexpr (BS >= 16) {
             const int64_t o = (BS == 16 && cow_phys >= 0 && jc == nblk - 1)
@@ -264,10 +279,10 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
             if constexpr (APPEND) {
                 if (append_here && j == nblk - 1) {
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4)
+                    for (int s4 = 0; s4 < KC; ++s4)
                         if (row == o_new) buf[u].k[s4] = fk[s4];
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj)
+                    for (int jj = 0; jj < VJ; ++jj)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
@@ -288,16 +303,16 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     }   // active
 
     if constexpr (WGM) {
-        // LDS: [partition][row < group][acc 128 | m | l | pad 2]
+        // LDS: [partition][row < group][acc D | m | l | pad 2]
         extern __shared__ float wg_part[];
-        constexpr int RS = FD + 4;
+        constexpr int RS = D + 4;
         if (active && nparts > 1 && row_ok) {
             float* dst = wg_part + (part * group + row) * RS;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<f32x4*>(dst + 16 * jj + 4 * quad) = st.acc[jj];
+            for (int jj = 0; jj < VJ; ++jj) *reinterpret_cast<f32x4*>(dst + 16 * jj + 4 * quad) = st.acc[jj];
             if (quad == 0) {
-                dst[FD] = st.m;
-                dst[FD + 1] = lsum;
+                dst[D] = st.m;
+                dst[D + 1] = lsum;
             }
         }
         __syncthreads();
@@ -305,14 +320,14 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
         uint2* o = out_row();
         if (L == 0) {                          // empty history: zero output
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
             return;
         }
         if (nparts > 1) {
             // merge partitions 0..nparts-1 in order (the merge kernel's formula:
             // global max first, then fused multiply-adds in partition order);
             // lane: row, dims 32*quad..+31
-            merge_lds_row(wg_part + row * RS, group * RS, nparts, quad, o);
+            merge_lds_row<D>(wg_part + row * RS, group * RS, nparts, quad, o);
             return;
         }
         // a single partition: wave 0 holds the whole result (falls through)
@@ -323,7 +338,7 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
         const float inv = 1.f / lsum;
         uint2* o = out_row();
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
+        for (int jj = 0; jj < VJ; ++jj)
             o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
                                           pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
         return;
@@ -331,9 +346,9 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 
     if (!row_ok) return;
     const int64_t pidx = (static_cast<int64_t>(seq) * num_q_heads + hq) * max_parts + part;
-    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+    f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * D);
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
+    for (int jj = 0; jj < VJ; ++jj) acc_out[4 * jj + quad] = st.acc[jj];
     if (quad == 0) {
         ws_m[pidx] = st.m;
         ws_l[pidx] = lsum;
@@ -344,7 +359,7 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // the wave of the request's last partition stores k_new/v_new into the cache
 // and uses them in place of whatever its load of that slot returned.
 // WGM: the partitions of one (request, KV head) are the waves of one
-// workgroup (wave w = partition w, at most kMaxWgParts of them) and are
+// workgroup (wave w = partition w, at most fast_wg_parts(D) of them) and are
 // merged through LDS after a workgroup barrier, instead of by the merge
 // kernel.  Waves without a partition wait at the barrier.
 //
@@ -355,8 +370,8 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // once: with more items than that, a one-wave-per-item grid would leave its
 // last items running as a tail on a mostly idle device.  Each item is
 // computed exactly as in the plain grid, so the bits are the same.
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST>
-__global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kernel(
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST, int D>
+__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -379,7 +394,7 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
                     num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
                     scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src};
   auto body = [&](const int seq, const int part) {
-      fast_item<NBUF, NT, APPEND, WGM, BS>(fa, h, seq, part);
+      fast_item<NBUF, NT, APPEND, WGM, BS, D>(fa, h, seq, part);
   };
 
     if constexpr (PERSIST) {
@@ -408,9 +423,9 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_fast_kerne
                 zm &= zm - 1;
                 if (row < group) {
                     uint2* o = reinterpret_cast<uint2*>(
-                        out + (static_cast<int64_t>(seq) * num_q_heads + h * group + row) * FD);
+                        out + (static_cast<int64_t>(seq) * num_q_heads + h * group + row) * D);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+                    for (int j = 0; j < D / 16; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
                 }
             }
         }
@@ -814,7 +829,7 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_ke
         __syncthreads();
         if (part != 0 || !mine) return;
         if (my_L > 0 && my_nparts > 1) {
-            merge_lds_row(wg_part + row * RS, FG * RS, my_nparts, quad,
+            merge_lds_row<FD>(wg_part + row * RS, FG * RS, my_nparts, quad,
                           reinterpret_cast<uint2*>(out + (static_cast<int64_t>(my_seq) * num_q_heads + hq) * FD));
             if (quad == 0) ws_l[(static_cast<int64_t>(my_seq) * num_q_heads + hq) * max_parts] = -1.f;
             return;
@@ -1019,7 +1034,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
                       num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
                       scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, nullptr};
-    fast_item<PA_FAST_NBUF, NT, APPEND, false, FBS>(fa, h, seq0 + m, part);
+    fast_item<PA_FAST_NBUF, NT, APPEND, false, FBS, FD>(fa, h, seq0 + m, part);
 }
 
 // ============================================================================
@@ -1329,13 +1344,14 @@ int workgroups_per_cu(const void* kernel) {
     return per_cu;
 }
 
-template <bool NT, bool APPEND, int BS>
+template <bool NT, bool APPEND, int BS, int D>
 int launch_fast(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
-    const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (FD + 4) * sizeof(float);
-    if (a.max_parts >= 2 && a.max_parts <= kMaxWgParts && wg_lds <= kMaxWgLds) {
+    const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (D + 4) * sizeof(float);
+    constexpr int NB = fast_nbuf(D);
+    if (a.max_parts >= 2 && a.max_parts <= fast_wg_parts(D) && wg_lds <= kMaxWgLds) {
         // partitions of a request are the waves of one workgroup, merged in LDS
-        hipLaunchKernelGGL((decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, true, BS, false>),
+        hipLaunchKernelGGL((decode_fast_kernel<NB, NT, APPEND, true, BS, false, D>),
                            dim3(a.num_kv_heads, a.num_seqs, 1), dim3(64 * a.max_parts), wg_lds,
                            a.stream, static_cast<const __bf16*>(a.k_cache),
                            static_cast<const __bf16*>(a.v_cache), static_cast<const __bf16*>(a.q),
@@ -1351,13 +1367,13 @@ int launch_fast(const DecodeArgs& a) {
     // head as fit, each taking every Z-th item (at most 64 requests).
     const int64_t upper = static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.max_parts;
     static const int per_cu = workgroups_per_cu(reinterpret_cast<const void*>(
-        &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, true>));
+        &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D>));
     const int64_t resident = static_cast<int64_t>(per_cu) * device_cu_count();
     const bool persist = a.num_seqs <= 64 && resident >= a.num_kv_heads && upper > resident;
     const dim3 grid = persist ? dim3(a.num_kv_heads, static_cast<unsigned>(std::min<int64_t>(resident / a.num_kv_heads, 65535)), 1)
                               : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
-    auto kernel = persist ? &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, true>
-                          : &decode_fast_kernel<PA_FAST_NBUF, NT, APPEND, false, BS, false>;
+    auto kernel = persist ? &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D>
+                          : &decode_fast_kernel<NB, NT, APPEND, false, BS, false, D>;
     hipLaunchKernelGGL(kernel, grid, dim3(64), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
@@ -1368,8 +1384,13 @@ int launch_fast(const DecodeArgs& a) {
                        a.num_kv_heads, a.cow_src, a.num_seqs);
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
-    return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
-                      a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
+    if constexpr (D == FD)
+        return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                          a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
+    hipLaunchKernelGGL((reduce_kernel<uint16_t, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
+                       a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
+                       a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
+    return check_launch("decode merge");
 }
 
 template <int MAXR, bool NT, bool APPEND>
@@ -1430,10 +1451,19 @@ int launch_cascade(const DecodeArgs& a) {
                       a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
+template <int BS, int D>
+int launch_fast_bsd(const DecodeArgs& a, bool nt) {
+    if (a.k_new) return nt ? launch_fast<true, true, BS, D>(a) : launch_fast<false, true, BS, D>(a);
+    return nt ? launch_fast<true, false, BS, D>(a) : launch_fast<false, false, BS, D>(a);
+}
+
 template <int BS>
 int launch_fast_bs(const DecodeArgs& a, bool nt) {
-    if (a.k_new) return nt ? launch_fast<true, true, BS>(a) : launch_fast<false, true, BS>(a);
-    return nt ? launch_fast<true, false, BS>(a) : launch_fast<false, false, BS>(a);
+    switch (a.head_dim) {
+        case 64: return launch_fast_bsd<BS, 64>(a, nt);
+        case 256: return launch_fast_bsd<BS, 256>(a, nt);
+        default: return launch_fast_bsd<BS, FD>(a, nt);
+    }
 }
 
 template <bool NT, bool APPEND>
@@ -1459,7 +1489,8 @@ int launch_decode(const DecodeArgs& a_in) {
     pa_cache_desc_t c{a_in.num_blocks, a_in.block_size, a_in.num_kv_heads, a_in.head_dim, a_in.dtype,
                       a_in.block_stride};
     DecodeArgs a = a_in;
-    if (a.cow_src != nullptr && a.k_new != nullptr && !(fast_path_ok(&c, a.group) && a.part_tokens % FBS == 0)) {
+    if (a.cow_src != nullptr && a.k_new != nullptr &&
+        !(fast_decode_ok(&c, a.group) && a.block_size == FBS && a.part_tokens % FBS == 0)) {
         // only the block-size-16 MFMA kernels fold the copy in: copy first
         int st = launch_cow_last_block(&c, const_cast<void*>(a.k_cache), const_cast<void*>(a.v_cache),
                                        a.cow_src, a.block_tables, a.context_lens, a.num_seqs,

@@ -45,15 +45,20 @@ __device__ __forceinline__ int clamp_block(int e, int64_t num_blocks) {
 }
 
 
-constexpr int FD = 128;          // head_dim
-constexpr int FBS = 16;          // block_size
-constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile
+constexpr int FD = 128;          // head_dim of the grouped, prefix-run and prefill kernels
+constexpr int FBS = 16;          // positions per tile (block_size 16)
+constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile at head_dim 128
 constexpr int FG = 16;           // query rows of the score MFMA
 
-struct Tile {
-    bf16x8 k[4];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
-    s16x4 v[8];    // V: dim 16*j + l%16, tokens 4*(l/16)..+3 -> A operand of PV j
+// One 16-position tile of head_dim D (a multiple of 32, at most 256) in MFMA
+// operand layout.
+template <int D>
+struct TileT {
+    static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim a multiple of 32, at most 256");
+    bf16x8 k[D / 32];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
+    s16x4 v[D / 16];    // V: dim 16*j + l%16, tokens 4*(l/16)..+3 -> A operand of PV j
 };
+using Tile = TileT<FD>;
 
 // NT: non-temporal loads (streaming hint), for batches without shared blocks.
 template <bool NT, typename V>
@@ -62,27 +67,28 @@ __device__ __forceinline__ V load16(const V* p) {
     else return *p;
 }
 
-template <bool NT>
-__device__ __forceinline__ void load_tile(Tile& t, const __bf16* __restrict__ k_tile,
+template <bool NT, int D>
+__device__ __forceinline__ void load_tile(TileT<D>& t, const __bf16* __restrict__ k_tile,
                                           const __bf16* __restrict__ v_tile, int lane) {
     const bf16x8* kp = reinterpret_cast<const bf16x8*>(k_tile) + lane;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + 64 * s);
+    for (int s = 0; s < D / 32; ++s) t.k[s] = load16<NT>(kp + 64 * s);
     const s16x4* vp = reinterpret_cast<const s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 64 * j);
+    for (int j = 0; j < D / 16; ++j) t.v[j] = load16<NT>(vp + 64 * j);
 }
 
 // The inverse of load_tile: the tile's bytes back to a block (whole lines),
 // with the non-temporal hint (measured: 2.4 us less on the fan-out step).
-__device__ __forceinline__ void store_tile(const Tile& t, __bf16* __restrict__ k_tile,
+template <int D>
+__device__ __forceinline__ void store_tile(const TileT<D>& t, __bf16* __restrict__ k_tile,
                                            __bf16* __restrict__ v_tile, int lane) {
     bf16x8* kp = reinterpret_cast<bf16x8*>(k_tile) + lane;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) __builtin_nontemporal_store(t.k[s], kp + 64 * s);
+    for (int s = 0; s < D / 32; ++s) __builtin_nontemporal_store(t.k[s], kp + 64 * s);
     s16x4* vp = reinterpret_cast<s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) __builtin_nontemporal_store(t.v[j], vp + 64 * j);
+    for (int j = 0; j < D / 16; ++j) __builtin_nontemporal_store(t.v[j], vp + 64 * j);
 }
 
 // The same tile out of blocks of BS tokens: tile `sub` of one block when BS
@@ -90,30 +96,32 @@ __device__ __forceinline__ void store_tile(const Tile& t, __bf16* __restrict__ k
 // BS = 8 (K [D/8][8][8], V [D][8] per head) the tile's first 8 tokens come
 // from block `a`, the next 8 from block `b` (K rows 8..15 and V token groups
 // 2..3).  k_a/v_a, k_b/v_b point at the head's region in blocks a and b.
-template <bool NT, int BS>
-__device__ __forceinline__ void load_tile_bs(Tile& t, const __bf16* __restrict__ k_a,
+template <bool NT, int BS, int D>
+__device__ __forceinline__ void load_tile_bs(TileT<D>& t, const __bf16* __restrict__ k_a,
                                              const __bf16* __restrict__ v_a,
                                              const __bf16* __restrict__ k_b,
                                              const __bf16* __restrict__ v_b, int sub, int lane) {
     const int row = lane & 15, quad = lane >> 4;
     if constexpr (BS >= 16) {                 // tile `sub` of the block: a 16-position tile
-        load_tile<NT>(t, k_a + sub * FTILE, v_a + sub * FTILE, lane);
+        load_tile<NT>(t, k_a + sub * (D * FBS), v_a + sub * (D * FBS), lane);
     } else {
         static_assert(BS == 8, "blocks of 8, 16, 32 or 64 tokens");
         const bf16x8* kp = reinterpret_cast<const bf16x8*>(row < 8 ? k_a : k_b) + (row & 7);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
+        for (int s = 0; s < D / 32; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
         const s16x4* vp = reinterpret_cast<const s16x4*>(quad < 2 ? v_a : v_b) + row * 2 + (quad & 1);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t.v[j] = load16<NT>(vp + 32 * j);
+        for (int j = 0; j < D / 16; ++j) t.v[j] = load16<NT>(vp + 32 * j);
     }
 }
 
-struct SoftmaxState {
-    float m;        // running max of log2-domain scores for query row lane%16
-    float l;        // this lane's share of the running sum
-    f32x4 acc[8];   // output accumulator
+template <int D>
+struct SoftmaxStateT {
+    float m;            // running max of log2-domain scores for query row lane%16
+    float l;            // this lane's share of the running sum
+    f32x4 acc[D / 16];  // output accumulator: dims 16*j + 4*(lane/16) + i of row lane%16
 };
+using SoftmaxState = SoftmaxStateT<FD>;
 
 // Reductions across the four 16-lane rows of the wave with the gfx950 row
 // swaps: permlane16_swap exchanges rows (0,1) and (2,3), permlane32_swap
@@ -162,13 +170,14 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // where the VALU, not memory, bounds the loop.
 constexpr float kLazyMaxLog2 = 8.f;
 
-__device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
-                                                  const bf16x8 (&qv)[4], float scale_log2,
+template <int D>
+__device__ __forceinline__ void consume_tile_rows(SoftmaxStateT<D>& st, TileT<D>& t,
+                                                  const bf16x8 (&qv)[D / 32], float scale_log2,
                                                   int lane, int row_valid, int v_valid,
                                                   bool masked) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
+    for (int k = 0; k < D / 32; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
     const int tok_base = 4 * (lane >> 4);
     float sc[4];
 #pragma unroll
@@ -180,7 +189,7 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
     }
     if (v_valid < FBS) {   // (wave-uniform) values past the history may be stale bytes
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < D / 16; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (tok_base + i >= v_valid) t.v[j][i] = 0;
@@ -192,7 +201,7 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
         st.m = raise ? mx : st.m;
         st.l *= alpha;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st.acc[j] *= alpha;
+        for (int j = 0; j < D / 16; ++j) st.acc[j] *= alpha;
     }
     const bool dead = st.m == -INFINITY;           // nothing visible to this row yet
     float p[4];
@@ -203,7 +212,7 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxState& st, Tile& t,
     const u32x2 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     const s16x4 pb = __builtin_bit_cast(s16x4, pp);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < D / 16; ++j)
         st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
 }
 
@@ -319,8 +328,10 @@ __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile
 
 // One block of 16 tokens seen alike by every row: `valid` of its tokens are
 // visible (16 except in the last block of a request).
-__device__ __forceinline__ void consume_tile(SoftmaxState& st, Tile& t, const bf16x8 (&qv)[4],
-                                             float scale_log2, int lane, int valid) {
+template <int D>
+__device__ __forceinline__ void consume_tile(SoftmaxStateT<D>& st, TileT<D>& t,
+                                             const bf16x8 (&qv)[D / 32], float scale_log2, int lane,
+                                             int valid) {
     consume_tile_rows(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
 }
 

@@ -278,7 +278,7 @@ def test_separate_dense_pools(dtype):
 
 @pytest.mark.parametrize("dtype,d,bs,hq,hkv", [
     ("f32", 16, 4, 2, 2), ("f32", 128, 16, 8, 2), ("f32", 32, 1, 3, 1),
-    ("bf16", 64, 8, 4, 2), ("bf16", 256, 16, 8, 2), ("bf16", 128, 4, 4, 4),
+    ("bf16", 64, 4, 4, 2), ("bf16", 256, 4, 8, 2), ("bf16", 128, 4, 4, 4),
     ("bf16", 128, 16, 40, 2), ("f32", 64, 32, 4, 2), ("bf16", 64, 48, 8, 2),
 ])
 @pytest.mark.parametrize("part", [0, 64])
@@ -390,8 +390,8 @@ def test_fanout_step_end_to_end():
                           to_np(w.k_cache)[w.shared_blocks].view(np.uint16))
 
 
-@pytest.mark.parametrize("shape", ["fast", "fast_g8", "generic_f32", "generic_bf16_d64",
-                                   "grouped", "grouped_g8"])
+@pytest.mark.parametrize("shape", ["fast", "fast_g8", "fast_d64", "fast_d256", "generic_f32",
+                                   "generic_bf16_d64", "grouped", "grouped_g8"])
 @pytest.mark.parametrize("part", [0, 32])
 @pytest.mark.parametrize("stream_kv", [False, True])
 def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
@@ -405,7 +405,9 @@ def test_decode_append_equals_write_then_decode(shape, part, stream_kv):
               grouped=dict(hq=8, hkv=2, d=128, bs=16, dtype="bf16"),
               grouped_g8=dict(hq=16, hkv=2, d=128, bs=16, dtype="bf16"),
               generic_f32=dict(hq=4, hkv=2, d=32, bs=16, dtype="f32"),
-              generic_bf16_d64=dict(hq=4, hkv=2, d=64, bs=8, dtype="bf16"))[shape]
+              fast_d64=dict(hq=8, hkv=2, d=64, bs=16, dtype="bf16"),
+              fast_d256=dict(hq=8, hkv=2, d=256, bs=16, dtype="bf16"),
+              generic_bf16_d64=dict(hq=4, hkv=2, d=64, bs=4, dtype="bf16"))[shape]
     if part % kw["bs"]:
         pytest.skip("partition must be a multiple of the block size")
     w = inputs.paged_random("ap", len(lens), 0, 300, kw["hq"], kw["hkv"], head_dim=kw["d"],
@@ -714,7 +716,7 @@ def test_validate_mode_rejects_bad_indices(monkeypatch):
 # the benchmark workloads at full size, every output row against the oracle
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["gqa", "prefix", "long", "fanout"])
+@pytest.mark.parametrize("name", ["gqa", "prefix", "long", "fanout", "gqa_d64", "gqa_d256"])
 def test_full_size_step(name):
     """The benchmark's step at full size, launched as bench.py launches it
     (pa_decode_step with its flags and automatic partition; the fan-out
@@ -1036,6 +1038,67 @@ def test_fast_path_block_sizes(bs, group):
     assert_close(w, fused, oracle_decode(w), f"bs={bs} append")
 
 
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bs", [8, 16, 64])
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_fast_path_head_dims(d, bs, group):
+    """The MFMA decode at head_dim 64 and 256 (K chunks and V operands per
+    lane scale with D): against the oracle at several partition sizes, the
+    streaming hint giving the same bits, and the folded append equal to
+    write + decode."""
+    hkv = 2
+    lens = [0, 1, 15, 16, 17, 63, 64, 65, 129, 300, 511, 700]
+    w = inputs.paged_random("fhd", len(lens), 0, 700, hkv * group, hkv, head_dim=d, block_size=bs,
+                            num_blocks=-(-700 // bs) * len(lens) + 8, seed=d + bs + group,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    ref = oracle_decode(w)
+    g = max(16, bs)
+    cap = min(64 * bs, 1024)
+    for part in sorted({0, g, 5 * g, cap}):
+        say(f"decode D={d} bs={bs} g={group} part={part}")
+        out = run_decode(w, partition_tokens=part)
+        assert_close(w, out, ref, f"D={d} bs={bs} g={group} part={part}")
+        assert not to_np(out)[0].any()
+        assert same_bits(out, run_decode(w, partition_tokens=part, stream_kv=True))
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    slots = ops.slot_mapping(w.block_size, w.block_tables, w.new_pos, w.new_seq)
+    ops.write_kv(spec, w.k_cache, w.v_cache, w.new_k, w.new_v, slots)
+    sep = run_decode(w, partition_tokens=g)
+    k_sep, v_sep = w.k_cache.clone(), w.v_cache.clone()
+    w.k_cache.copy_(k0)
+    w.v_cache.copy_(v0)
+    fused = ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, w.block_tables,
+                              w.context_lens, w.max_context_len, w.scale, partition_tokens=g)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
+    assert same_bits(fused, sep)
+    assert_close(w, fused, oracle_decode(w), f"D={d} bs={bs} append")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_fast_path_head_dims_persistent(d):
+    """Many partitions at head_dim 64 and 256: the call over all requests
+    (persistent waves where the grid outgrows the resident waves) gives each
+    request the bits it gets when decoded on its own, and is close to the
+    oracle."""
+    say(f"persistent waves D={d}")
+    w = inputs.paged_random("pwd", 8, 1, 2200, 32, 8, head_dim=d, num_blocks=1400, seed=76 + d,
+                            device=DEV)
+    w.context_lens[3] = 0
+    poison_tails(w)
+    spec = ops.CacheSpec.of(w)
+    out = run_decode(w, partition_tokens=16)
+    assert_close(w, out, oracle_decode(w), f"persistent D={d}")
+    for i in range(w.num_seqs):
+        one = ops.decode(spec, w.q[i:i + 1].contiguous(), w.k_cache, w.v_cache,
+                         w.block_tables[i:i + 1].contiguous(), w.context_lens[i:i + 1].contiguous(),
+                         w.max_context_len, w.scale, partition_tokens=16)
+        assert same_bits(out[i:i + 1], one), f"request {i}"
+
+
 @pytest.mark.parametrize("bs", [8, 32])
 def test_block_size_placement_invariance(bs):
     say(f"placement invariance bs={bs}")
@@ -1112,7 +1175,9 @@ def test_decode_step_fanout(grouped, stream_kv, part):
 
 
 @pytest.mark.parametrize("dtype,bs,d,hq", [("bf16", 16, 128, 8), ("bf16", 32, 128, 8),
-                                           ("bf16", 8, 128, 32), ("f32", 16, 64, 4)])
+                                           ("bf16", 8, 128, 32), ("f32", 16, 64, 4),
+                                           ("bf16", 16, 64, 8), ("bf16", 16, 256, 8),
+                                           ("bf16", 64, 256, 4)])
 def test_decode_step_block_manager_pairs(dtype, bs, d, hq):
     """Requests forked by the block manager, then one step: the pairs
     pa_bm_append reports, given per request, fold into pa_decode_step on
