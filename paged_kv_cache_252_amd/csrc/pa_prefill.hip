@@ -180,16 +180,25 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 // The same work with the tiles staged in LDS: a workgroup of W waves takes
 // W * RG * 16/g consecutive query tokens of one request and KV head; each tile
 // is copied from memory to LDS once per workgroup by the waves together (8 / W
-// KiB each, global_load_lds: no registers on the way), S - 1 tiles ahead of
-// the one being consumed, and every wave reads its MFMA operands from LDS.  One barrier per tile: after it, the tile is in LDS and
-// every wave is done with the previous one, whose stage is then refilled.
+// KiB each, global_load_lds: no registers on the way), and every wave reads
+// its MFMA operands from LDS.  Tiles are consumed in pairs (pair_softmax_pv:
+// one PV MFMA of K 32 for both), S - 2 tiles ahead of the pair being
+// consumed.  One barrier per pair: after it, the pair is in LDS and every
+// wave is done with the previous pair, whose stages are then refilled.
 
-// LDS stages: S - 1 tiles in flight while one is consumed; waves per
-// workgroup sharing them.  Measured on the chunked-prefill workload: 4 waves
-// with 3, 4 or 6 stages 216-217 us, 8 stages 236 us (the LDS then limits the
-// workgroups per CU); 2 waves 228-242 us, 8 waves 291 us.
-constexpr int kPrefillStages = 4;
-constexpr int kPrefillLdsWaves = 4;
+// LDS stages (an even number) and waves per workgroup sharing them.
+// Measured on the chunked-prefill workload with pairs: 4 waves with 4, 6 or
+// 8 stages 200, 197 and 202 us; 2 waves 261 us, 8 waves 208 us.  (Per tile,
+// with 16x16x16 PV MFMAs, it took 208 us.)  200 VGPRs: two waves per SIMD;
+// held to 168 (three waves) it spills and takes 295 us.
+#ifndef PA_PREFILL_STAGES
+#define PA_PREFILL_STAGES 6
+#endif
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 4
+#endif
+constexpr int kPrefillStages = PA_PREFILL_STAGES;
+constexpr int kPrefillLdsWaves = PA_PREFILL_WAVES;
 
 template <int RG, int S, int W>
 __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
@@ -201,6 +210,7 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
     float scale_log2, unsigned q_sign, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
     static_assert(W == 2 || W == 4 || W == 8, "a tile is 8 KiB: 8 / W copies of 1 KiB per wave");
+    static_assert(S % 2 == 0 && S >= 4, "stages hold whole pairs of tiles");
     constexpr int kCopies = 8 / W;
     __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
     const int h = blockIdx.x;
@@ -310,31 +320,71 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
             lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
         }
     };
+    // Tiles are consumed in pairs (b, b + 1), one barrier per pair; S - 2
+    // tiles are in flight while a pair is consumed.
 #pragma unroll
-    for (int t = 0; t < S - 1; ++t) issue(t);
-    for (int b = 0; b < nblk; ++b) {
-        wait_vmcnt<kCopies * (S - 2)>();         // this thread's copies of tile b have landed
-        __builtin_amdgcn_s_barrier();            // everyone's; and tile b - 1 is consumed
-        const int t_next = b + S - 1;            // refilling tile b - 1's stage
-        if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare)
+    for (int t = 0; t < S - 2; ++t) issue(t);
+    for (int b = 0; b < nblk; b += 2) {
+        wait_vmcnt<kCopies * (S - 4)>();         // this thread's copies of tiles b, b + 1 have landed
+        __builtin_amdgcn_s_barrier();            // everyone's; and tiles b - 2, b - 1 are consumed
+        const int t_next = b + S - 2;            // refilling their stages
+        if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare; t_next is even)
         issue(t_next);
+        issue(t_next + 1);
         const int start = tok0 + FBS * b;
         if (start < lim_max) {                   // (wave-uniform) something of it is visible here
-            const __bf16* stage = &ring[b % S][0];
-            Tile t;
-            const bf16x8* kp = reinterpret_cast<const bf16x8*>(stage) + lane;
+            const __bf16* sa = &ring[b % S][0];
+            const __bf16* sb = &ring[(b + 1) % S][0];
+            const bool has_b = b + 1 < nblk && start + FBS < lim_max;   // (wave-uniform)
+            f32x4 s_a[RG], s_b[RG];
+            s16x4 va[8], vb[8];
+            {
+                Tile t;
+                const bf16x8* kp = reinterpret_cast<const bf16x8*>(sa) + lane;
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
-            const s16x4* vp = reinterpret_cast<const s16x4*>(stage + FTILE) +
-                              2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
+                for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
+                tile_scores<RG>(s_a, t, qv);
+            }
+            if (has_b) {
+                Tile t;
+                const bf16x8* kp = reinterpret_cast<const bf16x8*>(sb) + lane;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) t.v[j] = vp[64 * j];
-            const int v_valid = clampi(lim_max - start, 0, FBS);
-            const bool masked = start + FBS > lim_min;
-            int rv[RG];
+                for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
+                tile_scores<RG>(s_b, t, qv);
+            } else {
 #pragma unroll
-            for (int u = 0; u < RG; ++u) rv[u] = clampi(lim[u] - start, 0, FBS);
-            consume_tile_groups<RG>(st, t, qv, scale_log2, lane, rv, v_valid, masked);
+                for (int u = 0; u < RG; ++u) s_b[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            __builtin_amdgcn_sched_barrier(0);   // V loads after the score MFMAs: fewer live registers
+            const int vo = 2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
+            const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + FTILE) + vo;
+            const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + FTILE) + vo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                va[j] = vpa[64 * j];
+                vb[j] = has_b ? vpb[64 * j] : s16x4{0, 0, 0, 0};
+            }
+            // values past the wave's visible positions may be stale bytes
+            const int tok_base = 4 * quad;
+            const int va_valid = clampi(lim_max - start, 0, FBS);
+            const int vb_valid = has_b ? clampi(lim_max - start - FBS, 0, FBS) : 0;
+            if (va_valid < FBS || vb_valid < FBS) {   // (wave-uniform)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (tok_base + i >= va_valid) va[j][i] = 0;
+                        if (tok_base + i >= vb_valid) vb[j][i] = 0;
+                    }
+            }
+            const bool masked = !has_b || start + 2 * FBS > lim_min;
+            int rva[RG], rvb[RG];
+#pragma unroll
+            for (int u = 0; u < RG; ++u) {
+                rva[u] = clampi(lim[u] - start, 0, FBS);
+                rvb[u] = has_b ? clampi(lim[u] - start - FBS, 0, FBS) : 0;
+            }
+            pair_softmax_pv<RG>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
         }
     }
     wait_vmcnt<0>();                             // no copy may land after the workgroup ends
