@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4   /* 4: PA_DECODE_PREFIX_RUNS */
+#define PA_ABI_VERSION 5   /* 4: PA_DECODE_PREFIX_RUNS; 5: PA_DECODE_APPEND_TILES */
 
 typedef enum {
     PA_F32 = 0,   /* IEEE binary32 */
@@ -145,6 +145,18 @@ typedef struct {
                                    PA_DECODE_GROUP_SHARED, which reads each once per group);
                                    -10% for a prefix shared by many requests decoded one
                                    request per wave, whose repeat reads must hit the caches */
+#define PA_DECODE_APPEND_TILES 8u  /* pa_decode_append / pa_decode_step on the MFMA path with
+                                      block size 16, 32 or 64: the wave that appends a
+                                      request's token writes the 16-position tile holding it
+                                      back whole, token included, once it has read the tile
+                                      (full-line stores), instead of storing the token's K
+                                      chunks and V elements on their own (the V column of a
+                                      dim-major tile lands in partial sectors).  A store-pattern
+                                      choice only: cache bytes and output are identical.
+                                      Applied without the flag when num_seqs * Hkv >= 1024;
+                                      measured on MI355X: -3.6% step time at 2,048 appends,
+                                      +2% at 256, where the tile stores come at the end of the
+                                      longest walks.  Ignored by pa_decode and elsewhere. */
 
 /* Version of this ABI (PA_ABI_VERSION of the library that was built). */
 int pa_abi_version(void);
@@ -283,6 +295,7 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *                 [block_size, 1024] (the fast path also needs a multiple of 16)
  *   flags         0 or an OR of PA_DECODE_STREAM_KV (a cache hint; results are the
  *                 same), PA_DECODE_GROUP_SHARED and PA_DECODE_PREFIX_RUNS
+ *                 (PA_DECODE_APPEND_TILES is accepted and has no effect here)
  */
 int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache,
               const void* q, const int32_t* block_tables, const int32_t* context_lens,
@@ -312,6 +325,7 @@ int pa_decode(const pa_cache_desc_t* c, const void* k_cache, const void* v_cache
  *
  *   k_cache, v_cache  written at the appended slots
  *   k_new, v_new      [num_seqs][Hkv][D], dtype c->dtype, 16-byte aligned
+ *   flags             as for pa_decode, plus PA_DECODE_APPEND_TILES
  *   other arguments   as for pa_decode
  */
 int pa_decode_append(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,

@@ -270,7 +270,8 @@ static int decode_impl(const char* fn, const pa_cache_desc_t* c, const void* k_c
         return fail(PA_ERR_SHAPE, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
                     max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
     if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-    if (flags & ~(PA_DECODE_STREAM_KV | PA_DECODE_GROUP_SHARED | PA_DECODE_PREFIX_RUNS))
+    if (flags & ~(PA_DECODE_STREAM_KV | PA_DECODE_GROUP_SHARED | PA_DECODE_PREFIX_RUNS |
+                  PA_DECODE_APPEND_TILES))
         return fail(PA_ERR_UNSUPPORTED, "unknown decode flags 0x%x", flags);
     if (num_seqs == 0) return ok();
     if (!k_cache || !v_cache || !q || !block_tables || !context_lens || !out)

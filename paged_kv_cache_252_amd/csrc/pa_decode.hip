@@ -82,6 +82,7 @@ struct FastArgs {
     const __bf16* __restrict__ v_new;
     int num_kv_heads;
     const int32_t* __restrict__ cow_src;
+    int append_tiles;   // the appended token's tile is written back whole (blocks of 16 or more)
 };
 
 // Merge of the partitions 0..nparts-1 of one query row whose partial states
@@ -192,6 +193,11 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     const int ob_new = (L - 1) % BS;                  // slot within the last block
     bf16x8 fk[KC];
     short fv[VJ];
+    // append_tiles (blocks of 16 or more): the tile that receives the token
+    // is written back whole from registers once it is loaded (full lines),
+    // instead of the token's 16-byte K chunks and 2-byte V elements being
+    // stored at once, which land in partial sectors.  (wave-uniform)
+    const bool whole_tile = BS >= 16 && a.append_tiles != 0;
     // Copy-on-write folded in (blocks of 16): the last block is read from
     // cow_src[seq] and written back whole, new token included, to the
     // request's own block, so the token needs no store of its own.
@@ -217,12 +223,12 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
             constexpr int TT = BS >= 16 ? 16 : BS;
             const int64_t tile_base = toff + static_cast<int64_t>(ob_new / TT) * TT * D;
             const int pt = ob_new % TT;
-            if (cow_phys < 0 && row == o_new) {
+            if (!whole_tile && cow_phys < 0 && row == o_new) {
                 bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + tile_base);
 #pragma unroll
                 for (int s4 = 0; s4 < KC; ++s4) kd[(4 * s4 + quad) * TT + pt] = fk[s4];
             }
-            if (cow_phys < 0 && quad == o_new / 4) {
+            if (!whole_tile && cow_phys < 0 && quad == o_new / 4) {
                 short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + tile_base);
 #pragma unroll
                 for (int j = 0; j < VJ; ++j) vd[(16 * j + row) * TT + pt] = fv[j];
@@ -288,6 +294,10 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
                             if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
                     if (cow_phys >= 0) {                  // the copy, with the token in it
                         const int64_t o = entry_off(nent - 1);
+                        store_tile(buf[u], const_cast<__bf16*>(k_head) + o, const_cast<__bf16*>(v_head) + o, lane);
+                    } else if (BS >= 16 && whole_tile) {   // the tile back, with the token in it
+                        constexpr int SUB = BS >= 16 ? BS / 16 : 1;   // tiles per block
+                        const int64_t o = entry_off(j / SUB) + static_cast<int64_t>(j % SUB) * (D * FBS);
                         store_tile(buf[u], const_cast<__bf16*>(k_head) + o, const_cast<__bf16*>(v_head) + o, lane);
                     }
                 }
@@ -371,7 +381,7 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // last items running as a tail on a mostly idle device.  Each item is
 // computed exactly as in the plain grid, so the bits are the same.
 template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST, int D>
-__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) void decode_fast_kernel(
+__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) __attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -379,7 +389,7 @@ __global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) void decode_fast_
     int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
     const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
-    int num_seqs) {
+    int num_seqs, int append_tiles) {
     // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
     // dealt to the XCDs round-robin, so each XCD sees every partition index
     // and the same heads for all requests (a shared prefix's head slice then
@@ -392,7 +402,8 @@ __global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) void decode_fast_
   // one (request, partition) item
   const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
                     num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
-                    scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src};
+                    scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src,
+                    append_tiles};
   auto body = [&](const int seq, const int part) {
       fast_item<NBUF, NT, APPEND, WGM, BS, D>(fa, h, seq, part);
   };
@@ -896,7 +907,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     int num_seqs, int num_q_heads, int group, int max_blocks_per_seq, int len_clamp,
     int part_tokens, int max_parts, float scale_log2, __bf16* __restrict__ out,
     float* __restrict__ ws_acc, float* __restrict__ ws_m, float* __restrict__ ws_l,
-    const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new, int num_kv_heads) {
+    const __bf16* __restrict__ k_new, const __bf16* __restrict__ v_new, int num_kv_heads,
+    int append_tiles) {
     constexpr int S = kCascadeStages;
     constexpr int kCopies = 2;                       // KiB of each 8 KiB tile per wave
     __shared__ __align__(16) __bf16 ring[S][2 * FTILE];
@@ -936,13 +948,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     __syncthreads();
     if (!not_shared) {
         const int32_t* tab0 = block_tables + static_cast<int64_t>(seq0) * max_blocks_per_seq + blk0;
+        bool bad = false;
         for (int i = threadIdx.x; i < nmem * nblk; i += 256) {
             const int m = i / nblk;
             const int j = i - m * nblk;
-            bool bad = tab0[static_cast<int64_t>(m) * max_blocks_per_seq + j] != tab0[j];
+            bad = bad || tab0[static_cast<int64_t>(m) * max_blocks_per_seq + j] != tab0[j];
             if (j == 0) bad = bad || clampL(context_lens[seq0 + m]) <= tok1;
-            if (bad) not_shared = 1;                 // (every writer writes 1)
         }
+        // one LDS write per wave (many lanes storing to one word would serialise)
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) not_shared = 1;
     }
     __syncthreads();
     const bool shared = not_shared == 0;
@@ -1033,7 +1047,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     if (m >= nmem) return;
     const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
                       num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
-                      scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, nullptr};
+                      scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, nullptr,
+                      append_tiles};
     fast_item<PA_FAST_NBUF, NT, APPEND, false, FBS, FD>(fa, h, seq0 + m, part);
 }
 
@@ -1344,6 +1359,17 @@ int workgroups_per_cu(const void* kernel) {
     return per_cu;
 }
 
+// Whether the append writes each token's tile back whole: asked for, or a
+// batch of at least kAppendTilesMin (request, KV head) appends.  Measured
+// (blocks of 16, D 128): 2,048 appends (the shared-prefix step) 87.6 -> 84.4
+// us; 256 (the GQA step) 53.1 -> 54.3 us, where the whole-tile stores come at
+// the end of the longest walks.
+constexpr int64_t kAppendTilesMin = 1024;
+int append_tiles(const DecodeArgs& a) {
+    return (a.flags & PA_DECODE_APPEND_TILES) != 0 ||
+           static_cast<int64_t>(a.num_seqs) * a.num_kv_heads >= kAppendTilesMin;
+}
+
 template <bool NT, bool APPEND, int BS, int D>
 int launch_fast(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
@@ -1359,7 +1385,7 @@ int launch_fast(const DecodeArgs& a) {
                            a.num_q_heads, a.group, a.max_blocks_per_seq, a.len_clamp, a.part_tokens,
                            a.max_parts, sl2, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                            static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                           a.num_kv_heads, a.cow_src, a.num_seqs);
+                           a.num_kv_heads, a.cow_src, a.num_seqs, append_tiles(a));
         return check_launch("decode (fast, workgroup merge)");
     }
     // One wave per (KV head, request, partition), unless that grid holds more
@@ -1381,7 +1407,7 @@ int launch_fast(const DecodeArgs& a) {
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
                        static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                       a.num_kv_heads, a.cow_src, a.num_seqs);
+                       a.num_kv_heads, a.cow_src, a.num_seqs, append_tiles(a));
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
     if constexpr (D == FD)
@@ -1444,7 +1470,7 @@ int launch_cascade(const DecodeArgs& a) {
                        a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
                        static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                       a.num_kv_heads);
+                       a.num_kv_heads, append_tiles(a));
     int st = check_launch("decode (prefix runs)");
     if (st != PA_OK) return st;
     return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,

@@ -31,6 +31,7 @@ PA_F32, PA_BF16 = 0, 1
 PA_DECODE_STREAM_KV = 1
 PA_DECODE_GROUP_SHARED = 2
 PA_DECODE_PREFIX_RUNS = 4
+PA_DECODE_APPEND_TILES = 8
 _DTYPES = {"f32": (PA_F32, torch.float32), "bf16": (PA_BF16, torch.bfloat16)}
 
 
@@ -343,9 +344,11 @@ def _decode_args(spec, q, k_cache, v_cache, block_tables, context_lens, max_cont
     return dev, s, hq, out, workspace, ws_bytes
 
 
-def _flags(stream_kv: bool, group_shared: bool, prefix_runs: bool = False) -> int:
+def _flags(stream_kv: bool, group_shared: bool, prefix_runs: bool = False,
+           append_tiles: bool = False) -> int:
     return ((PA_DECODE_STREAM_KV if stream_kv else 0) | (PA_DECODE_GROUP_SHARED if group_shared else 0)
-            | (PA_DECODE_PREFIX_RUNS if prefix_runs else 0))
+            | (PA_DECODE_PREFIX_RUNS if prefix_runs else 0)
+            | (PA_DECODE_APPEND_TILES if append_tiles else 0))
 
 
 def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
@@ -380,10 +383,13 @@ def decode(spec: CacheSpec, q, k_cache, v_cache, block_tables, context_lens,
 def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tables,
                   context_lens, max_context_len: int, scale: float, out=None, workspace=None,
                   partition_tokens: int = 0, stream_kv: bool = False,
-                  group_shared: bool = False, prefix_runs: bool = False):
+                  group_shared: bool = False, prefix_runs: bool = False,
+                  append_tiles: bool = False):
     """``pa_decode_append``: append each request's token at position L-1, then decode.
 
     ``k_new``/``v_new`` are [num_seqs, Hkv, head_dim]; the caches are written.
+    ``append_tiles`` sets ``PA_DECODE_APPEND_TILES`` (the token's tile is
+    written back whole; same bytes).
     """
     dev, s, hq, out, workspace, ws_bytes = _decode_args(
         spec, q, k_cache, v_cache, block_tables, context_lens, max_context_len, out, workspace,
@@ -398,14 +404,14 @@ def decode_append(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, block_tabl
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(q),
         _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1], max_context_len,
         float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
-        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
+        _flags(stream_kv, group_shared, prefix_runs, append_tiles), _stream(dev)))
     return out
 
 
 def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, block_tables,
                 context_lens, max_context_len: int, scale: float, out=None, workspace=None,
                 partition_tokens: int = 0, stream_kv: bool = False, group_shared: bool = False,
-                prefix_runs: bool = False):
+                prefix_runs: bool = False, append_tiles: bool = False):
     """``pa_decode_step``: copy-on-write of each request's last block from
     ``cow_src[i]`` (int32 [num_seqs], -1 = none), then append + decode."""
     dev, s, hq, out, workspace, ws_bytes = _decode_args(
@@ -425,7 +431,7 @@ def decode_step(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src, blo
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
         _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
         max_context_len, float(scale), _ptr(out), _ptr(workspace), ws_bytes, partition_tokens,
-        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
+        _flags(stream_kv, group_shared, prefix_runs, append_tiles), _stream(dev)))
     return out
 
 
@@ -436,7 +442,8 @@ NOALLOC_MAX_BYTES = 64 << 20
 def decode_step_noalloc(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_src,
                         block_tables, context_lens, max_context_len: int, scale: float, out,
                         partition_tokens: int = 0, stream_kv: bool = False,
-                        group_shared: bool = False, prefix_runs: bool = False):
+                        group_shared: bool = False, prefix_runs: bool = False,
+                        append_tiles: bool = False):
     """``pa_decode_step_noalloc``: ``decode_step`` with the split-K partials
     in the library's static scratch instead of a workspace.  ``out`` must be
     given (nothing is allocated here either)."""
@@ -458,7 +465,7 @@ def decode_step_noalloc(spec: CacheSpec, q, k_cache, v_cache, k_new, v_new, cow_
         ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(cow_src),
         _ptr(q), _ptr(block_tables), _ptr(context_lens), s, hq, block_tables.shape[1],
         max_context_len, float(scale), _ptr(out), partition_tokens,
-        _flags(stream_kv, group_shared, prefix_runs), _stream(dev)))
+        _flags(stream_kv, group_shared, prefix_runs, append_tiles), _stream(dev)))
     return out
 
 

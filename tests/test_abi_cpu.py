@@ -29,7 +29,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert ops.abi_version() == 4
+    assert ops.abi_version() == 5
     assert ops.status_string(0) == "PA_OK"
     assert ops.status_string(5) == "PA_ERR_UNSUPPORTED"
     assert ops.status_string(8) == "PA_ERR_VALIDATE"
@@ -80,7 +80,7 @@ def test_decode_argument_checks(lib):
     assert _decode(lib, _desc(block_size=8), max_blocks=8, part=8) == 2
     assert _decode(lib, _desc(block_size=32), max_blocks=2, part=16) == 2
     assert _decode(lib, _desc(), ptr=(1 << 20) + 8) == 4            # misaligned buffers
-    assert _decode(lib, _desc(), flags=8) == 5                      # unknown flag bit
+    assert _decode(lib, _desc(), flags=16) == 5                     # unknown flag bit
     d = _desc()
     assert lib.pa_decode(ctypes.byref(d), None, None, None, None, None, 2, 32, 4, 64, 0.1, None,
                          None, 0, 16, 0, None) == 1

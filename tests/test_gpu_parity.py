@@ -1078,6 +1078,65 @@ def test_fast_path_head_dims(d, bs, group):
     assert_close(w, fused, oracle_decode(w), f"D={d} bs={bs} append")
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
+def test_append_tiles_same_bytes(d, bs):
+    """PA_DECODE_APPEND_TILES (the token's tile written back whole) leaves the
+    same cache bytes, NaN-poisoned free slots included, and the same output
+    bits as the token's own stores, at several partition sizes and with the
+    copy-on-write fold of pa_decode_step; both match the oracle."""
+    hkv = 2
+    lens = [1, 15, 16, 17, 31, 32, 33, 64, 65, 200, 511, 700]
+    w = inputs.paged_random("atl", len(lens), 0, 700, 4 * hkv, hkv, head_dim=d, block_size=bs,
+                            num_blocks=-(-700 // bs) * len(lens) + 8 + len(lens), seed=d + 3 * bs,
+                            device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_step_tokens(w)
+    spec = ops.CacheSpec.of(w)
+    k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+    g = max(16, bs)
+    for part in sorted({0, g, 4 * g}):
+        say(f"append tiles D={d} bs={bs} part={part}")
+        outs, caches = [], []
+        for tiles in (False, True):
+            w.k_cache.copy_(k0)
+            w.v_cache.copy_(v0)
+            outs.append(ops.decode_append(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v,
+                                          w.block_tables, w.context_lens, w.max_context_len,
+                                          w.scale, partition_tokens=part, append_tiles=tiles))
+            torch.cuda.synchronize()
+            caches.append((w.k_cache.clone(), w.v_cache.clone()))
+        assert torch.equal(bits(caches[0][0]), bits(caches[1][0]))
+        assert torch.equal(bits(caches[0][1]), bits(caches[1][1]))
+        assert same_bits(outs[0], outs[1])
+    assert_close(w, outs[1], oracle_decode(w), f"append tiles D={d} bs={bs}")
+    # with copy-on-write sources: every request's last block copied from a free block
+    tab, lens_np = to_np(w.block_tables), to_np(w.context_lens)
+    used = set(int(b) for b in tab[tab >= 0])
+    free = [b for b in range(w.num_blocks) if b not in used]
+    src = np.full(w.num_seqs, -1, dtype=np.int32)
+    for i in range(w.num_seqs):
+        if lens_np[i] > 0 and i % 2 == 0:
+            src[i] = free[i]
+    cow = torch.as_tensor(src, device=DEV)
+    sel = torch.as_tensor(src[src >= 0].astype(np.int64), device=DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(d + bs)
+    k0[sel] = torch.randn(k0[sel].shape, generator=gen, device=DEV).to(k0.dtype)
+    v0[sel] = torch.randn(v0[sel].shape, generator=gen, device=DEV).to(v0.dtype)
+    res = []
+    for tiles in (False, True):
+        w.k_cache.copy_(k0)
+        w.v_cache.copy_(v0)
+        o = ops.decode_step(spec, w.q, w.k_cache, w.v_cache, w.new_k, w.new_v, cow, w.block_tables,
+                            w.context_lens, w.max_context_len, w.scale, partition_tokens=g,
+                            append_tiles=tiles)
+        torch.cuda.synchronize()
+        res.append((o, w.k_cache.clone(), w.v_cache.clone()))
+    assert same_bits(res[0][0], res[1][0])
+    assert torch.equal(bits(res[0][1]), bits(res[1][1])) and torch.equal(bits(res[0][2]), bits(res[1][2]))
+
+
 @pytest.mark.parametrize("d", [64, 256])
 def test_fast_path_head_dims_persistent(d):
     """Many partitions at head_dim 64 and 256: the call over all requests
