@@ -10,9 +10,10 @@
 // paged storage; long histories are split into partitions whose partial
 // states are merged by a second, fixed-order reduction.
 //
-// Fast path (bf16, head_dim 128, block_size 16, up to 16 query heads per
-// KV head): one 64-lane wave per (request, KV head, partition).  Per block
-// of 16 tokens:
+// Fast path (bf16, head_dim D = 64, 128 or 256, block_size 8, 16, 32 or 64,
+// up to 16 query heads per KV head): one 64-lane wave per (request, KV head,
+// partition).  Per tile of 16 tokens (written for D 128; the counts scale
+// with D):
 //   * K tile (4 KiB) -> 4 x 16-byte loads per lane, each wave-wide load a
 //     contiguous 1 KiB, straight into the A operand of
 //     v_mfma_f32_16x16x32_bf16 (16 tokens x 32 dims) against the query
@@ -380,8 +381,13 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // once: with more items than that, a one-wave-per-item grid would leave its
 // last items running as a tail on a mostly idle device.  Each item is
 // computed exactly as in the plain grid, so the bits are the same.
+//
+// The block-16 workgroup-merge kernels at head_dim 64 and 128 are held to
+// three waves per SIMD (at most 168 VGPRs), which the append variant with
+// its tile write-back would otherwise exceed by two registers.
 template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST, int D>
-__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64) __attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void decode_fast_kernel(
+__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64)
+__attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void decode_fast_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -824,7 +830,7 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_ke
     const float lsum = sum_across_rows(st.l);
     const int my_nparts = (my_L + part_tokens - 1) / part_tokens;
     if (WGM && uniform) {
-        // LDS: [partition][row][acc 128 | m | l | pad 2]; wave 0 merges and
+        // LDS: [partition][row][acc FD | m | l | pad 2]; wave 0 merges and
         // marks the row as done for the merge kernel (l of partition 0 < 0)
         extern __shared__ float wg_part[];
         constexpr int RS = FD + 4;
