@@ -292,7 +292,9 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *                 is 0).  Calls in flight at the same time must not share a
  *                 workspace.
  *   partition_tokens  0 = automatic; otherwise a multiple of block_size in
- *                 [block_size, 1024] (the fast path also needs a multiple of 16)
+ *                 [block_size, 1024] (the MFMA path, bf16 with block size 8, 16, 32
+ *                 or 64 and head_dim 64, 128 or 256, also needs a multiple of 16
+ *                 and at most 64 blocks: 512 positions at block size 8)
  *   flags         0 or an OR of PA_DECODE_STREAM_KV (a cache hint; results are the
  *                 same), PA_DECODE_GROUP_SHARED and PA_DECODE_PREFIX_RUNS
  *                 (PA_DECODE_APPEND_TILES is accepted and has no effect here)
