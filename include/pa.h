@@ -112,8 +112,9 @@ typedef struct {
     int32_t block_size;    /* token positions per block: 1..256 (MFMA decode: 8, 16, 32
                               or 64; the grouped, prefix-run and prefill kernels: 16) */
     int32_t num_kv_heads;  /* Hkv >= 1 */
-    int32_t head_dim;      /* D: 16, 32, 64, 128 or 256 (MFMA decode, bf16: 64, 128 or
-                              256; the grouped, prefix-run and prefill kernels: 128) */
+    int32_t head_dim;      /* D: 16, 32, 64, 128 or 256 (MFMA decode: bf16 64, 128 or 256,
+                              fp32 64 or 128; the grouped, prefix-run and prefill kernels:
+                              bf16 128) */
     int32_t dtype;         /* pa_dtype_t of K, V, q, out, k_new, v_new */
     int64_t block_stride;  /* elements from block b to block b+1 in k_cache and in v_cache;
                               0 means dense (Hkv * block_size * head_dim) */
@@ -292,9 +293,9 @@ size_t pa_decode_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs,
  *                 is 0).  Calls in flight at the same time must not share a
  *                 workspace.
  *   partition_tokens  0 = automatic; otherwise a multiple of block_size in
- *                 [block_size, 1024] (the MFMA path, bf16 with block size 8, 16, 32
- *                 or 64 and head_dim 64, 128 or 256, also needs a multiple of 16
- *                 and at most 64 blocks: 512 positions at block size 8)
+ *                 [block_size, 1024] (the MFMA path -- block size 8, 16, 32 or 64;
+ *                 bf16 at head_dim 64, 128 or 256, fp32 at 64 or 128 -- also needs a
+ *                 multiple of 16 and at most 64 blocks: 512 positions at block size 8)
  *   flags         0 or an OR of PA_DECODE_STREAM_KV (a cache hint; results are the
  *                 same), PA_DECODE_GROUP_SHARED and PA_DECODE_PREFIX_RUNS
  *                 (PA_DECODE_APPEND_TILES is accepted and has no effect here)

@@ -56,44 +56,65 @@ constexpr size_t kMaxWgLds = 32768;
 // Load-ring depth of the fast path at head_dim d.
 constexpr int fast_nbuf(int d) { return d <= 64 ? PA_FAST_NBUF_D64 : PA_FAST_NBUF; }
 
-// Waves of a workgroup-merge workgroup of the fast path at head_dim d: at 256
-// a wave holds twice the tiles and accumulators, more than the 256 registers
-// each of eight waves may have, so its workgroups take at most four.
-constexpr int fast_wg_parts(int d) { return d > FD ? 4 : kMaxWgParts; }
+// Waves of a workgroup-merge workgroup of the fast path at head_dim d with
+// elements of esize bytes: with tiles twice those of bf16 at 128 (bf16 at 256,
+// fp32 at 128) a wave needs more than the 256 registers each of eight waves
+// may have, so those workgroups take at most four.
+constexpr int fast_wg_parts(int d, int esize = 2) { return d * esize > FD * 2 ? 4 : kMaxWgParts; }
 
 // ============================================================================
 // Fast path
 // ============================================================================
 
-// The arguments of one decode launch on the fast path.
-struct FastArgs {
-    const __bf16* __restrict__ k_cache;
-    const __bf16* __restrict__ v_cache;
-    const __bf16* __restrict__ q;
+// The arguments of one decode launch on the fast path (element type E).
+template <typename E>
+struct FastArgsT {
+    const E* __restrict__ k_cache;
+    const E* __restrict__ v_cache;
+    const E* __restrict__ q;
     const int32_t* __restrict__ block_tables;
     const int32_t* __restrict__ context_lens;
     int64_t num_blocks, blk_stride;
     int num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts;
     float scale_log2;
-    __bf16* __restrict__ out;
+    E* __restrict__ out;
     float* __restrict__ ws_acc;
     float* __restrict__ ws_m;
     float* __restrict__ ws_l;
-    const __bf16* __restrict__ k_new;
-    const __bf16* __restrict__ v_new;
+    const E* __restrict__ k_new;
+    const E* __restrict__ v_new;
     int num_kv_heads;
     const int32_t* __restrict__ cow_src;
     int append_tiles;   // the appended token's tile is written back whole (blocks of 16 or more)
 };
+using FastArgs = FastArgsT<__bf16>;
+
+// Four consecutive output elements: bf16 (rounded to nearest even) or fp32.
+template <typename E> struct Out4T;
+template <> struct Out4T<__bf16> { using T = uint2; };
+template <> struct Out4T<float> { using T = f32x4; };
+template <typename E>
+__device__ __forceinline__ typename Out4T<E>::T out4(const f32x4 v, const float inv) {
+    if constexpr (std::is_same<E, float>::value) {
+        return f32x4{v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv};
+    } else {
+        return make_uint2(pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv));
+    }
+}
+template <typename E>
+__device__ __forceinline__ typename Out4T<E>::T out4_zero() {
+    if constexpr (std::is_same<E, float>::value) return f32x4{0.f, 0.f, 0.f, 0.f};
+    else return make_uint2(0u, 0u);
+}
 
 // Merge of the partitions 0..nparts-1 of one query row whose partial states
 // sit in LDS at base + p * pstride (acc[D], then m and l), with the merge
 // kernel's formula: global maximum first, then fused multiply-adds in
 // partition order, one division.  Lane quad writes dims D/4*quad..+D/4-1 of
-// the bf16 output row o.
-template <int D>
+// the output row o.
+template <int D, typename E = __bf16>
 __device__ __forceinline__ void merge_lds_row(const float* base, int pstride, int nparts, int quad,
-                                              uint2* o) {
+                                              typename Out4T<E>::T* o) {
     constexpr int K = D / 16;                    // float4 chunks per lane
     float M = base[D];
     for (int p = 1; p < nparts; ++p) M = fmaxf(M, base[p * pstride + D]);
@@ -110,34 +131,36 @@ __device__ __forceinline__ void merge_lds_row(const float* base, int pstride, in
         den = __builtin_fmaf(src[D + 1], w, den);
     }
     const float inv = 1.f / den;
-    uint2* ob = o + K * quad;
+    typename Out4T<E>::T* ob = o + K * quad;
 #pragma unroll
-    for (int k = 0; k < K; ++k)
-        ob[k] = make_uint2(pack_bf16x2(num[k][0] * inv, num[k][1] * inv),
-                           pack_bf16x2(num[k][2] * inv, num[k][3] * inv));
+    for (int k = 0; k < K; ++k) ob[k] = out4<E>(num[k], inv);
 }
 
 // One wave's item of the fast path: partition `part` of request `seq` for KV
-// head h (the grid and the flags are described at decode_fast_kernel); head_dim D.
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, int D>
-__device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const int seq, const int part) {
-    constexpr int KC = D / 32;                        // K chunks (and q chunks) per lane
+// head h (the grid and the flags are described at decode_fast_kernel); head_dim
+// D, element type E (bf16, or fp32 through the fp32 MFMAs).
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, int D, typename E = __bf16>
+__device__ __forceinline__ void fast_item(const FastArgsT<E>& a, const int h, const int seq, const int part) {
+    using KChunk = typename ElemT<E>::KChunk;         // 16 bytes of a K row (and of q)
+    using VElem = std::conditional_t<std::is_same<E, float>::value, float, short>;
+    using O4 = typename Out4T<E>::T;
+    constexpr int KC = TileT<D, E>::KC;               // K chunks (and q chunks) per lane
     constexpr int VJ = D / 16;                        // V operands / accumulator chunks per lane
-    const __bf16* __restrict__ k_cache = a.k_cache;
-    const __bf16* __restrict__ v_cache = a.v_cache;
-    const __bf16* __restrict__ q = a.q;
+    const E* __restrict__ k_cache = a.k_cache;
+    const E* __restrict__ v_cache = a.v_cache;
+    const E* __restrict__ q = a.q;
     const int32_t* __restrict__ block_tables = a.block_tables;
     const int32_t* __restrict__ context_lens = a.context_lens;
     const int64_t num_blocks = a.num_blocks, blk_stride = a.blk_stride;
     const int num_q_heads = a.num_q_heads, group = a.group, max_blocks_per_seq = a.max_blocks_per_seq;
     const int len_clamp = a.len_clamp, part_tokens = a.part_tokens, max_parts = a.max_parts;
     const float scale_log2 = a.scale_log2;
-    __bf16* __restrict__ out = a.out;
+    E* __restrict__ out = a.out;
     float* __restrict__ ws_acc = a.ws_acc;
     float* __restrict__ ws_m = a.ws_m;
     float* __restrict__ ws_l = a.ws_l;
-    const __bf16* __restrict__ k_new = a.k_new;
-    const __bf16* __restrict__ v_new = a.v_new;
+    const E* __restrict__ k_new = a.k_new;
+    const E* __restrict__ v_new = a.v_new;
     const int num_kv_heads = a.num_kv_heads;
     const int32_t* __restrict__ cow_src = a.cow_src;
     const int lane = threadIdx.x & 63;
@@ -150,14 +173,14 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     const int hq = h * group + row;
     const bool row_ok = row < group;
     auto out_row = [&]() {
-        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * D);
+        return reinterpret_cast<O4*>(out + (static_cast<int64_t>(seq) * num_q_heads + hq) * D);
     };
 
     if (!WGM && tok0 >= L) {
         if (L == 0 && part == 0 && row_ok) {   // empty history: zero output
-            uint2* o = out_row();
+            O4* o = out_row();
 #pragma unroll
-            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = out4_zero<E>();
         }
         return;
     }
@@ -192,8 +215,8 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     const bool append_here = APPEND && part == nparts - 1;
     const int o_new = (L - 1) % FBS;                  // slot within the last tile
     const int ob_new = (L - 1) % BS;                  // slot within the last block
-    bf16x8 fk[KC];
-    short fv[VJ];
+    KChunk fk[KC];
+    VElem fv[VJ];
     // append_tiles (blocks of 16 or more): the tile that receives the token
     // is written back whole from registers once it is loaded (full lines),
     // instead of the token's 16-byte K chunks and 2-byte V elements being
@@ -212,8 +235,8 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     if constexpr (APPEND) {
         if (append_here) {
             const int64_t nrow = (static_cast<int64_t>(seq) * num_kv_heads + h) * D;
-            const bf16x8* kn = reinterpret_cast<const bf16x8*>(k_new + nrow);
-            const short* vn = reinterpret_cast<const short*>(v_new + nrow);
+            const KChunk* kn = reinterpret_cast<const KChunk*>(k_new + nrow);
+            const VElem* vn = reinterpret_cast<const VElem*>(v_new + nrow);
 #pragma unroll
             for (int s4 = 0; s4 < KC; ++s4) fk[s4] = kn[4 * s4 + quad];
 #pragma unroll
@@ -225,12 +248,12 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
             const int64_t tile_base = toff + static_cast<int64_t>(ob_new / TT) * TT * D;
             const int pt = ob_new % TT;
             if (!whole_tile && cow_phys < 0 && row == o_new) {
-                bf16x8* kd = reinterpret_cast<bf16x8*>(const_cast<__bf16*>(k_cache) + tile_base);
+                KChunk* kd = reinterpret_cast<KChunk*>(const_cast<E*>(k_cache) + tile_base);
 #pragma unroll
                 for (int s4 = 0; s4 < KC; ++s4) kd[(4 * s4 + quad) * TT + pt] = fk[s4];
             }
             if (!whole_tile && cow_phys < 0 && quad == o_new / 4) {
-                short* vd = reinterpret_cast<short*>(const_cast<__bf16*>(v_cache) + tile_base);
+                VElem* vd = reinterpret_cast<VElem*>(const_cast<E*>(v_cache) + tile_base);
 #pragma unroll
                 for (int j = 0; j < VJ; ++j) vd[(16 * j + row) * TT + pt] = fv[j];
             }
@@ -238,19 +261,19 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     }
 
     // Query rows of this KV head as the B operand (rows >= group are zero).
-    bf16x8 qv[KC];
+    KChunk qv[KC];
     {
-        const bf16x8* qp = reinterpret_cast<const bf16x8*>(
+        const KChunk* qp = reinterpret_cast<const KChunk*>(
             q + (static_cast<int64_t>(seq) * num_q_heads + (row_ok ? hq : 0)) * D);
 #pragma unroll
         for (int s = 0; s < KC; ++s) {
-            bf16x8 v = qp[4 * s + quad];
-            qv[s] = row_ok ? v : bf16x8{};
+            KChunk v = qp[4 * s + quad];
+            qv[s] = row_ok ? v : KChunk{};
         }
     }
 
-    const __bf16* k_head = k_cache + static_cast<int64_t>(h) * HT;
-    const __bf16* v_head = v_cache + static_cast<int64_t>(h) * HT;
+    const E* k_head = k_cache + static_cast<int64_t>(h) * HT;
+    const E* v_head = v_cache + static_cast<int64_t>(h) * HT;
 
     // A ring of NBUF tiles: while block j is consumed, blocks j+1 .. j+NBUF-1
     // are in flight.  Loads are unconditional (past the end they repeat the
@@ -259,20 +282,20 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     // scheduling barriers keep each tile's loads issued ahead of the previous
     // tile's arithmetic; without them the compiler sinks loads next to their
     // first use and every block waits a full memory latency.
-    TileT<D> buf[NBUF];
+    TileT<D, E> buf[NBUF];
     auto entry_off = [&](int e) {
         return static_cast<int64_t>(__builtin_amdgcn_readlane(my_phys, e < nent ? e : nent - 1)) * blk_stride;
     };
-    auto load_t = [&](TileT<D>& t, int jj) {   // tile jj (clamped to the last)
+    auto load_t = [&](TileT<D, E>& t, int jj) {   // tile jj (clamped to the last)
         const int jc = jj < nblk ? jj : nblk - 1;
         if constexpr (BS >= 16) {
             const int64_t o = (BS == 16 && cow_phys >= 0 && jc == nblk - 1)
                                   ? static_cast<int64_t>(cow_phys) * blk_stride
                                   : entry_off(jc / (BS / 16));
-            load_tile_bs<NT, BS>(t, k_head + o, v_head + o, nullptr, nullptr, jc % (BS / 16), lane);
+            load_tile_bs<NT, BS, D, E>(t, k_head + o, v_head + o, nullptr, nullptr, jc % (BS / 16), lane);
         } else {
             const int64_t oa = entry_off(2 * jc), ob = entry_off(2 * jc + 1);
-            load_tile_bs<NT, BS>(t, k_head + oa, v_head + oa, k_head + ob, v_head + ob, 0, lane);
+            load_tile_bs<NT, BS, D, E>(t, k_head + oa, v_head + oa, k_head + ob, v_head + ob, 0, lane);
         }
     };
 #pragma unroll
@@ -295,11 +318,11 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
                             if (quad * 4 + e == o_new) buf[u].v[jj][e] = fv[jj];
                     if (cow_phys >= 0) {                  // the copy, with the token in it
                         const int64_t o = entry_off(nent - 1);
-                        store_tile(buf[u], const_cast<__bf16*>(k_head) + o, const_cast<__bf16*>(v_head) + o, lane);
+                        store_tile(buf[u], const_cast<E*>(k_head) + o, const_cast<E*>(v_head) + o, lane);
                     } else if (BS >= 16 && whole_tile) {   // the tile back, with the token in it
                         constexpr int SUB = BS >= 16 ? BS / 16 : 1;   // tiles per block
                         const int64_t o = entry_off(j / SUB) + static_cast<int64_t>(j % SUB) * (D * FBS);
-                        store_tile(buf[u], const_cast<__bf16*>(k_head) + o, const_cast<__bf16*>(v_head) + o, lane);
+                        store_tile(buf[u], const_cast<E*>(k_head) + o, const_cast<E*>(v_head) + o, lane);
                     }
                 }
             }
@@ -328,17 +351,17 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
         }
         __syncthreads();
         if (part != 0 || !row_ok) return;
-        uint2* o = out_row();
+        O4* o = out_row();
         if (L == 0) {                          // empty history: zero output
 #pragma unroll
-            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+            for (int j = 0; j < VJ; ++j) o[4 * j + quad] = out4_zero<E>();
             return;
         }
         if (nparts > 1) {
             // merge partitions 0..nparts-1 in order (the merge kernel's formula:
             // global max first, then fused multiply-adds in partition order);
             // lane: row, dims 32*quad..+31
-            merge_lds_row<D>(wg_part + row * RS, group * RS, nparts, quad, o);
+            merge_lds_row<D, E>(wg_part + row * RS, group * RS, nparts, quad, o);
             return;
         }
         // a single partition: wave 0 holds the whole result (falls through)
@@ -347,11 +370,9 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
     if (nparts == 1) {
         if (!row_ok) return;
         const float inv = 1.f / lsum;
-        uint2* o = out_row();
+        O4* o = out_row();
 #pragma unroll
-        for (int jj = 0; jj < VJ; ++jj)
-            o[4 * jj + quad] = make_uint2(pack_bf16x2(st.acc[jj][0] * inv, st.acc[jj][1] * inv),
-                                          pack_bf16x2(st.acc[jj][2] * inv, st.acc[jj][3] * inv));
+        for (int jj = 0; jj < VJ; ++jj) o[4 * jj + quad] = out4<E>(st.acc[jj], inv);
         return;
     }
 
@@ -370,7 +391,7 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // the wave of the request's last partition stores k_new/v_new into the cache
 // and uses them in place of whatever its load of that slot returned.
 // WGM: the partitions of one (request, KV head) are the waves of one
-// workgroup (wave w = partition w, at most fast_wg_parts(D) of them) and are
+// workgroup (wave w = partition w, at most fast_wg_parts(D, sizeof(E)) of them) and are
 // merged through LDS after a workgroup barrier, instead of by the merge
 // kernel.  Waves without a partition wait at the barrier.
 //
@@ -382,19 +403,23 @@ __device__ __forceinline__ void fast_item(const FastArgs& a, const int h, const 
 // last items running as a tail on a mostly idle device.  Each item is
 // computed exactly as in the plain grid, so the bits are the same.
 //
-// The block-16 workgroup-merge kernels at head_dim 64 and 128 are held to
-// three waves per SIMD (at most 168 VGPRs), which the append variant with
+// The bf16 block-16 workgroup-merge kernels at head_dim 64 and 128 are held
+// to three waves per SIMD (at most 168 VGPRs), which the append variant with
 // its tile write-back would otherwise exceed by two registers.
-template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST, int D>
-__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D) : 64)
-__attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void decode_fast_kernel(
-    const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
-    const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
+//
+// E = float: the same kernel on fp32 caches, with the fp32 MFMA (K 4) for
+// scores and values; the probabilities stay fp32.
+template <int NBUF, bool NT, bool APPEND, bool WGM, int BS, bool PERSIST, int D, typename E>
+__global__ __launch_bounds__(WGM ? 64 * fast_wg_parts(D, sizeof(E)) : 64)
+__attribute__((amdgpu_waves_per_eu((std::is_same<E, __bf16>::value && WGM && BS == 16 && D <= 128) ? 3 : 1)))
+void decode_fast_kernel(
+    const E* __restrict__ k_cache, const E* __restrict__ v_cache,
+    const E* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
     int num_q_heads, int group, int max_blocks_per_seq, int len_clamp, int part_tokens,
-    int max_parts, float scale_log2, __bf16* __restrict__ out, float* __restrict__ ws_acc,
-    float* __restrict__ ws_m, float* __restrict__ ws_l, const __bf16* __restrict__ k_new,
-    const __bf16* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
+    int max_parts, float scale_log2, E* __restrict__ out, float* __restrict__ ws_acc,
+    float* __restrict__ ws_m, float* __restrict__ ws_l, const E* __restrict__ k_new,
+    const E* __restrict__ v_new, int num_kv_heads, const int32_t* __restrict__ cow_src,
     int num_seqs, int append_tiles) {
     // Grid (Hkv, S, partitions) with the KV head fastest: workgroups are
     // dealt to the XCDs round-robin, so each XCD sees every partition index
@@ -406,12 +431,12 @@ __attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void
     const int quad = lane >> 4;
 
   // one (request, partition) item
-  const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
-                    num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
-                    scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src,
-                    append_tiles};
+  const FastArgsT<E> fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
+                        num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
+                        scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, cow_src,
+                        append_tiles};
   auto body = [&](const int seq, const int part) {
-      fast_item<NBUF, NT, APPEND, WGM, BS, D>(fa, h, seq, part);
+      fast_item<NBUF, NT, APPEND, WGM, BS, D, E>(fa, h, seq, part);
   };
 
     if constexpr (PERSIST) {
@@ -439,10 +464,10 @@ __attribute__((amdgpu_waves_per_eu((WGM && BS == 16 && D <= 128) ? 3 : 1))) void
                 const int seq = static_cast<int>(__builtin_ctzll(zm));
                 zm &= zm - 1;
                 if (row < group) {
-                    uint2* o = reinterpret_cast<uint2*>(
+                    auto* o = reinterpret_cast<typename Out4T<E>::T*>(
                         out + (static_cast<int64_t>(seq) * num_q_heads + h * group + row) * D);
 #pragma unroll
-                    for (int j = 0; j < D / 16; ++j) o[4 * j + quad] = make_uint2(0u, 0u);
+                    for (int j = 0; j < D / 16; ++j) o[4 * j + quad] = out4_zero<E>();
                 }
             }
         }
@@ -1376,21 +1401,24 @@ int append_tiles(const DecodeArgs& a) {
            static_cast<int64_t>(a.num_seqs) * a.num_kv_heads >= kAppendTilesMin;
 }
 
-template <bool NT, bool APPEND, int BS, int D>
+template <bool NT, bool APPEND, int BS, int D, typename E>
 int launch_fast(const DecodeArgs& a) {
     const float sl2 = a.scale * kLog2e;
     const size_t wg_lds = static_cast<size_t>(a.max_parts) * a.group * (D + 4) * sizeof(float);
     constexpr int NB = fast_nbuf(D);
-    if (a.max_parts >= 2 && a.max_parts <= fast_wg_parts(D) && wg_lds <= kMaxWgLds) {
+    const E* kc = static_cast<const E*>(a.k_cache);
+    const E* vc = static_cast<const E*>(a.v_cache);
+    const E* qq = static_cast<const E*>(a.q);
+    const E* kn = static_cast<const E*>(a.k_new);
+    const E* vn = static_cast<const E*>(a.v_new);
+    E* out = static_cast<E*>(a.out);
+    if (a.max_parts >= 2 && a.max_parts <= fast_wg_parts(D, sizeof(E)) && wg_lds <= kMaxWgLds) {
         // partitions of a request are the waves of one workgroup, merged in LDS
-        hipLaunchKernelGGL((decode_fast_kernel<NB, NT, APPEND, true, BS, false, D>),
+        hipLaunchKernelGGL((decode_fast_kernel<NB, NT, APPEND, true, BS, false, D, E>),
                            dim3(a.num_kv_heads, a.num_seqs, 1), dim3(64 * a.max_parts), wg_lds,
-                           a.stream, static_cast<const __bf16*>(a.k_cache),
-                           static_cast<const __bf16*>(a.v_cache), static_cast<const __bf16*>(a.q),
-                           a.block_tables, a.context_lens, a.num_blocks, a.block_stride,
-                           a.num_q_heads, a.group, a.max_blocks_per_seq, a.len_clamp, a.part_tokens,
-                           a.max_parts, sl2, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
-                           static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
+                           a.stream, kc, vc, qq, a.block_tables, a.context_lens, a.num_blocks,
+                           a.block_stride, a.num_q_heads, a.group, a.max_blocks_per_seq, a.len_clamp,
+                           a.part_tokens, a.max_parts, sl2, out, a.ws_acc, a.ws_m, a.ws_l, kn, vn,
                            a.num_kv_heads, a.cow_src, a.num_seqs, append_tiles(a));
         return check_launch("decode (fast, workgroup merge)");
     }
@@ -1399,30 +1427,34 @@ int launch_fast(const DecodeArgs& a) {
     // head as fit, each taking every Z-th item (at most 64 requests).
     const int64_t upper = static_cast<int64_t>(a.num_kv_heads) * a.num_seqs * a.max_parts;
     static const int per_cu = workgroups_per_cu(reinterpret_cast<const void*>(
-        &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D>));
+        &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D, E>));
     const int64_t resident = static_cast<int64_t>(per_cu) * device_cu_count();
     const bool persist = a.num_seqs <= 64 && resident >= a.num_kv_heads && upper > resident;
     const dim3 grid = persist ? dim3(a.num_kv_heads, static_cast<unsigned>(std::min<int64_t>(resident / a.num_kv_heads, 65535)), 1)
                               : dim3(a.num_kv_heads, a.num_seqs, a.max_parts);
-    auto kernel = persist ? &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D>
-                          : &decode_fast_kernel<NB, NT, APPEND, false, BS, false, D>;
-    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, a.stream,
-                       static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
-                       static_cast<const __bf16*>(a.q), a.block_tables, a.context_lens,
-                       a.num_blocks, a.block_stride, a.num_q_heads, a.group,
-                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2,
-                       static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
-                       static_cast<const __bf16*>(a.k_new), static_cast<const __bf16*>(a.v_new),
-                       a.num_kv_heads, a.cow_src, a.num_seqs, append_tiles(a));
+    auto kernel = persist ? &decode_fast_kernel<NB, NT, APPEND, false, BS, true, D, E>
+                          : &decode_fast_kernel<NB, NT, APPEND, false, BS, false, D, E>;
+    hipLaunchKernelGGL(kernel, grid, dim3(64), 0, a.stream, kc, vc, qq, a.block_tables,
+                       a.context_lens, a.num_blocks, a.block_stride, a.num_q_heads, a.group,
+                       a.max_blocks_per_seq, a.len_clamp, a.part_tokens, a.max_parts, sl2, out,
+                       a.ws_acc, a.ws_m, a.ws_l, kn, vn, a.num_kv_heads, a.cow_src, a.num_seqs,
+                       append_tiles(a));
     int st = check_launch("decode (fast)");
     if (st != PA_OK || a.max_parts <= 1) return st;
-    if constexpr (D == FD)
-        return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
-                          a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
-    hipLaunchKernelGGL((reduce_kernel<uint16_t, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
-                       a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
-                       a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
-    return check_launch("decode merge");
+    if constexpr (std::is_same<E, float>::value) {
+        hipLaunchKernelGGL((reduce_kernel<float, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
+                           a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
+                           a.max_parts, a.ws_acc, a.ws_m, a.ws_l, out);
+        return check_launch("decode merge");
+    } else {
+        if constexpr (D == FD)
+            return merge_bf16(a.context_lens, static_cast<int64_t>(a.num_seqs) * a.num_q_heads, a.num_q_heads,
+                              a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
+        hipLaunchKernelGGL((reduce_kernel<uint16_t, D>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
+                           a.stream, a.context_lens, a.num_q_heads, a.len_clamp, a.part_tokens,
+                           a.max_parts, a.ws_acc, a.ws_m, a.ws_l, static_cast<uint16_t*>(a.out));
+        return check_launch("decode merge");
+    }
 }
 
 template <int MAXR, bool NT, bool APPEND>
@@ -1483,18 +1515,20 @@ int launch_cascade(const DecodeArgs& a) {
                       a.len_clamp, a.part_tokens, a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
-template <int BS, int D>
+template <int BS, int D, typename E>
 int launch_fast_bsd(const DecodeArgs& a, bool nt) {
-    if (a.k_new) return nt ? launch_fast<true, true, BS, D>(a) : launch_fast<false, true, BS, D>(a);
-    return nt ? launch_fast<true, false, BS, D>(a) : launch_fast<false, false, BS, D>(a);
+    if (a.k_new) return nt ? launch_fast<true, true, BS, D, E>(a) : launch_fast<false, true, BS, D, E>(a);
+    return nt ? launch_fast<true, false, BS, D, E>(a) : launch_fast<false, false, BS, D, E>(a);
 }
 
 template <int BS>
 int launch_fast_bs(const DecodeArgs& a, bool nt) {
+    if (a.dtype == PA_F32)   // fp32: head_dim 64 or 128 (fast_decode_ok)
+        return a.head_dim == 64 ? launch_fast_bsd<BS, 64, float>(a, nt) : launch_fast_bsd<BS, FD, float>(a, nt);
     switch (a.head_dim) {
-        case 64: return launch_fast_bsd<BS, 64>(a, nt);
-        case 256: return launch_fast_bsd<BS, 256>(a, nt);
-        default: return launch_fast_bsd<BS, FD>(a, nt);
+        case 64: return launch_fast_bsd<BS, 64, __bf16>(a, nt);
+        case 256: return launch_fast_bsd<BS, 256, __bf16>(a, nt);
+        default: return launch_fast_bsd<BS, FD, __bf16>(a, nt);
     }
 }
 

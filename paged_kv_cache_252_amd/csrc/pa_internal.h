@@ -80,12 +80,14 @@ inline bool fast_path_ok(const pa_cache_desc_t* c, int group) {
            group <= 16;
 }
 
-// The MFMA decode kernel handles this shape: head_dim 64, 128 or 256 (blocks
-// of 8 pair up into its 16-token tiles; blocks of 32 or 64 split into them).
+// The MFMA decode kernel handles this shape: bf16 at head_dim 64, 128 or 256,
+// fp32 (the fp32 MFMA) at 64 or 128; blocks of 8 pair up into its 16-token
+// tiles, blocks of 32 or 64 split into them.
 inline bool fast_decode_ok(const pa_cache_desc_t* c, int group) {
     const int bs = c->block_size, d = c->head_dim;
-    return c->dtype == PA_BF16 && (d == 64 || d == 128 || d == 256) &&
-           (bs == 8 || bs == 16 || bs == 32 || bs == 64) && group >= 1 && group <= 16;
+    const bool dims = c->dtype == PA_BF16 ? (d == 64 || d == 128 || d == 256)
+                                          : (c->dtype == PA_F32 && (d == 64 || d == 128));
+    return dims && (bs == 8 || bs == 16 || bs == 32 || bs == 64) && group >= 1 && group <= 16;
 }
 
 // Partitions of the MFMA decode kernel are whole tiles and whole blocks.

@@ -6,6 +6,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -50,13 +52,28 @@ constexpr int FBS = 16;          // positions per tile (block_size 16)
 constexpr int FTILE = FD * FBS;  // elements of one (block, head) tile at head_dim 128
 constexpr int FG = 16;           // query rows of the score MFMA
 
+// Element types of the MFMA tiles: a K chunk is 16 bytes (X elements), a V
+// group the four positions 4*(l/16)..+3 of one dim.
+template <typename E> struct ElemT;
+template <> struct ElemT<__bf16> {
+    using KChunk = bf16x8;
+    using VGroup = s16x4;
+    static constexpr int X = 8;
+};
+template <> struct ElemT<float> {
+    using KChunk = f32x4;
+    using VGroup = f32x4;
+    static constexpr int X = 4;
+};
+
 // One 16-position tile of head_dim D (a multiple of 32, at most 256) in MFMA
-// operand layout.
-template <int D>
+// operand layout; element type E (bf16, or fp32 for the fp32 MFMAs).
+template <int D, typename E = __bf16>
 struct TileT {
     static_assert(D % 32 == 0 && D >= 32 && D <= 256, "head_dim a multiple of 32, at most 256");
-    bf16x8 k[D / 32];   // K: chunk (4*s + l/16), token l%16 -> A operand of step s
-    s16x4 v[D / 16];    // V: dim 16*j + l%16, tokens 4*(l/16)..+3 -> A operand of PV j
+    static constexpr int KC = D / (4 * ElemT<E>::X);   // K chunks per lane
+    typename ElemT<E>::KChunk k[KC];   // K: chunk (4*s + l/16), token l%16
+    typename ElemT<E>::VGroup v[D / 16];   // V: dim 16*j + l%16, tokens 4*(l/16)..+3
 };
 using Tile = TileT<FD>;
 
@@ -67,26 +84,30 @@ __device__ __forceinline__ V load16(const V* p) {
     else return *p;
 }
 
-template <bool NT, int D>
-__device__ __forceinline__ void load_tile(TileT<D>& t, const __bf16* __restrict__ k_tile,
-                                          const __bf16* __restrict__ v_tile, int lane) {
-    const bf16x8* kp = reinterpret_cast<const bf16x8*>(k_tile) + lane;
+template <bool NT, int D, typename E>
+__device__ __forceinline__ void load_tile(TileT<D, E>& t, const E* __restrict__ k_tile,
+                                          const E* __restrict__ v_tile, int lane) {
+    using KC = typename ElemT<E>::KChunk;
+    using VG = typename ElemT<E>::VGroup;
+    const KC* kp = reinterpret_cast<const KC*>(k_tile) + lane;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) t.k[s] = load16<NT>(kp + 64 * s);
-    const s16x4* vp = reinterpret_cast<const s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
+    for (int s = 0; s < TileT<D, E>::KC; ++s) t.k[s] = load16<NT>(kp + 64 * s);
+    const VG* vp = reinterpret_cast<const VG*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) t.v[j] = load16<NT>(vp + 64 * j);
 }
 
 // The inverse of load_tile: the tile's bytes back to a block (whole lines),
 // with the non-temporal hint (measured: 2.4 us less on the fan-out step).
-template <int D>
-__device__ __forceinline__ void store_tile(const TileT<D>& t, __bf16* __restrict__ k_tile,
-                                           __bf16* __restrict__ v_tile, int lane) {
-    bf16x8* kp = reinterpret_cast<bf16x8*>(k_tile) + lane;
+template <int D, typename E>
+__device__ __forceinline__ void store_tile(const TileT<D, E>& t, E* __restrict__ k_tile,
+                                           E* __restrict__ v_tile, int lane) {
+    using KC = typename ElemT<E>::KChunk;
+    using VG = typename ElemT<E>::VGroup;
+    KC* kp = reinterpret_cast<KC*>(k_tile) + lane;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) __builtin_nontemporal_store(t.k[s], kp + 64 * s);
-    s16x4* vp = reinterpret_cast<s16x4*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
+    for (int s = 0; s < TileT<D, E>::KC; ++s) __builtin_nontemporal_store(t.k[s], kp + 64 * s);
+    VG* vp = reinterpret_cast<VG*>(v_tile) + (lane & 15) * 4 + (lane >> 4);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) __builtin_nontemporal_store(t.v[j], vp + 64 * j);
 }
@@ -96,20 +117,22 @@ __device__ __forceinline__ void store_tile(const TileT<D>& t, __bf16* __restrict
 // BS = 8 (K [D/8][8][8], V [D][8] per head) the tile's first 8 tokens come
 // from block `a`, the next 8 from block `b` (K rows 8..15 and V token groups
 // 2..3).  k_a/v_a, k_b/v_b point at the head's region in blocks a and b.
-template <bool NT, int BS, int D>
-__device__ __forceinline__ void load_tile_bs(TileT<D>& t, const __bf16* __restrict__ k_a,
-                                             const __bf16* __restrict__ v_a,
-                                             const __bf16* __restrict__ k_b,
-                                             const __bf16* __restrict__ v_b, int sub, int lane) {
+template <bool NT, int BS, int D, typename E>
+__device__ __forceinline__ void load_tile_bs(TileT<D, E>& t, const E* __restrict__ k_a,
+                                             const E* __restrict__ v_a,
+                                             const E* __restrict__ k_b,
+                                             const E* __restrict__ v_b, int sub, int lane) {
+    using KC = typename ElemT<E>::KChunk;
+    using VG = typename ElemT<E>::VGroup;
     const int row = lane & 15, quad = lane >> 4;
     if constexpr (BS >= 16) {                 // tile `sub` of the block: a 16-position tile
         load_tile<NT>(t, k_a + sub * (D * FBS), v_a + sub * (D * FBS), lane);
     } else {
         static_assert(BS == 8, "blocks of 8, 16, 32 or 64 tokens");
-        const bf16x8* kp = reinterpret_cast<const bf16x8*>(row < 8 ? k_a : k_b) + (row & 7);
+        const KC* kp = reinterpret_cast<const KC*>(row < 8 ? k_a : k_b) + (row & 7);
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
-        const s16x4* vp = reinterpret_cast<const s16x4*>(quad < 2 ? v_a : v_b) + row * 2 + (quad & 1);
+        for (int s = 0; s < TileT<D, E>::KC; ++s) t.k[s] = load16<NT>(kp + (4 * s + quad) * 8);
+        const VG* vp = reinterpret_cast<const VG*>(quad < 2 ? v_a : v_b) + row * 2 + (quad & 1);
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) t.v[j] = load16<NT>(vp + 32 * j);
     }
@@ -170,14 +193,26 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 // where the VALU, not memory, bounds the loop.
 constexpr float kLazyMaxLog2 = 8.f;
 
-template <int D>
-__device__ __forceinline__ void consume_tile_rows(SoftmaxStateT<D>& st, TileT<D>& t,
-                                                  const bf16x8 (&qv)[D / 32], float scale_log2,
-                                                  int lane, int row_valid, int v_valid,
-                                                  bool masked) {
+template <int D, typename E>
+__device__ __forceinline__ void consume_tile_rows(SoftmaxStateT<D>& st, TileT<D, E>& t,
+                                                  const typename ElemT<E>::KChunk (&qv)[TileT<D, E>::KC],
+                                                  float scale_log2, int lane, int row_valid,
+                                                  int v_valid, bool masked) {
+    constexpr bool F32 = std::is_same<E, float>::value;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (F32) {
+        // fp32: K 4 per MFMA; at step (k, e) the lanes of quad q hold dim 16k + 4q + e
+        // of their token (A) and of their query row (B)
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
+        for (int k = 0; k < TileT<D, E>::KC; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                s = __builtin_amdgcn_mfma_f32_16x16x4f32(t.k[k][e], qv[k][e], s, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int k = 0; k < TileT<D, E>::KC; ++k)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(t.k[k], qv[k], s, 0, 0, 0);
+    }
     const int tok_base = 4 * (lane >> 4);
     float sc[4];
 #pragma unroll
@@ -208,12 +243,22 @@ __device__ __forceinline__ void consume_tile_rows(SoftmaxStateT<D>& st, TileT<D>
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = dead ? 0.f : fast_exp2(sc[i] - st.m);
     st.l += (p[0] + p[1]) + (p[2] + p[3]);
-    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    const s16x4 pb = __builtin_bit_cast(s16x4, pp);
+    if constexpr (F32) {
+        // fp32: step e takes positions 4q + e of every quad q; the lane holds
+        // those probabilities (p[e]) and values (v[j][e]) already
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j)
-        st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
+        for (int j = 0; j < D / 16; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(t.v[j][e], p[e], st.acc[j], 0, 0, 0);
+    } else {
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        const s16x4 pb = __builtin_bit_cast(s16x4, pp);
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+            st.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(t.v[j], pb, st.acc[j], 0, 0, 0);
+    }
 }
 
 // Maximum of floats on the VALU without the quieting of signalling NaNs that
@@ -397,11 +442,11 @@ __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile
 
 // One block of 16 tokens seen alike by every row: `valid` of its tokens are
 // visible (16 except in the last block of a request).
-template <int D>
-__device__ __forceinline__ void consume_tile(SoftmaxStateT<D>& st, TileT<D>& t,
-                                             const bf16x8 (&qv)[D / 32], float scale_log2, int lane,
-                                             int valid) {
-    consume_tile_rows(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
+template <int D, typename E>
+__device__ __forceinline__ void consume_tile(SoftmaxStateT<D>& st, TileT<D, E>& t,
+                                             const typename ElemT<E>::KChunk (&qv)[TileT<D, E>::KC],
+                                             float scale_log2, int lane, int valid) {
+    consume_tile_rows<D, E>(st, t, qv, scale_log2, lane, valid, valid, valid < FBS);
 }
 
 // 16 bytes per lane from gptr to LDS at lds_base + lane * 16 (lds_base

@@ -1038,27 +1038,27 @@ def test_fast_path_block_sizes(bs, group):
     assert_close(w, fused, oracle_decode(w), f"bs={bs} append")
 
 
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 256), ("f32", 64), ("f32", 128)])
 @pytest.mark.parametrize("bs", [8, 16, 64])
 @pytest.mark.parametrize("group", [1, 4, 16])
-def test_fast_path_head_dims(d, bs, group):
+def test_fast_path_head_dims(dtype, d, bs, group):
     """The MFMA decode at head_dim 64 and 256 (K chunks and V operands per
-    lane scale with D): against the oracle at several partition sizes, the
-    streaming hint giving the same bits, and the folded append equal to
-    write + decode."""
+    lane scale with D), and on fp32 caches through the fp32 MFMA: against the
+    oracle at several partition sizes, the streaming hint giving the same
+    bits, and the folded append equal to write + decode."""
     hkv = 2
     lens = [0, 1, 15, 16, 17, 63, 64, 65, 129, 300, 511, 700]
     w = inputs.paged_random("fhd", len(lens), 0, 700, hkv * group, hkv, head_dim=d, block_size=bs,
-                            num_blocks=-(-700 // bs) * len(lens) + 8, seed=d + bs + group,
-                            device=DEV, lens=lens)
+                            dtype=dtype, num_blocks=-(-700 // bs) * len(lens) + 8,
+                            seed=d + bs + group, device=DEV, lens=lens)
     poison_tails(w)
     ref = oracle_decode(w)
     g = max(16, bs)
     cap = min(64 * bs, 1024)
     for part in sorted({0, g, 5 * g, cap}):
-        say(f"decode D={d} bs={bs} g={group} part={part}")
+        say(f"decode {dtype} D={d} bs={bs} g={group} part={part}")
         out = run_decode(w, partition_tokens=part)
-        assert_close(w, out, ref, f"D={d} bs={bs} g={group} part={part}")
+        assert_close(w, out, ref, f"{dtype} D={d} bs={bs} g={group} part={part}")
         assert not to_np(out)[0].any()
         assert same_bits(out, run_decode(w, partition_tokens=part, stream_kv=True))
     inputs.add_step_tokens(w)
@@ -1075,12 +1075,12 @@ def test_fast_path_head_dims(d, bs, group):
     torch.cuda.synchronize()
     assert torch.equal(bits(w.k_cache), bits(k_sep)) and torch.equal(bits(w.v_cache), bits(v_sep))
     assert same_bits(fused, sep)
-    assert_close(w, fused, oracle_decode(w), f"D={d} bs={bs} append")
+    assert_close(w, fused, oracle_decode(w), f"{dtype} D={d} bs={bs} append")
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("bf16", 256), ("f32", 128)])
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])
-def test_append_tiles_same_bytes(d, bs):
+def test_append_tiles_same_bytes(dtype, d, bs):
     """PA_DECODE_APPEND_TILES (the token's tile written back whole) leaves the
     same cache bytes, NaN-poisoned free slots included, and the same output
     bits as the token's own stores, at several partition sizes and with the
@@ -1088,15 +1088,15 @@ def test_append_tiles_same_bytes(d, bs):
     hkv = 2
     lens = [1, 15, 16, 17, 31, 32, 33, 64, 65, 200, 511, 700]
     w = inputs.paged_random("atl", len(lens), 0, 700, 4 * hkv, hkv, head_dim=d, block_size=bs,
-                            num_blocks=-(-700 // bs) * len(lens) + 8 + len(lens), seed=d + 3 * bs,
-                            device=DEV, lens=lens)
+                            dtype=dtype, num_blocks=-(-700 // bs) * len(lens) + 8 + len(lens),
+                            seed=d + 3 * bs, device=DEV, lens=lens)
     poison_tails(w)
     inputs.add_step_tokens(w)
     spec = ops.CacheSpec.of(w)
     k0, v0 = w.k_cache.clone(), w.v_cache.clone()
     g = max(16, bs)
     for part in sorted({0, g, 4 * g}):
-        say(f"append tiles D={d} bs={bs} part={part}")
+        say(f"append tiles {dtype} D={d} bs={bs} part={part}")
         outs, caches = [], []
         for tiles in (False, True):
             w.k_cache.copy_(k0)
@@ -1109,7 +1109,7 @@ def test_append_tiles_same_bytes(d, bs):
         assert torch.equal(bits(caches[0][0]), bits(caches[1][0]))
         assert torch.equal(bits(caches[0][1]), bits(caches[1][1]))
         assert same_bits(outs[0], outs[1])
-    assert_close(w, outs[1], oracle_decode(w), f"append tiles D={d} bs={bs}")
+    assert_close(w, outs[1], oracle_decode(w), f"append tiles {dtype} D={d} bs={bs}")
     # with copy-on-write sources: every request's last block copied from a free block
     tab, lens_np = to_np(w.block_tables), to_np(w.context_lens)
     used = set(int(b) for b in tab[tab >= 0])
@@ -1137,20 +1137,20 @@ def test_append_tiles_same_bytes(d, bs):
     assert torch.equal(bits(res[0][1]), bits(res[1][1])) and torch.equal(bits(res[0][2]), bits(res[1][2]))
 
 
-@pytest.mark.parametrize("d", [64, 256])
-def test_fast_path_head_dims_persistent(d):
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 256), ("f32", 128)])
+def test_fast_path_head_dims_persistent(dtype, d):
     """Many partitions at head_dim 64 and 256: the call over all requests
     (persistent waves where the grid outgrows the resident waves) gives each
     request the bits it gets when decoded on its own, and is close to the
     oracle."""
-    say(f"persistent waves D={d}")
-    w = inputs.paged_random("pwd", 8, 1, 2200, 32, 8, head_dim=d, num_blocks=1400, seed=76 + d,
-                            device=DEV)
+    say(f"persistent waves {dtype} D={d}")
+    w = inputs.paged_random("pwd", 8, 1, 2200, 32, 8, head_dim=d, dtype=dtype, num_blocks=1400,
+                            seed=76 + d, device=DEV)
     w.context_lens[3] = 0
     poison_tails(w)
     spec = ops.CacheSpec.of(w)
     out = run_decode(w, partition_tokens=16)
-    assert_close(w, out, oracle_decode(w), f"persistent D={d}")
+    assert_close(w, out, oracle_decode(w), f"persistent {dtype} D={d}")
     for i in range(w.num_seqs):
         one = ops.decode(spec, w.q[i:i + 1].contiguous(), w.k_cache, w.v_cache,
                          w.block_tables[i:i + 1].contiguous(), w.context_lens[i:i + 1].contiguous(),
