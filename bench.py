@@ -53,6 +53,9 @@ WORKLOADS = {
     "gqa_d256": dict(make=inputs.gqa_d256, replicas=8,
                      desc="GQA decode at head_dim 256: 32 requests, context U[512,4096], "
                           "32 q / 8 KV heads, block 16, bf16, blocks shuffled in a 65536-block pool"),
+    "gqa_f32": dict(make=inputs.gqa_f32, replicas=8,
+                    desc="GQA decode on an fp32 cache: 32 requests, context U[512,4096], "
+                         "32 q / 8 KV heads, head_dim 128, block 16, blocks shuffled in a 65536-block pool"),
     "prefix": dict(make=inputs.shared_prefix, replicas=4, runs=True,
                    desc="shared prefix: 256 requests, first 2048 tokens in the same 128 blocks, "
                         "private suffix U[64,512], 32 q / 8 KV heads, head_dim 128, block 16, bf16"),
@@ -561,7 +564,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOADS),
                     help="the headline workload of the JSON line")
-    ap.add_argument("--extra", default="prefix,long,fanout,prefill,gqa_d64,gqa_d256",
+    ap.add_argument("--extra", default="prefix,long,fanout,prefill,gqa_d64,gqa_d256,gqa_f32",
                     help="comma-separated workloads also measured into the line's 'workloads' "
                          "object ('none' = only the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")

@@ -27,10 +27,10 @@ Recipe (all workloads):
 
 Named presets follow the five workload descriptions of the paged decode
 benchmark: a tiny fp32 example built around the worked block table
-[9, 2, 14]; GQA decode (also at head_dim 64 and 256); a long shared prefix;
-long-context split-K; and a fan-out step in which four branches share each
-prompt and each branch copies the prompt's partly filled last block before
-writing its new token.
+[9, 2, 14]; GQA decode (also at head_dim 64 and 256, and in fp32); a long
+shared prefix; long-context split-K; and a fan-out step in which four
+branches share each prompt and each branch copies the prompt's partly filled
+last block before writing its new token.
 """
 
 from __future__ import annotations
@@ -194,13 +194,13 @@ def paged_random(name: str, num_seqs: int, len_lo: int, len_hi: int, num_q_heads
 
 def gqa(seed: int = 1, device="cpu", poison: bool = True, num_seqs: int = 32,
         len_lo: int = 512, len_hi: int = 4096, num_blocks: int = 65536,
-        head_dim: int = 128) -> Workload:
+        head_dim: int = 128, dtype: str = "bf16") -> Workload:
     """GQA decode: 32 requests, L ~ U[512, 4096], 32 q / 8 KV heads, D 128
-    (or ``head_dim``), block size 16, bf16, blocks shuffled from a
-    65536-block pool."""
-    name = "gqa" if head_dim == 128 else f"gqa_d{head_dim}"
-    return paged_random(name, num_seqs, len_lo, len_hi, 32, 8, head_dim=head_dim, seed=seed,
-                        device=device, poison=poison, num_blocks=num_blocks)
+    (or ``head_dim``), block size 16, bf16 (or ``dtype``), blocks shuffled
+    from a 65536-block pool."""
+    name = "gqa" + ("" if head_dim == 128 else f"_d{head_dim}") + ("" if dtype == "bf16" else f"_{dtype}")
+    return paged_random(name, num_seqs, len_lo, len_hi, 32, 8, head_dim=head_dim, dtype=dtype,
+                        seed=seed, device=device, poison=poison, num_blocks=num_blocks)
 
 
 def gqa_d64(**kw) -> Workload:
@@ -211,6 +211,11 @@ def gqa_d64(**kw) -> Workload:
 def gqa_d256(**kw) -> Workload:
     """The GQA decode workload at head_dim 256."""
     return gqa(head_dim=256, **kw)
+
+
+def gqa_f32(**kw) -> Workload:
+    """The GQA decode workload on an fp32 cache."""
+    return gqa(dtype="f32", **kw)
 
 
 def long_context(seed: int = 3, device="cpu", poison: bool = True, num_seqs: int = 8,
@@ -406,6 +411,7 @@ PRESETS = {
     "gqa": gqa,
     "gqa_d64": gqa_d64,
     "gqa_d256": gqa_d256,
+    "gqa_f32": gqa_f32,
     "prefix": shared_prefix,
     "long": long_context,
     "fanout": fanout,
