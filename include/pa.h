@@ -416,9 +416,16 @@ int pa_decode_step_noalloc(const pa_cache_desc_t* c, void* k_cache, void* v_cach
  *   max_q_len     >= every n_i (host); sizes the grid
  *   workspace     >= pa_prefill_workspace_bytes(...) bytes
  *   flags         0
- * Compiled set: bf16, head_dim 128, block_size 16, Hq/Hkv dividing 16; other
- * shapes return PA_ERR_UNSUPPORTED.  Indices and row offsets read on the
- * device are clamped into range (no fault); PA_VALIDATE=1 rejects them.
+ * MFMA prefill kernels: bf16, head_dim 128, block_size 16, Hq/Hkv dividing
+ * 16 (partition_tokens 0 or a multiple of 16 in [16, 2^20]).  Every other
+ * shape pa_decode accepts runs each query row as a decode request: a small
+ * kernel gives row r of request i a copy of i's first ceil(max_context_len /
+ * block_size) table entries and its visible length L - n_i + j + 1 (clamped
+ * to [0, L]; a row outside every request's range gets 0), then the decode
+ * kernels run total_q requests; partition_tokens then follows pa_decode's
+ * rule with num_seqs = total_q, and the workspace holds the copies too.
+ * Indices and row offsets read on the device are clamped into range (no
+ * fault); PA_VALIDATE=1 rejects them.
  */
 size_t pa_prefill_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, int32_t total_q,
                                   int32_t max_q_len, int32_t num_q_heads,

@@ -189,6 +189,25 @@ size_t prefill_workspace(const pa_cache_desc_t* c, int32_t total_q, int32_t num_
     return partials + static_cast<size_t>(ceil_div(static_cast<int64_t>(total_q) * 4, 16) * 16);
 }
 
+// Shapes without an MFMA prefill kernel run each query row as a decode
+// request.  Workspace: the rows' table copies [total_q][row_blocks] int32,
+// their visible lengths [total_q] int32, then decode's partials for total_q
+// rows, each part starting on a 16-byte boundary.
+int32_t prefill_row_blocks(const pa_cache_desc_t* c, int32_t max_context_len) {
+    return static_cast<int32_t>(std::max<int64_t>(1, ceil_div(std::max(max_context_len, 0), c->block_size)));
+}
+
+size_t round16(size_t n) { return (n + 15) / 16 * 16; }
+
+size_t prefill_rows_workspace(const pa_cache_desc_t* c, int32_t total_q, int32_t num_q_heads,
+                              int32_t max_context_len, int32_t part) {
+    if (total_q <= 0) return 0;
+    const size_t rows = static_cast<size_t>(total_q);
+    return round16(rows * prefill_row_blocks(c, max_context_len) * sizeof(int32_t)) +
+           round16(rows * sizeof(int32_t)) +
+           workspace_bytes(c, total_q, num_q_heads, max_context_len, part);
+}
+
 // A prefill wave walks any number of 64-block chunks, so its partition is not
 // capped at 1024 tokens: the history is split only when there are too few
 // (request, query tile, KV head) waves to fill the device.
@@ -522,6 +541,11 @@ size_t pa_prefill_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, in
     if (check_desc(c) || check_heads(c, num_seqs, num_q_heads) || total_q < 0 || max_q_len < 0)
         return 0;
     int32_t part = 0;
+    if (!prefill_shape_ok(c, num_q_heads / c->num_kv_heads)) {
+        if (resolve_partition(c, total_q, num_q_heads, max_context_len, partition_tokens, &part))
+            return 0;
+        return prefill_rows_workspace(c, total_q, num_q_heads, max_context_len, part);
+    }
     if (prefill_partition(c, num_seqs, max_q_len, num_q_heads, max_context_len, partition_tokens, &part))
         return 0;
     return prefill_workspace(c, total_q, num_q_heads, max_context_len, part);
@@ -538,9 +562,8 @@ int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cach
     if (st) return st;
     if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
     const int group = num_q_heads / c->num_kv_heads;
-    if (!prefill_shape_ok(c, group))
-        return fail(PA_ERR_UNSUPPORTED,
-                    "pa_prefill supports bf16, head_dim 128, block_size 16 and Hq/Hkv dividing 16");
+    // outside the MFMA prefill kernels' set, each query row is a decode request
+    const bool as_rows = !prefill_shape_ok(c, group);
     if (total_q < 0 || total_q > kMaxGridYZ)
         return fail(PA_ERR_SHAPE, "total_q %d outside [0, %d]", total_q, kMaxGridYZ);
     if (max_q_len < 0) return fail(PA_ERR_SHAPE, "max_q_len %d < 0", max_q_len);
@@ -551,7 +574,7 @@ int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cach
                     max_context_len, static_cast<long long>(max_blocks_per_seq) * c->block_size);
     if (!std::isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
     if (flags != 0) return fail(PA_ERR_UNSUPPORTED, "unknown prefill flags 0x%x", flags);
-    const int64_t rows = prefill_waves_rows(num_seqs, max_q_len, group);
+    const int64_t rows = as_rows ? 0 : prefill_waves_rows(num_seqs, max_q_len, group);
     if (rows > kMaxGridYZ)
         return fail(PA_ERR_SHAPE, "num_seqs * ceil(max_q_len / %d) = %lld exceeds %d", 16 / group,
                     (long long)rows, kMaxGridYZ);
@@ -561,9 +584,15 @@ int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cach
     if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
         return fail(PA_ERR_ALIGN, "pa_prefill: caches, q and out must be 16-byte aligned");
     int32_t part = 0;
-    if ((st = prefill_partition(c, num_seqs, max_q_len, num_q_heads, max_context_len, partition_tokens, &part)))
+    if (as_rows) {
+        if ((st = resolve_partition(c, total_q, num_q_heads, max_context_len, partition_tokens, &part)))
+            return st;
+    } else if ((st = prefill_partition(c, num_seqs, max_q_len, num_q_heads, max_context_len,
+                                       partition_tokens, &part))) {
         return st;
-    const size_t need = prefill_workspace(c, total_q, num_q_heads, max_context_len, part);
+    }
+    const size_t need = as_rows ? prefill_rows_workspace(c, total_q, num_q_heads, max_context_len, part)
+                                : prefill_workspace(c, total_q, num_q_heads, max_context_len, part);
     if (need > 0) {
         if (!workspace) return fail(PA_ERR_WORKSPACE, "pa_prefill needs %zu bytes of workspace, got NULL", need);
         if (workspace_bytes_given < need)
@@ -599,6 +628,52 @@ int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cach
     if (parts64 > kMaxGridYZ)
         return fail(PA_ERR_SHAPE, "max_context_len %d needs %lld partitions of %d tokens (> %d)",
                     max_context_len, (long long)parts64, part, kMaxGridYZ);
+    if (as_rows) {
+        const int32_t row_blocks = prefill_row_blocks(c, max_context_len);
+        char* base = static_cast<char*>(workspace);
+        int32_t* row_tables = reinterpret_cast<int32_t*>(base);
+        base += round16(static_cast<size_t>(total_q) * row_blocks * sizeof(int32_t));
+        int32_t* row_lens = reinterpret_cast<int32_t*>(base);
+        base += round16(static_cast<size_t>(total_q) * sizeof(int32_t));
+        if ((st = launch_prefill_rows(q_start, block_tables, context_lens, num_seqs, total_q,
+                                      max_blocks_per_seq, row_blocks, max_context_len, row_tables,
+                                      row_lens, s)))
+            return st;
+        DecodeArgs a;
+        a.k_cache = k_cache;
+        a.v_cache = v_cache;
+        a.q = q;
+        a.block_tables = row_tables;
+        a.context_lens = row_lens;
+        a.num_blocks = c->num_blocks;
+        a.block_stride = block_stride(c);
+        a.block_size = c->block_size;
+        a.num_kv_heads = c->num_kv_heads;
+        a.head_dim = c->head_dim;
+        a.dtype = c->dtype;
+        a.num_seqs = total_q;
+        a.num_q_heads = num_q_heads;
+        a.group = group;
+        a.max_blocks_per_seq = row_blocks;
+        a.len_clamp = max_context_len;
+        a.part_tokens = part;
+        a.max_parts = static_cast<int32_t>(parts64);
+        a.scale = scale;
+        a.flags = 0;
+        a.out = out;
+        const size_t slots = static_cast<size_t>(total_q) * num_q_heads * a.max_parts;
+        const bool split = workspace_bytes(c, total_q, num_q_heads, max_context_len, part) > 0;
+        float* ws = split ? reinterpret_cast<float*>(base) : nullptr;
+        a.ws_acc = ws;
+        a.ws_m = split ? ws + slots * c->head_dim : nullptr;
+        a.ws_l = split ? ws + slots * (c->head_dim + 1) : nullptr;
+        a.k_new = nullptr;
+        a.v_new = nullptr;
+        a.cow_src = nullptr;
+        a.stream = s;
+        if ((st = launch_decode(a))) return st;
+        return ok();
+    }
     PrefillArgs p;
     DecodeArgs& a = p.d;
     a.k_cache = k_cache;

@@ -143,6 +143,15 @@ struct PrefillArgs {
 
 int launch_prefill(const PrefillArgs& a);
 
+// Shapes without an MFMA prefill kernel: row r of the packed query rows gets
+// row_tables[r][0 .. row_blocks) = its request's first row_blocks table
+// entries (row_blocks <= max_blocks_per_seq) and row_lens[r] = the positions
+// it sees, so that launch_decode runs the rows as total_q requests.
+int launch_prefill_rows(const int32_t* q_start, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+                        int32_t max_blocks_per_seq, int32_t row_blocks, int32_t len_clamp,
+                        int32_t* row_tables, int32_t* row_lens, hipStream_t stream);
+
 // The split-K merge of bf16, head_dim 128 partials: row r (of `rows`) and
 // query head hq combine the ceil(lens[r] / part_tokens) partitions of
 // ws_* [rows][Hq][max_parts] into out[r][hq] (rows with one partition are

@@ -486,4 +486,51 @@ int launch_prefill(const PrefillArgs& p) {
                         a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
+// ----------------------------------------------------------------------------
+// Shapes outside the MFMA prefill kernels: each query row as a decode request
+// ----------------------------------------------------------------------------
+//
+// Row r of request i sees the first L_i - n_i + j + 1 positions of i's
+// history (j = r - q_start[i]); that is a decode over i's block table cut at
+// that length.  This kernel gives every row its own copy of the first
+// row_blocks entries of i's table row and its visible length, so the decode
+// kernels run the chunk unchanged with one request per row.  Workgroup r
+// finds its request by binary search over q_start: the largest i with
+// q_start[i] <= r (empty requests in between are skipped that way).  A row
+// that falls in no request's range (a q_start that is not a partition of
+// [0, total_q)) gets length 0 and decodes to zeros.
+__global__ __launch_bounds__(64) void prefill_rows_kernel(
+    const int32_t* __restrict__ q_start, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int num_seqs, int max_blocks_per_seq,
+    int row_blocks, int len_clamp, int32_t* __restrict__ row_tables,
+    int32_t* __restrict__ row_lens) {
+    const int r = blockIdx.x;
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (q_start[mid] <= r) lo = mid;
+        else hi = mid - 1;
+    }
+    const int qs = q_start[lo];
+    const int n = q_start[lo + 1] - qs;
+    const int j = r - qs;
+    const int L = min(max(context_lens[lo], 0), len_clamp);
+    const int vis = (j >= 0 && j < n) ? min(max(L - n + j + 1, 0), L) : 0;
+    if (threadIdx.x == 0) row_lens[r] = vis;
+    const int32_t* src = block_tables + static_cast<int64_t>(lo) * max_blocks_per_seq;
+    int32_t* dst = row_tables + static_cast<int64_t>(r) * row_blocks;
+    for (int b = threadIdx.x; b < row_blocks; b += 64) dst[b] = src[b];
+}
+
+int launch_prefill_rows(const int32_t* q_start, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t total_q,
+                        int32_t max_blocks_per_seq, int32_t row_blocks, int32_t len_clamp,
+                        int32_t* row_tables, int32_t* row_lens, hipStream_t stream) {
+    if (num_seqs == 0 || total_q == 0) return PA_OK;
+    hipLaunchKernelGGL(prefill_rows_kernel, dim3(total_q), dim3(64), 0, stream, q_start,
+                       block_tables, context_lens, num_seqs, max_blocks_per_seq, row_blocks,
+                       len_clamp, row_tables, row_lens);
+    return check_launch("prefill rows");
+}
+
 }  // namespace pa

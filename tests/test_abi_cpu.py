@@ -116,17 +116,29 @@ def test_cache_op_argument_checks(lib):
 
 
 def _prefill(lib, d, num_seqs=2, total_q=4, max_q_len=2, num_q_heads=32, max_blocks=4,
-             max_len=64, part=0, flags=0, scale=0.1):
+             max_len=64, part=0, flags=0, scale=0.1, ws=1 << 30):
     p = ctypes.c_void_p(1 << 20)
     return lib.pa_prefill(ctypes.byref(d), p, p, p, p, p, p, num_seqs, total_q, max_q_len,
-                          num_q_heads, max_blocks, max_len, scale, p, p, 1 << 30, part, flags, None)
+                          num_q_heads, max_blocks, max_len, scale, p, p, ws, part, flags, None)
 
 
 def test_prefill_argument_checks(lib):
     """pa_prefill rejects what it cannot run before touching the device."""
     d = _desc()
-    assert _prefill(lib, d, num_q_heads=24) == 5                   # g = 3 does not divide 16
-    assert _prefill(lib, _desc(dtype=0, head_dim=32)) == 5         # outside the compiled set
+    f32 = _desc(dtype=0, head_dim=32, block_size=4)
+    # shapes outside the MFMA prefill kernels (g = 3; fp32) take the rows-as-
+    # decodes route, whose workspace always holds the row tables and lengths
+    for dd, hq, mb in ((d, 24, 4), (f32, 32, 16)):
+        assert _prefill(lib, dd, num_q_heads=hq, max_blocks=mb, ws=16) == 6
+        assert _prefill(lib, dd, num_q_heads=hq, max_blocks=mb, flags=1) == 5
+        assert _prefill(lib, dd, num_q_heads=hq, max_blocks=mb, total_q=70000) == 2
+    assert _prefill(lib, f32, max_blocks=16, part=6) == 2            # decode's partition rule
+    bs = 4
+    rb = 64 // bs
+    parts = 64 // 16
+    want = 4 * rb * 4 + 16 + 4 * 32 * parts * (32 + 2) * 4             # tables, lengths, partials
+    assert lib.pa_prefill_workspace_bytes(ctypes.byref(f32), 2, 4, 2, 32, 64, 16) == want
+    assert lib.pa_prefill_workspace_bytes(ctypes.byref(f32), 2, 4, 2, 32, 16, 16) == 4 * 4 * 4 + 16
     assert _prefill(lib, d, total_q=-1) == 2
     assert _prefill(lib, d, total_q=70000) == 2
     assert _prefill(lib, d, max_q_len=-3) == 2

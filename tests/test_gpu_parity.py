@@ -995,6 +995,76 @@ def test_prefill_validate_rejects_bad_offsets(monkeypatch):
     assert e.value.status == 8
 
 
+# Shapes outside the MFMA prefill kernels: each query row runs as a decode
+# request over a copy of its request's table, cut at the positions it sees.
+ROWS_SHAPES = [
+    ("f32", 16, 4, 4),       # generic decode kernel
+    ("f32", 128, 16, 8),     # fp32 matrix-core decode
+    ("bf16", 64, 8, 8),
+    ("bf16", 256, 16, 4),
+    ("bf16", 128, 32, 8),
+    ("bf16", 128, 16, 6),    # Hq/Hkv = 3 does not divide 16
+]
+
+
+def _rows_workload(dtype, d, bs, hq, seed=71):
+    lens = [1, 15, 16, 17, 40, 100, 0, 77, 33]
+    w = inputs.paged_random("pfr", len(lens), 0, 100, hq, 2, head_dim=d, block_size=bs,
+                            dtype=dtype, num_blocks=120, seed=seed, device=DEV, lens=lens)
+    poison_tails(w)
+    return inputs.add_query_chunks(w, [1, 15, 3, 17, 40, 9, 2, 0, 35])
+
+
+@pytest.mark.parametrize("dtype,d,bs,hq", ROWS_SHAPES)
+@pytest.mark.parametrize("part", [0, 32])
+def test_prefill_rows_route_matches_oracle(dtype, d, bs, hq, part):
+    """Whole prompts, single tokens, empty chunks and chunks longer than the
+    history, at shapes the MFMA prefill kernels do not take, against the oracle."""
+    say(f"prefill rows {dtype} d={d} bs={bs} hq={hq} part={part}")
+    w = _rows_workload(dtype, d, bs, hq)
+    out = _run_prefill(w, partition_tokens=part)
+    assert_close(w, out, _oracle_prefill(w), f"prefill rows {dtype} d={d} bs={bs}")
+
+
+@pytest.mark.parametrize("dtype,d,bs,hq", [ROWS_SHAPES[0], ROWS_SHAPES[3]])
+def test_prefill_rows_route_is_decode_per_row(dtype, d, bs, hq):
+    """The route's table copies and lengths are exact: pa_decode over tables
+    and lengths expanded row by row on the host gives the same bits."""
+    say(f"prefill rows == decode per row {dtype} d={d}")
+    w = _rows_workload(dtype, d, bs, hq, seed=72)
+    got = _run_prefill(w, partition_tokens=32)
+    qs, lens = to_np(w.q_start), to_np(w.context_lens)
+    bt = to_np(w.block_tables)
+    rows, row_lens = [], []
+    for i in range(w.num_seqs):
+        n = int(qs[i + 1] - qs[i])
+        for j in range(n):
+            rows.append(bt[i])
+            row_lens.append(min(max(int(lens[i]) - n + j + 1, 0), int(lens[i])))
+    spec = ops.CacheSpec.of(w)
+    want = ops.decode(spec, w.q_chunk, w.k_cache, w.v_cache,
+                      torch.as_tensor(np.stack(rows), device=DEV),
+                      torch.as_tensor(np.array(row_lens, dtype=np.int32), device=DEV),
+                      w.max_context_len, w.scale, partition_tokens=32)
+    assert same_bits(got, want)
+
+
+def test_prefill_rows_route_bad_offsets_stay_in_range():
+    """A q_start that is not a partition of the rows (a request claiming rows
+    past total_q, one going backwards) reads nothing out of range: rows in no
+    request's range come out as zeros, and the call completes."""
+    say("prefill rows bad offsets")
+    w = _rows_workload("f32", 16, 4, 4, seed=73)
+    bad = w.q_start.clone()
+    total = int(bad[-1])
+    bad[3] = total + 50
+    bad[4] = 2
+    w.q_start = bad
+    out = _run_prefill(w, partition_tokens=32)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+
+
 # ----------------------------------------------------------------------------
 # the MFMA decode path at block sizes 8, 32 and 64
 # ----------------------------------------------------------------------------
