@@ -186,22 +186,54 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 // consumed.  One barrier per pair: after it, the pair is in LDS and every
 // wave is done with the previous pair, whose stages are then refilled.
 
-// LDS stages (an even number) and waves per workgroup sharing them.
-// Measured on the chunked-prefill workload with pairs: 4 waves with 4, 6 or
-// 8 stages 200, 197 and 202 us; 2 waves 261 us, 8 waves 208 us.  (Per tile,
-// with 16x16x16 PV MFMAs, it took 208 us.)  200 VGPRs: two waves per SIMD;
-// held to 168 (three waves) it spills and takes 295 us.
+// LDS stages (an even number), waves per workgroup sharing them, row groups
+// per wave and the occupancy asked of the compiler.  Measured on the
+// chunked-prefill workload (us per call, current loop): 4, 6 or 8 stages
+// 189.0-189.2 alike; 2 waves 249, 8 waves 201; one row group (134 VGPRs,
+// three waves per SIMD, each tile read from LDS for half as many rows) 223,
+// and at four stages held to 128 VGPRs (four waves) 214; three groups 280
+// (one wave per SIMD) or 197 held to 256 VGPRs; four groups 232.  Two groups
+// at 194 VGPRs leave two waves per SIMD; held to 168 (three) they spill.
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 6
 #endif
 #ifndef PA_PREFILL_WAVES
 #define PA_PREFILL_WAVES 4
 #endif
+#ifndef PA_PREFILL_ROW_GROUPS
+#define PA_PREFILL_ROW_GROUPS 2
+#endif
+#ifndef PA_PREFILL_WAVES_PER_SIMD
+#define PA_PREFILL_WAVES_PER_SIMD 1
+#endif
 constexpr int kPrefillStages = PA_PREFILL_STAGES;
 constexpr int kPrefillLdsWaves = PA_PREFILL_WAVES;
+constexpr int kPrefillRowGroups = PA_PREFILL_ROW_GROUPS;
+
+// Workgroups start in grid order, and a request's workgroups run about as
+// long as its history: when the longest requests come last, their
+// workgroups start in the second wave of the grid and set the end of the
+// call.  Requests are therefore taken longest first (ties by index): rank r
+// of the grid's request axis is the request with the r-th longest length.
+// One lane per request ranks it against the others; more than 64 requests
+// keep the grid order.
+__device__ __forceinline__ int longest_first(const int32_t* __restrict__ context_lens,
+                                             int num_seqs, int rank, int len_clamp) {
+    if (num_seqs > 64) return rank;
+    const int lane = threadIdx.x & 63;
+    const int key = lane < num_seqs ? min(max(context_lens[lane], 0), len_clamp) : -1;
+    int r = 0;
+    for (int t = 0; t < num_seqs; ++t) {
+        const int kt = __shfl(key, t);
+        r += (kt > key || (kt == key && t < lane)) ? 1 : 0;
+    }
+    const unsigned long long b = __ballot(lane < num_seqs && r == rank);
+    return b ? __ffsll(b) - 1 : rank;
+}
 
 template <int RG, int S, int W>
-__global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
+__global__ __launch_bounds__(64 * W)
+__attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -214,8 +246,10 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
     constexpr int kCopies = 8 / W;
     __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
     const int h = blockIdx.x;
-    const int seq = blockIdx.y / tiles_per_seq;
-    const int wgt = blockIdx.y - seq * tiles_per_seq;
+    const int rank = blockIdx.y / tiles_per_seq;
+    // a request's last query tokens see the most positions: they go first
+    const int wgt = tiles_per_seq - 1 - (blockIdx.y - rank * tiles_per_seq);
+    const int seq = longest_first(context_lens, gridDim.y / tiles_per_seq, rank, len_clamp);
     const int part = blockIdx.z;
     const int wave = static_cast<int>(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -291,48 +325,64 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
     // the partition's table entries, kTbl at a time, in LDS: the copies need
     // them without a scalar-load wait in the loop
     constexpr int kTbl = 256;
-    __shared__ int tbl[kTbl];
-    auto load_tbl = [&](int t0) {   // entries t0 .. t0 + kTbl - 1 (those < nblk)
-        for (int i = threadIdx.x; i < kTbl && t0 + i < nblk; i += 64 * W)
-            tbl[i] = clamp_block(tab[t0 + i], num_blocks);
+    __shared__ __align__(16) int tbl[kTbl];
+    // entries t0 .. t0 + kTbl - 1; those past the walk repeat its last entry,
+    // so a copy past the end reads a valid block
+    auto load_tbl = [&](int t0) {
+        for (int i = threadIdx.x; i < kTbl; i += 64 * W)
+            tbl[i] = clamp_block(tab[min(t0 + i, nblk - 1)], num_blocks);
         __syncthreads();
     };
     load_tbl(0);
     const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) __bf16*)(&ring[0][0])));
-    // tile t (past the end: the last one again, so every thread issues the same
-    // number of copies per tile) into stage t % S; the stage's 8 KiB are K
+    // tile t (past the end: a block of the walk, so every thread issues the
+    // same number of copies per tile) into stage t % S; the stage's 8 KiB are K
     // then V, and wave w copies KiB w * kCopies .. (w + 1) * kCopies - 1
     // V stage layout: 16-byte chunk c of the tile sits at chunk c ^ ((c >> 4) & 1)
     // (the two chunks of a dim swap for dims 8..15 of every 16), so the 8-byte
     // reads of rows r and r + 8, 256 bytes apart, fall in different LDS banks.
     const int v_swz_lane = lane ^ ((lane >> 4) & 1);
-    auto issue = [&](int t) {
-        const int tc = t < nblk ? t : nblk - 1;
-        const int64_t o = static_cast<int64_t>(tbl[tc % kTbl]) * blk_stride +
-                          static_cast<int64_t>(h) * FTILE;
+    // the block offset is wave-uniform: scalar arithmetic, one SGPR base per
+    // copy and a fixed per-lane byte offset
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    auto issue_e = [&](int t, int e) {
+        const int64_t o = static_cast<int64_t>(e) * blk_stride + static_cast<int64_t>(h) * FTILE;
         const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
-            const int kib = wave * kCopies + c;            // 0..3 K, 4..7 V
-            const __bf16* src = kib < 4 ? k_cache + o + (kib & 3) * 512 + lane * 8
-                                          : v_cache + o + (kib & 3) * 512 + v_swz_lane * 8;
-            lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
+            const int kib = wave_u * kCopies + c;          // 0..3 K, 4..7 V
+            const __bf16* base = (kib < 4 ? k_cache : v_cache) + o + (kib & 3) * 512;
+            const unsigned voff = static_cast<unsigned>((kib < 4 ? lane : v_swz_lane) * 16);
+            lds_copy16_s(base, voff, sb + kib * 1024);
         }
+    };
+    // tiles t, t + 1 (t even): both entries in one 8-byte LDS read (one LDS
+    // round trip per pair); past the walk the window holds its last entry
+    auto issue2 = [&](int t) {
+        const int2 e = *reinterpret_cast<const int2*>(&tbl[static_cast<unsigned>(t) % kTbl]);
+        issue_e(t, __builtin_amdgcn_readfirstlane(e.x));
+        issue_e(t + 1, __builtin_amdgcn_readfirstlane(e.y));
     };
     // Tiles are consumed in pairs (b, b + 1), one barrier per pair; S - 2
     // tiles are in flight while a pair is consumed.
 #pragma unroll
-    for (int t = 0; t < S - 2; ++t) issue(t);
+    for (int t = 0; t < S - 2; t += 2) issue2(t);
     for (int b = 0; b < nblk; b += 2) {
         wait_vmcnt<kCopies * (S - 4)>();         // this thread's copies of tiles b, b + 1 have landed
         __builtin_amdgcn_s_barrier();            // everyone's; and tiles b - 2, b - 1 are consumed
         const int t_next = b + S - 2;            // refilling their stages
         if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare; t_next is even)
-        issue(t_next);
-        issue(t_next + 1);
+        issue2(t_next);
         const int start = tok0 + FBS * b;
         if (start < lim_max) {                   // (wave-uniform) something of it is visible here
+            // raised wave priority while a pair is consumed, normal while the
+            // wave waits at the barrier and issues copies: the SIMD's other
+            // wave (another workgroup) then yields its issue slots to the one
+            // doing matrix and softmax work (189 -> 185 us on the chunked-prefill
+            // workload; raised only around the MFMAs it was slower)
+            __builtin_amdgcn_s_setprio(1);
+            __builtin_amdgcn_sched_barrier(0);
             const __bf16* sa = &ring[b % S][0];
             const __bf16* sb = &ring[(b + 1) % S][0];
             const bool has_b = b + 1 < nblk && start + FBS < lim_max;   // (wave-uniform)
@@ -345,24 +395,27 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
                 for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
                 tile_scores<RG>(s_a, t, qv);
             }
-            if (has_b) {
+            {   // tile b's stage holds landed bytes even past the walk (those
+                // copies read a block of the walk), so it is scored
+                // unconditionally and masked below when no row sees it
                 Tile t;
                 const bf16x8* kp = reinterpret_cast<const bf16x8*>(sb) + lane;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
                 tile_scores<RG>(s_b, t, qv);
-            } else {
-#pragma unroll
-                for (int u = 0; u < RG; ++u) s_b[u] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
-            __builtin_amdgcn_sched_barrier(0);   // V loads after the score MFMAs: fewer live registers
             const int vo = 2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
             const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + FTILE) + vo;
             const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + FTILE) + vo;
+            // volatile: the reads stay one per 8 bytes, in this order, and the
+            // two tiles' pieces of a dim land side by side as one MFMA
+            // operand; merged by the compiler into two-address reads of one
+            // tile, they cost 24 register copies per pair (184 -> 169 us)
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                va[j] = vpa[64 * j];
-                vb[j] = has_b ? vpb[64 * j] : s16x4{0, 0, 0, 0};
+                typedef const volatile __attribute__((address_space(3))) s16x4* lds_v;
+                va[j] = *(lds_v)(vpa + 64 * j);
+                vb[j] = *(lds_v)(vpb + 64 * j);
             }
             // values past the wave's visible positions may be stale bytes
             const int tok_base = 4 * quad;
@@ -385,6 +438,8 @@ __global__ __launch_bounds__(64 * W) void prefill_lds_kernel(
                 rvb[u] = has_b ? clampi(lim[u] - start - FBS, 0, FBS) : 0;
             }
             pair_softmax_pv<RG>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
     }
     wait_vmcnt<0>();                             // no copy may land after the workgroup ends
@@ -450,7 +505,7 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
 // workgroup sharing each tile through LDS.
 int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
-    constexpr int RG = 2;
+    constexpr int RG = kPrefillRowGroups;
     constexpr int W = kPrefillLdsWaves;
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;

@@ -459,6 +459,13 @@ __device__ __forceinline__ void lds_copy16(const void* gptr, unsigned lds_base) 
                  :: "v"(gptr), "s"(lds_base) : "memory");
 }
 
+// The same copy addressed as a wave-uniform base (SGPR pair) plus a 32-bit
+// per-lane byte offset: no 64-bit vector address arithmetic per copy.
+__device__ __forceinline__ void lds_copy16_s(const void* sbase, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {   // at most N vector memory ops outstanding
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
