@@ -188,8 +188,8 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 
 // LDS stages (an even number), waves per workgroup sharing them, row groups
 // per wave and the occupancy asked of the compiler.  Measured on the
-// chunked-prefill workload (us per call, current loop): 4, 6 or 8 stages
-// 189.0-189.2 alike; 2 waves 249, 8 waves 201; one row group (134 VGPRs,
+// chunked-prefill workload (us per call, with the loop at 189 us): 4, 6 or 8
+// stages 189.0-189.2 alike (at 160 us: 160, 161-162, 161-162); 2 waves 249, 8 waves 201; one row group (134 VGPRs,
 // three waves per SIMD, each tile read from LDS for half as many rows) 223,
 // and at four stages held to 128 VGPRs (four waves) 214; three groups 280
 // (one wave per SIMD) or 197 held to 256 VGPRs; four groups 232.  Two groups
@@ -364,6 +364,81 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         issue_e(t, __builtin_amdgcn_readfirstlane(e.x));
         issue_e(t + 1, __builtin_amdgcn_readfirstlane(e.y));
     };
+    // K half of pair b (tiles b, b + 1) into scores: tile b + 1's stage holds
+    // landed bytes even past the walk (those copies read a block of the
+    // walk), so it is scored unconditionally and masked later when no row
+    // sees it
+    auto pair_scores = [&](int b, f32x4 (&s_a)[RG], f32x4 (&s_b)[RG]) {
+        const __bf16* sa = &ring[b % S][0];
+        const __bf16* sb = &ring[(b + 1) % S][0];
+        // the 2 * RG accumulation chains of both tiles advance together, one
+        // 32-dim step at a time: a dependent MFMA waits about three issue
+        // slots for its predecessor, so 2 * RG >= 4 independent chains keep
+        // the matrix pipe full where one tile's RG chains left it idle
+        const bf16x8* kpa = reinterpret_cast<const bf16x8*>(sa) + lane;
+        const bf16x8* kpb = reinterpret_cast<const bf16x8*>(sb) + lane;
+        bf16x8 ka[4], kb[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            ka[s4] = kpa[64 * s4];
+            kb[s4] = kpb[64 * s4];
+        }
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            s_a[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            s_b[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int u = 0; u < RG; ++u) {
+                s_a[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k], qv[u][k], s_a[u], 0, 0, 0);
+                s_b[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[k], qv[u][k], s_b[u], 0, 0, 0);
+            }
+    };
+    // V half of pair b, the masks, the softmax and the PV MFMAs
+    auto pair_consume = [&](int b, f32x4 (&s_a)[RG], f32x4 (&s_b)[RG]) {
+        const int start = tok0 + FBS * b;
+        const __bf16* sa = &ring[b % S][0];
+        const __bf16* sb = &ring[(b + 1) % S][0];
+        const bool has_b = b + 1 < nblk && start + FBS < lim_max;   // (wave-uniform)
+        s16x4 va[8], vb[8];
+        const int vo = 2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
+        const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + FTILE) + vo;
+        const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + FTILE) + vo;
+        // volatile: the reads stay one per 8 bytes, in this order, and the
+        // two tiles' pieces of a dim land side by side as one MFMA
+        // operand; merged by the compiler into two-address reads of one
+        // tile, they cost 24 register copies per pair (184 -> 169 us)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            typedef const volatile __attribute__((address_space(3))) s16x4* lds_v;
+            va[j] = *(lds_v)(vpa + 64 * j);
+            vb[j] = *(lds_v)(vpb + 64 * j);
+        }
+        // values past the wave's visible positions may be stale bytes
+        const int tok_base = 4 * quad;
+        const int va_valid = clampi(lim_max - start, 0, FBS);
+        const int vb_valid = has_b ? clampi(lim_max - start - FBS, 0, FBS) : 0;
+        if (va_valid < FBS || vb_valid < FBS) {   // (wave-uniform)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (tok_base + i >= va_valid) va[j][i] = 0;
+                    if (tok_base + i >= vb_valid) vb[j][i] = 0;
+                }
+        }
+        const bool masked = !has_b || start + 2 * FBS > lim_min;
+        int rva[RG], rvb[RG];
+#pragma unroll
+        for (int u = 0; u < RG; ++u) {
+            rva[u] = clampi(lim[u] - start, 0, FBS);
+            rvb[u] = has_b ? clampi(lim[u] - start - FBS, 0, FBS) : 0;
+        }
+        pair_softmax_pv<RG>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
+    };
+    auto visible = [&](int b) { return tok0 + FBS * b < lim_max; };   // (wave-uniform)
     // Tiles are consumed in pairs (b, b + 1), one barrier per pair; S - 2
     // tiles are in flight while a pair is consumed.
 #pragma unroll
@@ -374,8 +449,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         const int t_next = b + S - 2;            // refilling their stages
         if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare; t_next is even)
         issue2(t_next);
-        const int start = tok0 + FBS * b;
-        if (start < lim_max) {                   // (wave-uniform) something of it is visible here
+        if (visible(b)) {
             // raised wave priority while a pair is consumed, normal while the
             // wave waits at the barrier and issues copies: the SIMD's other
             // wave (another workgroup) then yields its issue slots to the one
@@ -383,61 +457,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             // workload; raised only around the MFMAs it was slower)
             __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_barrier(0);
-            const __bf16* sa = &ring[b % S][0];
-            const __bf16* sb = &ring[(b + 1) % S][0];
-            const bool has_b = b + 1 < nblk && start + FBS < lim_max;   // (wave-uniform)
             f32x4 s_a[RG], s_b[RG];
-            s16x4 va[8], vb[8];
-            {
-                Tile t;
-                const bf16x8* kp = reinterpret_cast<const bf16x8*>(sa) + lane;
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
-                tile_scores<RG>(s_a, t, qv);
-            }
-            {   // tile b's stage holds landed bytes even past the walk (those
-                // copies read a block of the walk), so it is scored
-                // unconditionally and masked below when no row sees it
-                Tile t;
-                const bf16x8* kp = reinterpret_cast<const bf16x8*>(sb) + lane;
-#pragma unroll
-                for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = kp[64 * s4];
-                tile_scores<RG>(s_b, t, qv);
-            }
-            const int vo = 2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
-            const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + FTILE) + vo;
-            const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + FTILE) + vo;
-            // volatile: the reads stay one per 8 bytes, in this order, and the
-            // two tiles' pieces of a dim land side by side as one MFMA
-            // operand; merged by the compiler into two-address reads of one
-            // tile, they cost 24 register copies per pair (184 -> 169 us)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                typedef const volatile __attribute__((address_space(3))) s16x4* lds_v;
-                va[j] = *(lds_v)(vpa + 64 * j);
-                vb[j] = *(lds_v)(vpb + 64 * j);
-            }
-            // values past the wave's visible positions may be stale bytes
-            const int tok_base = 4 * quad;
-            const int va_valid = clampi(lim_max - start, 0, FBS);
-            const int vb_valid = has_b ? clampi(lim_max - start - FBS, 0, FBS) : 0;
-            if (va_valid < FBS || vb_valid < FBS) {   // (wave-uniform)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        if (tok_base + i >= va_valid) va[j][i] = 0;
-                        if (tok_base + i >= vb_valid) vb[j][i] = 0;
-                    }
-            }
-            const bool masked = !has_b || start + 2 * FBS > lim_min;
-            int rva[RG], rvb[RG];
-#pragma unroll
-            for (int u = 0; u < RG; ++u) {
-                rva[u] = clampi(lim[u] - start, 0, FBS);
-                rvb[u] = has_b ? clampi(lim[u] - start - FBS, 0, FBS) : 0;
-            }
-            pair_softmax_pv<RG>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
+            pair_scores(b, s_a, s_b);
+            pair_consume(b, s_a, s_b);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
         }
