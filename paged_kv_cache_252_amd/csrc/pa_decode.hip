@@ -816,15 +816,33 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_ke
             const int r = newest_member(c);
             if (r >= 0) {
                 substitute(t, r);
-                if ((cow_members >> r) & 1ull) {     // the copy, with the token in it
-                    const int64_t o = static_cast<int64_t>(task_phys(c)) * blk_stride;
-                    store_tile(t, const_cast<__bf16*>(k_head) + o, const_cast<__bf16*>(v_head) + o, lane);
-                }
             }
         }
         consume_tile_rows(st, t, qv, scale_log2, lane, row_valid, v_valid, masked);
     };
 
+    // The copies first: each member whose newest token this partition holds
+    // has that tile read from its source block, the token put in, and the
+    // tile written to its own block before the walk starts (the walk reads it
+    // from the source again; 139 against 142 us on the fan-out step, where the
+    // copies, written at the end of each walk, met the read stream of the
+    // waves still walking)
+    if constexpr (APPEND) {
+        if (cow_members != 0) {
+#pragma unroll
+            for (int r = 0; r < MAXR; ++r) {
+                int Lm;
+                if (!((cow_members >> r) & 1ull) || !appends_here(r, Lm)) continue;
+                const int jl = (Lm - 1) / FBS - blk0;
+                Tile t;
+                const int64_t so = static_cast<int64_t>(__builtin_amdgcn_readlane(cow_r, r)) * blk_stride;
+                load_tile<NT>(t, k_head + so, v_head + so, lane);
+                substitute(t, r);
+                const int64_t dst = static_cast<int64_t>(__builtin_amdgcn_readlane(phys[r], jl)) * blk_stride;
+                store_tile(t, const_cast<__bf16*>(k_head) + dst, const_cast<__bf16*>(v_head) + dst, lane);
+            }
+        }
+    }
     // Two tiles in flight, as on the fast path; past the last task the
     // prefetch repeats the current tile (still in cache).
     Tile ta, tb;
