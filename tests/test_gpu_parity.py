@@ -1304,6 +1304,29 @@ def test_decode_step_fanout(grouped, stream_kv, part):
     assert_close(w, got, oracle_decode(w), "decode_step fan-out")
 
 
+@pytest.mark.parametrize("branches", [3, 5, 1])
+def test_decode_step_fanout_mixed_groups(branches):
+    """Groups of consecutive requests that span prompts (3 or 5 branches per
+    prompt against 4 members per wave; 1: every member its own prompt): the
+    grouped step's copies load a new source tile where the source or the
+    newest slot changes and reuse it where both match, and the pool bytes
+    and outputs equal copy + append + decode."""
+    say(f"decode_step fan-out mixed groups branches={branches}")
+    w = inputs.fanout(num_prompts=7, branches=branches, prompt_lo=20, prompt_hi=300,
+                      num_blocks=500, device=DEV, seed=9 + branches)
+    spec = ops.CacheSpec.of(w)
+    cow_src = _cow_src_of(w)
+    assert int((cow_src >= 0).sum()) == w.cow_pairs.shape[0]
+    for part in (0, 64):
+        k0, v0 = w.k_cache.clone(), w.v_cache.clone()
+        ref, got = _step_both_ways(w, spec, w.cow_pairs, cow_src, partition_tokens=part,
+                                   stream_kv=True, group_shared=True)
+        assert same_bits(got, ref)
+        assert_close(w, got, oracle_decode(w), f"decode_step mixed groups part={part}")
+        w.k_cache.copy_(k0)
+        w.v_cache.copy_(v0)
+
+
 @pytest.mark.parametrize("dtype,bs,d,hq", [("bf16", 16, 128, 8), ("bf16", 32, 128, 8),
                                            ("bf16", 8, 128, 32), ("f32", 16, 64, 4),
                                            ("bf16", 16, 64, 8), ("bf16", 16, 256, 8),
