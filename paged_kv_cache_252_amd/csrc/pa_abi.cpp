@@ -170,10 +170,18 @@ int check_heads(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads)
     return PA_OK;
 }
 
-// Several query tokens per request: 16 / g tokens per wave.
-bool prefill_shape_ok(const pa_cache_desc_t* c, int group) {
-    return fast_path_ok(c, group) && 16 % group == 0;
+// Several query tokens per request: 16 / g tokens per wave.  The LDS kernel
+// takes blocks of 8, 16, 32 or 64; the kernel for short chunks (fewer than
+// two row groups of tokens) blocks of 16 only.
+bool prefill_mfma_ok(const pa_cache_desc_t* c, int group, int32_t max_q_len) {
+    const int bs = c->block_size;
+    if (c->dtype != PA_BF16 || c->head_dim != 128 || group < 1 || group > 16 || 16 % group != 0)
+        return false;
+    if (bs == 16) return true;
+    return (bs == 8 || bs == 32 || bs == 64) && max_q_len >= 2 * (16 / group);
 }
+
+int prefill_granule(const pa_cache_desc_t* c) { return c->block_size > 16 ? c->block_size : 16; }
 
 int64_t prefill_waves_rows(int32_t num_seqs, int32_t max_q_len, int group) {
     const int per = 16 / group;
@@ -216,19 +224,20 @@ constexpr int32_t kMaxPrefillPartitionTokens = 1 << 20;
 int prefill_partition(const pa_cache_desc_t* c, int32_t num_seqs, int32_t max_q_len,
                       int32_t num_q_heads, int32_t max_context_len, int32_t requested,
                       int32_t* out) {
+    const int g = prefill_granule(c);
     if (requested != 0) {
-        if (requested < 16 || requested > kMaxPrefillPartitionTokens || requested % 16 != 0)
-            return fail(PA_ERR_SHAPE, "partition_tokens %d must be a multiple of 16 in [16, %d]",
-                        requested, kMaxPrefillPartitionTokens);
+        if (requested < g || requested > kMaxPrefillPartitionTokens || requested % g != 0)
+            return fail(PA_ERR_SHAPE, "partition_tokens %d must be a multiple of %d in [%d, %d]",
+                        requested, g, g, kMaxPrefillPartitionTokens);
         *out = requested;
         return PA_OK;
     }
     const int64_t waves = prefill_waves_rows(num_seqs, max_q_len, num_q_heads / c->num_kv_heads) *
                           c->num_kv_heads;
     const int64_t target = static_cast<int64_t>(device_cu_count()) * kWavesPerCu;
-    const int64_t whole = std::max<int64_t>(ceil_div(std::max(max_context_len, 1), 16) * 16, 16);
+    const int64_t whole = std::max<int64_t>(ceil_div(std::max(max_context_len, 1), g) * g, g);
     const int64_t splits = std::max<int64_t>(1, ceil_div(target, std::max<int64_t>(waves, 1)));
-    int64_t p = ceil_div(ceil_div(whole, splits), 16) * 16;
+    int64_t p = ceil_div(ceil_div(whole, splits), g) * g;
     p = std::max<int64_t>(std::min<int64_t>(p, whole), std::min<int64_t>(whole, kMinAutoPartitionTokens));
     *out = static_cast<int32_t>(std::min<int64_t>(p, kMaxPrefillPartitionTokens));
     return PA_OK;
@@ -541,7 +550,7 @@ size_t pa_prefill_workspace_bytes(const pa_cache_desc_t* c, int32_t num_seqs, in
     if (check_desc(c) || check_heads(c, num_seqs, num_q_heads) || total_q < 0 || max_q_len < 0)
         return 0;
     int32_t part = 0;
-    if (!prefill_shape_ok(c, num_q_heads / c->num_kv_heads)) {
+    if (!prefill_mfma_ok(c, num_q_heads / c->num_kv_heads, max_q_len)) {
         if (resolve_partition(c, total_q, num_q_heads, max_context_len, partition_tokens, &part))
             return 0;
         return prefill_rows_workspace(c, total_q, num_q_heads, max_context_len, part);
@@ -563,7 +572,7 @@ int pa_prefill(const pa_cache_desc_t* c, const void* k_cache, const void* v_cach
     if ((st = check_heads(c, num_seqs, num_q_heads))) return st;
     const int group = num_q_heads / c->num_kv_heads;
     // outside the MFMA prefill kernels' set, each query row is a decode request
-    const bool as_rows = !prefill_shape_ok(c, group);
+    const bool as_rows = !prefill_mfma_ok(c, group, max_q_len);
     if (total_q < 0 || total_q > kMaxGridYZ)
         return fail(PA_ERR_SHAPE, "total_q %d outside [0, %d]", total_q, kMaxGridYZ);
     if (max_q_len < 0) return fail(PA_ERR_SHAPE, "max_q_len %d < 0", max_q_len);

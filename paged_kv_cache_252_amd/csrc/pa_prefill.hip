@@ -231,7 +231,7 @@ __device__ __forceinline__ int longest_first(const int32_t* __restrict__ context
     return b ? __ffsll(b) - 1 : rank;
 }
 
-template <int RG, int S, int W>
+template <int RG, int S, int W, int BS>
 __global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
@@ -243,7 +243,12 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
     static_assert(W == 2 || W == 4 || W == 8, "a tile is 8 KiB: 8 / W copies of 1 KiB per wave");
     static_assert(S % 2 == 0 && S >= 4, "stages hold whole pairs of tiles");
+    static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64,
+                  "blocks of half, one, two or four 16-position tiles");
     constexpr int kCopies = 8 / W;
+    constexpr int SUB = BS >= FBS ? BS / FBS : 1;  // tiles per block, back to back in its head region
+    // the first block entry of tile t (blocks of 8: a tile is two blocks)
+    auto first_entry = [](int t) { return BS == 8 ? 2 * t : t / SUB; };
     __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
     const int h = blockIdx.x;
     const int rank = blockIdx.y / tiles_per_seq;
@@ -319,18 +324,19 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int blk0 = tok0 / FBS;
-    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;
+    const int blk0 = tok0 / BS;                  // (partitions are whole blocks)
+    const int nblk = (tok1 - tok0 + FBS - 1) / FBS;   // tiles of the walk
+    const int nent = (tok1 - tok0 + BS - 1) / BS;     // blocks of the walk
     const int32_t* tab = block_tables + static_cast<int64_t>(seq) * max_blocks_per_seq + blk0;
     // the partition's table entries, kTbl at a time, in LDS: the copies need
     // them without a scalar-load wait in the loop
     constexpr int kTbl = 256;
     __shared__ __align__(16) int tbl[kTbl];
-    // entries t0 .. t0 + kTbl - 1; those past the walk repeat its last entry,
-    // so a copy past the end reads a valid block
-    auto load_tbl = [&](int t0) {
+    // block entries e0 .. e0 + kTbl - 1; those past the walk repeat its last
+    // entry, so a copy past the end reads a valid block
+    auto load_tbl = [&](int e0) {
         for (int i = threadIdx.x; i < kTbl; i += 64 * W)
-            tbl[i] = clamp_block(tab[min(t0 + i, nblk - 1)], num_blocks);
+            tbl[i] = clamp_block(tab[min(e0 + i, nent - 1)], num_blocks);
         __syncthreads();
     };
     load_tbl(0);
@@ -346,8 +352,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     // the block offset is wave-uniform: scalar arithmetic, one SGPR base per
     // copy and a fixed per-lane byte offset
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    auto issue_e = [&](int t, int e) {
-        const int64_t o = static_cast<int64_t>(e) * blk_stride + static_cast<int64_t>(h) * FTILE;
+    auto issue_e = [&](int t, int e) {   // tile t of the walk, from block e
+        const int64_t o = static_cast<int64_t>(e) * blk_stride +
+                          static_cast<int64_t>(h) * (SUB * FTILE) + static_cast<int64_t>(t % SUB) * FTILE;
         const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
@@ -359,10 +366,44 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     };
     // tiles t, t + 1 (t even): both entries in one 8-byte LDS read (one LDS
     // round trip per pair); past the walk the window holds its last entry
+    // Blocks of 8: the tile's positions 0..7 come from block ea, 8..15 from
+    // eb (per block and head, K [D/8][8][8] and V [D][8]); each lane copies
+    // the 16 bytes that land at its LDS chunk, from a vector address.
+    auto issue_e8 = [&](int t, int ea, int eb) {
+        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
+        const int64_t oa = static_cast<int64_t>(ea) * blk_stride + static_cast<int64_t>(h) * (8 * FD);
+        const int64_t ob = static_cast<int64_t>(eb) * blk_stride + static_cast<int64_t>(h) * (8 * FD);
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) {
+            const int kib = wave_u * kCopies + c;          // 0..3 K, 4..7 V
+            const __bf16* src;
+            if (kib < 4) {                                 // chunk (dims 8c'..8c'+7, position r)
+                const int C = (kib & 3) * 64 + lane;
+                const int cc = C >> 4, r = C & 15;
+                src = k_cache + (r < 8 ? oa : ob) + (cc * 8 + (r & 7)) * 8;
+            } else {                                       // chunk (dim d, positions 8*half..)
+                const int G = (kib & 3) * 64 + v_swz_lane;
+                src = v_cache + ((G & 1) ? ob : oa) + (G >> 1) * 8;
+            }
+            lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
+        }
+    };
+    // (blocks of 32 or 64: tiles t, t + 1 lie in one block, one entry;
+    // blocks of 8: four entries, one 16-byte LDS read)
     auto issue2 = [&](int t) {
-        const int2 e = *reinterpret_cast<const int2*>(&tbl[static_cast<unsigned>(t) % kTbl]);
-        issue_e(t, __builtin_amdgcn_readfirstlane(e.x));
-        issue_e(t + 1, __builtin_amdgcn_readfirstlane(e.y));
+        if constexpr (BS == 8) {
+            const int4 e = *reinterpret_cast<const int4*>(&tbl[static_cast<unsigned>(2 * t) % kTbl]);
+            issue_e8(t, __builtin_amdgcn_readfirstlane(e.x), __builtin_amdgcn_readfirstlane(e.y));
+            issue_e8(t + 1, __builtin_amdgcn_readfirstlane(e.z), __builtin_amdgcn_readfirstlane(e.w));
+        } else if constexpr (SUB == 1) {
+            const int2 e = *reinterpret_cast<const int2*>(&tbl[static_cast<unsigned>(t) % kTbl]);
+            issue_e(t, __builtin_amdgcn_readfirstlane(e.x));
+            issue_e(t + 1, __builtin_amdgcn_readfirstlane(e.y));
+        } else {
+            const int e = __builtin_amdgcn_readfirstlane(tbl[static_cast<unsigned>(t / SUB) % kTbl]);
+            issue_e(t, e);
+            issue_e(t + 1, e);
+        }
     };
     // K half of pair b (tiles b, b + 1) into scores: tile b + 1's stage holds
     // landed bytes even past the walk (those copies read a block of the
@@ -447,7 +488,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         wait_vmcnt<kCopies * (S - 4)>();         // this thread's copies of tiles b, b + 1 have landed
         __builtin_amdgcn_s_barrier();            // everyone's; and tiles b - 2, b - 1 are consumed
         const int t_next = b + S - 2;            // refilling their stages
-        if (t_next % kTbl == 0 && t_next < nblk) load_tbl(t_next);   // (uniform, rare; t_next is even)
+        // (uniform, rare; t_next is even, so it meets the first tile of every block)
+        if (t_next % SUB == 0 && first_entry(t_next) % kTbl == 0 && t_next < nblk)
+            load_tbl(first_entry(t_next));
         issue2(t_next);
         if (visible(b)) {
             // raised wave priority while a pair is consumed, normal while the
@@ -525,14 +568,15 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
 
 // Longer chunks: two row groups per wave, kPrefillLdsWaves waves per
 // workgroup sharing each tile through LDS.
-int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
+template <int BS>
+int launch_prefill_lds_bs(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
     constexpr int RG = kPrefillRowGroups;
     constexpr int W = kPrefillLdsWaves;
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages, W>), grid, dim3(64 * W), 0, a.stream,
+    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages, W, BS>), grid, dim3(64 * W), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
@@ -540,6 +584,16 @@ int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
                        sl2, q_sign, static_cast<__bf16*>(a.out), a.ws_acc, a.ws_m, a.ws_l,
                        p.ws_len);
     return check_launch("prefill");
+}
+
+int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
+    switch (p.d.block_size) {
+        case 8: return launch_prefill_lds_bs<8>(p, sl2, q_sign);
+        case 16: return launch_prefill_lds_bs<16>(p, sl2, q_sign);
+        case 32: return launch_prefill_lds_bs<32>(p, sl2, q_sign);
+        case 64: return launch_prefill_lds_bs<64>(p, sl2, q_sign);
+        default: return fail(PA_ERR_UNSUPPORTED, "prefill: block size %d", p.d.block_size);
+    }
 }
 
 }  // namespace
@@ -556,8 +610,10 @@ int launch_prefill(const PrefillArgs& p) {
     // (measured on the chunked-prefill workload with tiles in registers: 1
     // group 431 us, 2 groups 273 us, 4 groups 368 us -- 332 VGPRs leave one
     // wave per SIMD; staging the tiles in LDS then took it to 217 us)
-    const int st = p.max_q_len >= 2 * (FG / a.group) ? launch_prefill_lds(p, sl2, q_sign)
-                                                     : launch_prefill_short(p, sl2, q_sign);
+    const bool lds = p.max_q_len >= 2 * (FG / a.group);
+    if (!lds && a.block_size != FBS)   // (the host runs such calls as decodes)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: short chunks need blocks of 16");
+    const int st = lds ? launch_prefill_lds(p, sl2, q_sign) : launch_prefill_short(p, sl2, q_sign);
     if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
     return launch_merge(p.ws_len, p.total_q, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
                         a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);

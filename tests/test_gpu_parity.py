@@ -982,6 +982,46 @@ def test_prefill_long_history_one_partition():
         assert_close(w, _run_prefill(w, partition_tokens=part), want, f"prefill long part={part}")
 
 
+@pytest.mark.parametrize("bs", [8, 32, 64])
+@pytest.mark.parametrize("group", [1, 4, 16])
+@pytest.mark.parametrize("part", [0, 2])
+def test_prefill_block_sizes(bs, group, part):
+    """The MFMA prefill at blocks of 8, 32 and 64 positions (half, two or four
+    16-position tiles per block, positions past a request's length poisoned),
+    whole histories and split ones (partitions of two blocks, merged), against
+    the oracle; a short chunk (fewer than two row groups of tokens) runs as
+    per-row decodes and is checked too."""
+    say(f"prefill bs={bs} g={group} part={part}")
+    hkv = 2
+    lens = [1, 15, 16, 17, 40, 100, 0, 77, 33, 250]
+    w = inputs.paged_random("pfb", len(lens), 0, 250, hkv * group, hkv, block_size=bs,
+                            num_blocks=120, seed=68, device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_query_chunks(w, [1, 15, 3, 17, 40, 9, 2, 0, 35, 120])
+    split = part * max(bs, 16)
+    out = _run_prefill(w, partition_tokens=split)
+    assert_close(w, out, _oracle_prefill(w), f"prefill bs={bs} g={group} part={part}")
+    short = max(1, 2 * 16 // group - 1)
+    inputs.add_query_chunks(w, [min(short, L) for L in lens])
+    out = _run_prefill(w, partition_tokens=split)
+    assert_close(w, out, _oracle_prefill(w), f"prefill short bs={bs} g={group}")
+
+
+@pytest.mark.parametrize("bs", [8, 64])
+def test_prefill_block_sizes_long_history(bs):
+    """Blocks of 8 and 64 and a history of more than 256 blocks (the kernel holds
+    the partition's block entries in LDS 256 at a time and refills them)."""
+    say(f"prefill bs={bs} long history")
+    lens = [20011, 300]
+    w = inputs.paged_random("pfbl", len(lens), 0, max(lens), 8, 2, block_size=bs,
+                            num_blocks=20400 // bs + 8, seed=69, device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_query_chunks(w, [40, 17])
+    want = _oracle_prefill(w)
+    for part in (1 << 15, 4096):
+        assert_close(w, _run_prefill(w, partition_tokens=part), want, f"prefill bs={bs} long part={part}")
+
+
 def test_prefill_validate_rejects_bad_offsets(monkeypatch):
     say("prefill PA_VALIDATE")
     monkeypatch.setenv("PA_VALIDATE", "1")
