@@ -361,103 +361,6 @@ __device__ __forceinline__ void tile_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&
     }
 }
 
-// tile_softmax_pv for two tiles A and B at once (32 positions), for the
-// several-token kernels, whose matrix work is the bound.  The bf16 MFMA of K
-// 32 costs the same issue time as the one of K 16 (measured on gfx950), so
-// the PV of both tiles is one 16x16x32 MFMA per 16 dims instead of two
-// 16x16x16: lane l's eight K slots are A's positions 4*(l/16)..+3 then B's,
-// which is how the lane already holds both V operands (va, vb) and both
-// tiles' probabilities, so nothing moves between lanes.  The running maximum
-// is raised at most once per pair.  The caller has masked V past the
-// visible positions of each tile (a tile with nothing visible: V all zero,
-// row_valid 0).
-template <int RG>
-__device__ __forceinline__ void pair_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&sa)[RG],
-                                                f32x4 (&sb)[RG], const s16x4 (&va)[8],
-                                                const s16x4 (&vb)[8], float scale_log2, int lane,
-                                                const int (&rva)[RG], const int (&rvb)[RG],
-                                                bool masked) {
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    const int tok_base = 4 * (lane >> 4);
-    float mx[RG];
-    bool raise[RG];
-    bool any = false;
-#pragma unroll
-    for (int u = 0; u < RG; ++u) {
-        if (masked) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (tok_base + i >= rva[u]) sa[u][i] = -INFINITY;
-                if (tok_base + i >= rvb[u]) sb[u][i] = -INFINITY;
-            }
-        }
-        if constexpr (RG == 2) {   // the lane's maximum; rows combined below for both groups at once
-            float x = vmax3(sa[u][0], sa[u][1], sa[u][2]);
-            x = vmax3(sa[u][3], sb[u][0], x);
-            x = vmax3(sb[u][1], sb[u][2], x);
-            mx[u] = vmax(sb[u][3], x);
-            continue;
-        }
-        const float ma = vmax3(sa[u][0], sa[u][1], vmax(sa[u][2], sa[u][3]));
-        const float mb = vmax3(sb[u][0], sb[u][1], vmax(sb[u][2], sb[u][3]));
-        mx[u] = vmax_across_rows(vmax(ma, mb)) * scale_log2;
-        raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
-        any = any || raise[u];
-    }
-    if constexpr (RG == 2) {
-        // Both groups' row maxima with three row swaps instead of four: the
-        // first swaps group 0's odd rows against group 1's even rows, so the
-        // pairwise maximum holds group 0 in rows 0, 2 and group 1 in rows 1,
-        // 3; the second completes each; the third hands every row both.
-        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[0]), __float_as_uint(mx[1]),
-                                                  false, false);
-        const float m1 = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
-                                                  false);
-        const float m2 = vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
-        auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(m2), __float_as_uint(m2), false,
-                                                  false);
-        mx[0] = __uint_as_float(c[0]) * scale_log2;
-        mx[1] = __uint_as_float(c[1]) * scale_log2;
-#pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
-            any = any || raise[u];
-        }
-    }
-    if (__builtin_amdgcn_ballot_w64(any) != 0) {   // wave-uniform
-#pragma unroll
-        for (int u = 0; u < RG; ++u) {
-            const float alpha = raise[u] ? fast_exp2(st[u].m - mx[u]) : 1.f;
-            st[u].m = raise[u] ? mx[u] : st[u].m;
-            st[u].l *= alpha;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) st[u].acc[j] *= alpha;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < RG; ++u) {
-        const float nm = -st[u].m;
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(__builtin_fmaf(sa[u][i], scale_log2, nm));
-            p[4 + i] = fast_exp2(__builtin_fmaf(sb[u][i], scale_log2, nm));
-        }
-        const u32x4 pp = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-        st[u].l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pp);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const s16x8 v = __builtin_shufflevector(va[j], vb[j], 0, 1, 2, 3, 4, 5, 6, 7);
-            st[u].acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb,
-                                                                  st[u].acc[j], 0, 0, 0);
-        }
-    }
-}
-
 template <int RG>
 __device__ __forceinline__ void consume_tile_groups(SoftmaxState (&st)[RG], Tile& t,
                                                     const bf16x8 (&qv)[RG][4], float scale_log2,
