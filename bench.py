@@ -1,7 +1,7 @@
 """Benchmark of the paged decode hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout|prefill]
-                    [--extra prefix,long,fanout,prefill|none]
+    python bench.py [--steps K] [--warmup W] [--workload gqa|prefix|long|fanout|prefill|...]
+                    [--extra prefix,long,fanout,prefill,...|none]
 
 A step is one pass of the whole hot path over one batch of synthetic
 requests: ``pa_decode_step``, which makes each request's copy-on-write copy
@@ -25,6 +25,7 @@ measured the same way in the same run, each with a shorter oracle sample.
 from __future__ import annotations
 
 import argparse
+import functools
 import json
 import math
 import os
@@ -62,10 +63,20 @@ WORKLOADS = {
     "long": dict(make=inputs.long_context, replicas=1,
                  desc="long context: 8 requests, context U[32768,131072], 64 q / 8 KV heads, "
                       "head_dim 128, block 16, bf16, pool sized to fit"),
-    "prefill": dict(make=inputs.prefill_chunk, replicas=4,
+    "prefill": dict(make=inputs.prefill_chunk, replicas=4, prefill=True,
                     desc="chunked prefill after a prefix-cache hit: 16 requests, U[1024,3072] "
                          "cached positions + 256 new query tokens each attending causally, "
                          "32 q / 8 KV heads, head_dim 128, block 16, bf16"),
+    "prefill_d64": dict(make=functools.partial(inputs.prefill_chunk, head_dim=64), replicas=4,
+                        prefill=True,
+                        desc="chunked prefill at head_dim 64: 16 requests, U[1024,3072] cached "
+                             "positions + 256 new query tokens each attending causally, "
+                             "32 q / 8 KV heads, block 16, bf16"),
+    "prefill_d256": dict(make=functools.partial(inputs.prefill_chunk, head_dim=256), replicas=4,
+                         prefill=True,
+                         desc="chunked prefill at head_dim 256: 16 requests, U[1024,3072] cached "
+                              "positions + 256 new query tokens each attending causally, "
+                              "32 q / 8 KV heads, block 16, bf16"),
     "fanout": dict(make=inputs.fanout, replicas=1,
                    desc="fan-out step: 128 prompts x 4 branches, prompt U[256,2048] with a "
                         "partial last block, copy-on-write of that block per branch, one new "
@@ -372,11 +383,11 @@ def measure_decode(name: str, args, dev, replicas: int, partition: int, cpu_budg
     return res
 
 
-def measure_prefill(args, dev, replicas: int, partition: int, cpu_budget: float) -> dict:
+def measure_prefill(name, args, dev, replicas: int, partition: int, cpu_budget: float) -> dict:
     """A prefill step writes each request's new chunk of K/V (pa_write_kv) and
     runs pa_prefill for the chunk's queries."""
-    cfg = WORKLOADS["prefill"]
-    log("generating prefill")
+    cfg = WORKLOADS[name]
+    log(f"generating {name}")
     w = cfg["make"](device=dev, poison=False)
     spec = ops.CacheSpec.of(w)
     reps = replicas or cfg["replicas"]
@@ -402,7 +413,7 @@ def measure_prefill(args, dev, replicas: int, partition: int, cpu_budget: float)
                                        max_len, part)
     workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(w.q_chunk) for _ in tables]
-    log(f"prefill: {w.num_seqs} requests, {total_q} query rows, max len {max_len}, "
+    log(f"{name}: {w.num_seqs} requests, {total_q} query rows, max len {max_len}, "
         f"workspace {need} B, {reps} replicas")
 
     def attend(r):
@@ -421,8 +432,8 @@ def measure_prefill(args, dev, replicas: int, partition: int, cpu_budget: float)
     torch.cuda.synchronize()
     for r in range(1, reps):
         if not torch.equal(outs[r].view(torch.int16), outs[0].view(torch.int16)):
-            raise RuntimeError("prefill: replica outputs differ")
-    log(f"prefill: timing {args.steps} steps")
+            raise RuntimeError(f"{name}: replica outputs differ")
+    log(f"{name}: timing {args.steps} steps")
     ms = time_steps(step, args.steps, reps)
     us = time_calls(attend, args.kernel_iters, reps, dev)
     flops = prefill_flops(w)
@@ -430,11 +441,11 @@ def measure_prefill(args, dev, replicas: int, partition: int, cpu_budget: float)
     e = 2
     qo = 2 * total_q * w.num_q_heads * w.head_dim * e
     write = 2 * 2 * total_q * w.num_kv_heads * w.head_dim * e + 8 * total_q
-    res = {"name": "prefill", "desc": cfg["desc"], "w": w, "reps": reps, "part": part,
+    res = {"name": name, "prefill": True, "desc": cfg["desc"], "w": w, "reps": reps, "part": part,
            "ms_per_step": ms, "prefill_us": us, "flops": flops, "kv_unique": db["kv_unique"],
            "step_bytes": db["kv_unique"] + qo + write, "total_q": total_q}
     if cpu_budget > 0:
-        log(f"prefill: timing the CPU oracle ({cpu_budget:.0f} s budget)")
+        log(f"{name}: timing the CPU oracle ({cpu_budget:.0f} s budget)")
         res["cpu_baseline"] = cpu_baseline_prefill(w, cpu_budget)
     del outs, workspace, tables
     return res
@@ -489,7 +500,7 @@ def prefill_line(r: dict, args, copy_gbs) -> dict:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": r["desc"], "name": "prefill", "requests": w.num_seqs,
+        "config": {"workload": r["desc"], "name": r["name"], "requests": w.num_seqs,
                    "query_rows": r["total_q"], "max_context_len": w.max_context_len,
                    "replicas": r["reps"], "partition_tokens": r["part"]},
         "tokens_per_s": round(r["total_q"] / (ms * 1e-3), 1),
@@ -508,7 +519,7 @@ def prefill_line(r: dict, args, copy_gbs) -> dict:
 def workload_entry(r: dict) -> dict:
     """The compact record of one extra workload for the ``workloads`` object."""
     w, ms = r["w"], r["ms_per_step"]
-    if r["name"] == "prefill":
+    if r.get("prefill"):
         us = r["prefill_us"]
         tflops = r["flops"] / (us * 1e-6) / 1e12
         e = {"workload": r["desc"], "prefill_us": round(us, 3), "step_us": round(ms * 1e3, 3),
@@ -564,7 +575,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="gqa", choices=sorted(WORKLOADS),
                     help="the headline workload of the JSON line")
-    ap.add_argument("--extra", default="prefix,long,fanout,prefill,gqa_d64,gqa_d256,gqa_f32",
+    ap.add_argument("--extra", default="prefix,long,fanout,prefill,gqa_d64,gqa_d256,gqa_f32,"
+                                       "prefill_d64,prefill_d256",
                     help="comma-separated workloads also measured into the line's 'workloads' "
                          "object ('none' = only the headline)")
     ap.add_argument("--replicas", type=int, default=0, help="0 = the workload's default")
@@ -607,8 +619,8 @@ def main() -> int:
     # pool placed in memory that an earlier pool of the same process freed
     # decodes 3-7 % slower.  (All pools together take about 40 GB of HBM.)
     pools = []
-    if args.workload == "prefill":
-        r = measure_prefill(args, dev, args.replicas, args.partition, budget)
+    if WORKLOADS[args.workload].get("prefill"):
+        r = measure_prefill(args.workload, args, dev, args.replicas, args.partition, budget)
         line = prefill_line(r, args, copy_gbs)
     else:
         r = measure_decode(args.workload, args, dev, args.replicas, args.partition, budget,
@@ -620,8 +632,8 @@ def main() -> int:
         line["workloads"] = {}
         ebudget = 0.0 if args.no_cpu_baseline else args.extra_cpu_budget
         for name in extra:
-            if name == "prefill":
-                r = measure_prefill(args, dev, 0, 0, ebudget)
+            if WORKLOADS[name].get("prefill"):
+                r = measure_prefill(name, args, dev, 0, 0, ebudget)
             else:
                 r = measure_decode(name, args, dev, 0, 0, ebudget)
             line["workloads"][name] = workload_entry(r)

@@ -174,11 +174,13 @@ int check_heads(const pa_cache_desc_t* c, int32_t num_seqs, int32_t num_q_heads)
 // takes blocks of 8, 16, 32 or 64; the kernel for short chunks (fewer than
 // two row groups of tokens) blocks of 16 only.
 bool prefill_mfma_ok(const pa_cache_desc_t* c, int group, int32_t max_q_len) {
-    const int bs = c->block_size;
-    if (c->dtype != PA_BF16 || c->head_dim != 128 || group < 1 || group > 16 || 16 % group != 0)
+    const int bs = c->block_size, d = c->head_dim;
+    if (c->dtype != PA_BF16 || (d != 64 && d != 128 && d != 256) || group < 1 || group > 16 ||
+        16 % group != 0 || (bs != 8 && bs != 16 && bs != 32 && bs != 64))
         return false;
-    if (bs == 16) return true;
-    return (bs == 8 || bs == 32 || bs == 64) && max_q_len >= 2 * (16 / group);
+    // chunks shorter than two query tiles per wave: the register-tile
+    // kernel, which takes blocks of 16 at head_dim 128 only
+    return max_q_len >= 2 * (16 / group) || (bs == 16 && d == 128);
 }
 
 int prefill_granule(const pa_cache_desc_t* c) { return c->block_size > 16 ? c->block_size : 16; }

@@ -1572,12 +1572,20 @@ int launch_grouped_r(const DecodeArgs& a) {
 
 }  // namespace
 
-int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t len_clamp,
-                 int32_t part_tokens, int32_t max_parts, const float* ws_acc, const float* ws_m,
-                 const float* ws_l, void* out, hipStream_t stream) {
+int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                 int32_t len_clamp, int32_t part_tokens, int32_t max_parts, const float* ws_acc,
+                 const float* ws_m, const float* ws_l, void* out, hipStream_t stream) {
     // rows here are query rows, each with its own visible length in lens
-    return merge_bf16(lens, static_cast<int64_t>(rows) * num_q_heads, num_q_heads, len_clamp, part_tokens,
-                      max_parts, ws_acc, ws_m, ws_l, out, stream);
+    if (head_dim == 128)
+        return merge_bf16(lens, static_cast<int64_t>(rows) * num_q_heads, num_q_heads, len_clamp,
+                          part_tokens, max_parts, ws_acc, ws_m, ws_l, out, stream);
+    if (rows == 0) return PA_OK;
+    auto kernel = head_dim == 64 ? reduce_kernel<uint16_t, 64> : reduce_kernel<uint16_t, 256>;
+    if (head_dim != 64 && head_dim != 256) return fail(PA_ERR_UNSUPPORTED, "merge: head_dim %d", head_dim);
+    hipLaunchKernelGGL(kernel, dim3(num_q_heads, static_cast<unsigned>(rows)), dim3(kMergeThreads), 0, stream,
+                       lens, num_q_heads, len_clamp, part_tokens, max_parts, ws_acc, ws_m, ws_l,
+                       static_cast<uint16_t*>(out));
+    return check_launch("merge");
 }
 
 int launch_decode(const DecodeArgs& a_in) {

@@ -152,13 +152,13 @@ int launch_prefill_rows(const int32_t* q_start, const int32_t* block_tables,
                         int32_t max_blocks_per_seq, int32_t row_blocks, int32_t len_clamp,
                         int32_t* row_tables, int32_t* row_lens, hipStream_t stream);
 
-// The split-K merge of bf16, head_dim 128 partials: row r (of `rows`) and
-// query head hq combine the ceil(lens[r] / part_tokens) partitions of
-// ws_* [rows][Hq][max_parts] into out[r][hq] (rows with one partition are
-// left alone: their kernel wrote them).
-int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t len_clamp,
-                 int32_t part_tokens, int32_t max_parts, const float* ws_acc, const float* ws_m,
-                 const float* ws_l, void* out, hipStream_t stream);
+// The split-K merge of bf16 partials at head_dim 64, 128 or 256: row r (of
+// `rows`) and query head hq combine the ceil(lens[r] / part_tokens)
+// partitions of ws_* [rows][Hq][max_parts] into out[r][hq] (rows with one
+// partition are left alone: their kernel wrote them).
+int launch_merge(const int32_t* lens, int32_t rows, int32_t num_q_heads, int32_t head_dim,
+                 int32_t len_clamp, int32_t part_tokens, int32_t max_parts, const float* ws_acc,
+                 const float* ws_m, const float* ws_l, void* out, hipStream_t stream);
 
 int launch_write_kv(const pa_cache_desc_t* c, void* k_cache, void* v_cache, const void* k_new,
                     const void* v_new, const int64_t* slots, int32_t num_tokens,

@@ -20,10 +20,10 @@ namespace {
 // is raised at most once per pair.  The caller has masked V past the
 // visible positions of each tile (a tile with nothing visible: V all zero,
 // row_valid 0).
-template <int RG>
-__device__ __forceinline__ void pair_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&sa)[RG],
-                                                f32x4 (&sb)[RG], const s16x4 (&va)[8],
-                                                const s16x4 (&vb)[8], float scale_log2, int lane,
+template <int RG, int D>
+__device__ __forceinline__ void pair_softmax_pv(SoftmaxStateT<D> (&st)[RG], f32x4 (&sa)[RG],
+                                                f32x4 (&sb)[RG], const s16x4 (&va)[D / 16],
+                                                const s16x4 (&vb)[D / 16], float scale_log2, int lane,
                                                 const int (&rva)[RG], const int (&rvb)[RG],
                                                 bool masked) {
     typedef short s16x8 __attribute__((ext_vector_type(8)));
@@ -82,7 +82,7 @@ __device__ __forceinline__ void pair_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&
             st[u].m = raise[u] ? mx[u] : st[u].m;
             st[u].l *= alpha;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) st[u].acc[j] *= alpha;
+            for (int j = 0; j < D / 16; ++j) st[u].acc[j] *= alpha;
         }
     }
 #pragma unroll
@@ -99,7 +99,7 @@ __device__ __forceinline__ void pair_softmax_pv(SoftmaxState (&st)[RG], f32x4 (&
         st[u].l += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
         const bf16x8 pb = __builtin_bit_cast(bf16x8, pp);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < D / 16; ++j) {
             const s16x8 v = __builtin_shufflevector(va[j], vb[j], 0, 1, 2, 3, 4, 5, 6, 7);
             st[u].acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pb,
                                                                   st[u].acc[j], 0, 0, 0);
@@ -329,7 +329,7 @@ __device__ __forceinline__ int longest_first(const int32_t* __restrict__ context
     return b ? __ffsll(b) - 1 : rank;
 }
 
-template <int RG, int S, int W, int BS>
+template <int RG, int S, int W, int BS, int D>
 __global__ __launch_bounds__(64 * W)
 __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
@@ -339,15 +339,20 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     int tiles_per_seq, int max_blocks_per_seq, int len_clamp, int part_tokens, int max_parts,
     float scale_log2, unsigned q_sign, __bf16* __restrict__ out, float* __restrict__ ws_acc,
     float* __restrict__ ws_m, float* __restrict__ ws_l, int32_t* __restrict__ ws_len) {
-    static_assert(W == 2 || W == 4 || W == 8, "a tile is 8 KiB: 8 / W copies of 1 KiB per wave");
+    static_assert(W == 2 || W == 4 || W == 8, "waves per workgroup");
     static_assert(S % 2 == 0 && S >= 4, "stages hold whole pairs of tiles");
     static_assert(BS == 8 || BS == 16 || BS == 32 || BS == 64,
                   "blocks of half, one, two or four 16-position tiles");
-    constexpr int kCopies = 8 / W;
+    constexpr int TL = FBS * D;                   // elements of a 16-position tile
+    constexpr int KC = D / 32;                    // 16-byte K chunks per lane and tile
+    constexpr int VJ = D / 16;                    // V operands (and accumulators) per lane
+    constexpr int KK = D / 32;                    // KiB of the K half of a tile (a power of 2)
+    static_assert((2 * KK) % W == 0, "each wave copies whole KiB of every tile");
+    constexpr int kCopies = 2 * KK / W;
     constexpr int SUB = BS >= FBS ? BS / FBS : 1;  // tiles per block, back to back in its head region
     // the first block entry of tile t (blocks of 8: a tile is two blocks)
     auto first_entry = [](int t) { return BS == 8 ? 2 * t : t / SUB; };
-    __shared__ __align__(16) __bf16 ring[S][2 * FTILE];   // stage: K tile, then V tile
+    __shared__ __align__(16) __bf16 ring[S][2 * TL];      // stage: K tile, then V tile
     const int h = blockIdx.x;
     const int rank = blockIdx.y / tiles_per_seq;
     // a request's last query tokens see the most positions: they go first
@@ -386,7 +391,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         if (max_parts > 1 && part == 0 && h == 0 && row_ok[u] && row % group == 0 && quad == 0)
             ws_len[qi[u]] = lim[u];
     auto out_row = [&](int u) {
-        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
+        return reinterpret_cast<uint2*>(out + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * D);
     };
     auto zero_rows = [&]() {
 #pragma unroll
@@ -394,7 +399,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             if (part == 0 && row_ok[u] && lim[u] == 0) {
                 uint2* o = out_row(u);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+                for (int jj = 0; jj < VJ; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
             }
     };
     const int tok0 = part * part_tokens;
@@ -404,14 +409,14 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     }
     const int tok1 = min(wg_lim_max, tok0 + part_tokens);
 
-    bf16x8 qv[RG][4];
-    SoftmaxState st[RG];
+    bf16x8 qv[RG][KC];
+    SoftmaxStateT<D> st[RG];
 #pragma unroll
     for (int u = 0; u < RG; ++u) {
         const bf16x8* qp = reinterpret_cast<const bf16x8*>(
-            q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * FD);
+            q + (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * D);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
+        for (int s4 = 0; s4 < KC; ++s4) {
             typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
             const u32x4 v = __builtin_bit_cast(u32x4, qp[4 * s4 + quad]) ^ q_sign;
             qv[u][s4] = row_ok[u] ? __builtin_bit_cast(bf16x8, v) : bf16x8{};
@@ -419,7 +424,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         st[u].m = kNoMaxLog2;
         st[u].l = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < VJ; ++jj) st[u].acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     const int blk0 = tok0 / BS;                  // (partitions are whole blocks)
@@ -452,13 +457,13 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     auto issue_e = [&](int t, int e) {   // tile t of the walk, from block e
         const int64_t o = static_cast<int64_t>(e) * blk_stride +
-                          static_cast<int64_t>(h) * (SUB * FTILE) + static_cast<int64_t>(t % SUB) * FTILE;
-        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
+                          static_cast<int64_t>(h) * (SUB * TL) + static_cast<int64_t>(t % SUB) * TL;
+        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * TL * 2);
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
-            const int kib = wave_u * kCopies + c;          // 0..3 K, 4..7 V
-            const __bf16* base = (kib < 4 ? k_cache : v_cache) + o + (kib & 3) * 512;
-            const unsigned voff = static_cast<unsigned>((kib < 4 ? lane : v_swz_lane) * 16);
+            const int kib = wave_u * kCopies + c;          // K KiB 0..KK-1, then V
+            const __bf16* base = (kib < KK ? k_cache : v_cache) + o + (kib & (KK - 1)) * 512;
+            const unsigned voff = static_cast<unsigned>((kib < KK ? lane : v_swz_lane) * 16);
             lds_copy16_s(base, voff, sb + kib * 1024);
         }
     };
@@ -468,19 +473,19 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     // eb (per block and head, K [D/8][8][8] and V [D][8]); each lane copies
     // the 16 bytes that land at its LDS chunk, from a vector address.
     auto issue_e8 = [&](int t, int ea, int eb) {
-        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * FTILE * 2);
-        const int64_t oa = static_cast<int64_t>(ea) * blk_stride + static_cast<int64_t>(h) * (8 * FD);
-        const int64_t ob = static_cast<int64_t>(eb) * blk_stride + static_cast<int64_t>(h) * (8 * FD);
+        const unsigned sb = ring0 + static_cast<unsigned>((t % S) * 2 * TL * 2);
+        const int64_t oa = static_cast<int64_t>(ea) * blk_stride + static_cast<int64_t>(h) * (8 * D);
+        const int64_t ob = static_cast<int64_t>(eb) * blk_stride + static_cast<int64_t>(h) * (8 * D);
 #pragma unroll
         for (int c = 0; c < kCopies; ++c) {
-            const int kib = wave_u * kCopies + c;          // 0..3 K, 4..7 V
+            const int kib = wave_u * kCopies + c;          // K KiB 0..KK-1, then V
             const __bf16* src;
-            if (kib < 4) {                                 // chunk (dims 8c'..8c'+7, position r)
-                const int C = (kib & 3) * 64 + lane;
+            if (kib < KK) {                                // chunk (dims 8c'..8c'+7, position r)
+                const int C = (kib & (KK - 1)) * 64 + lane;
                 const int cc = C >> 4, r = C & 15;
                 src = k_cache + (r < 8 ? oa : ob) + (cc * 8 + (r & 7)) * 8;
             } else {                                       // chunk (dim d, positions 8*half..)
-                const int G = (kib & 3) * 64 + v_swz_lane;
+                const int G = (kib & (KK - 1)) * 64 + v_swz_lane;
                 src = v_cache + ((G & 1) ? ob : oa) + (G >> 1) * 8;
             }
             lds_copy16(src, __builtin_amdgcn_readfirstlane(sb + kib * 1024));
@@ -516,9 +521,9 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         // the matrix pipe full where one tile's RG chains left it idle
         const bf16x8* kpa = reinterpret_cast<const bf16x8*>(sa) + lane;
         const bf16x8* kpb = reinterpret_cast<const bf16x8*>(sb) + lane;
-        bf16x8 ka[4], kb[4];
+        bf16x8 ka[KC], kb[KC];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
+        for (int s4 = 0; s4 < KC; ++s4) {
             ka[s4] = kpa[64 * s4];
             kb[s4] = kpb[64 * s4];
         }
@@ -528,7 +533,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             s_b[u] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int k = 0; k < KC; ++k)
 #pragma unroll
             for (int u = 0; u < RG; ++u) {
                 s_a[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[k], qv[u][k], s_a[u], 0, 0, 0);
@@ -541,16 +546,16 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         const __bf16* sa = &ring[b % S][0];
         const __bf16* sb = &ring[(b + 1) % S][0];
         const bool has_b = b + 1 < nblk && start + FBS < lim_max;   // (wave-uniform)
-        s16x4 va[8], vb[8];
+        s16x4 va[VJ], vb[VJ];
         const int vo = 2 * ((2 * row + (quad >> 1)) ^ (row >> 3)) + (quad & 1);
-        const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + FTILE) + vo;
-        const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + FTILE) + vo;
+        const s16x4* vpa = reinterpret_cast<const s16x4*>(sa + TL) + vo;
+        const s16x4* vpb = reinterpret_cast<const s16x4*>(sb + TL) + vo;
         // volatile: the reads stay one per 8 bytes, in this order, and the
         // two tiles' pieces of a dim land side by side as one MFMA
         // operand; merged by the compiler into two-address reads of one
         // tile, they cost 24 register copies per pair (184 -> 169 us)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < VJ; ++j) {
             typedef const volatile __attribute__((address_space(3))) s16x4* lds_v;
             va[j] = *(lds_v)(vpa + 64 * j);
             vb[j] = *(lds_v)(vpb + 64 * j);
@@ -561,7 +566,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
         const int vb_valid = has_b ? clampi(lim_max - start - FBS, 0, FBS) : 0;
         if (va_valid < FBS || vb_valid < FBS) {   // (wave-uniform)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < VJ; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (tok_base + i >= va_valid) va[j][i] = 0;
@@ -575,7 +580,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             rva[u] = clampi(lim[u] - start, 0, FBS);
             rvb[u] = has_b ? clampi(lim[u] - start - FBS, 0, FBS) : 0;
         }
-        pair_softmax_pv<RG>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
+        pair_softmax_pv<RG, D>(st, s_a, s_b, va, vb, scale_log2, lane, rva, rvb, masked);
     };
     auto visible = [&](int b) { return tok0 + FBS * b < lim_max; };   // (wave-uniform)
     // Tiles are consumed in pairs (b, b + 1), one barrier per pair; S - 2
@@ -616,7 +621,7 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             if (part == 0 && lim[u] == 0) {
                 uint2* o = out_row(u);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
+                for (int jj = 0; jj < VJ; ++jj) o[4 * jj + quad] = make_uint2(0u, 0u);
             }
             continue;
         }
@@ -625,15 +630,15 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
             const float inv = 1.f / lsum;
             uint2* o = out_row(u);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
+            for (int jj = 0; jj < VJ; ++jj)
                 o[4 * jj + quad] = make_uint2(pack_bf16x2(st[u].acc[jj][0] * inv, st[u].acc[jj][1] * inv),
                                               pack_bf16x2(st[u].acc[jj][2] * inv, st[u].acc[jj][3] * inv));
             continue;
         }
         const int64_t pidx = (static_cast<int64_t>(qi[u]) * num_q_heads + hq) * max_parts + part;
-        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * FD);
+        f32x4* acc_out = reinterpret_cast<f32x4*>(ws_acc + pidx * D);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc_out[4 * jj + quad] = st[u].acc[jj];
+        for (int jj = 0; jj < VJ; ++jj) acc_out[4 * jj + quad] = st[u].acc[jj];
         if (quad == 0) {
             ws_m[pidx] = st[u].m;
             ws_l[pidx] = lsum;
@@ -664,17 +669,20 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
     return check_launch("prefill");
 }
 
-// Longer chunks: two row groups per wave, kPrefillLdsWaves waves per
-// workgroup sharing each tile through LDS.
-template <int BS>
-int launch_prefill_lds_bs(const PrefillArgs& p, float sl2, unsigned q_sign) {
+// Longer chunks: kPrefillLdsWaves waves per workgroup sharing each tile
+// through LDS; two row groups per wave at head_dim 64 and 128, one at 256
+// (where a row group alone holds 64 accumulator registers), with a ring of
+// four stages there (16 KiB a tile).
+template <int BS, int D>
+int launch_prefill_lds_bsd(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
-    constexpr int RG = kPrefillRowGroups;
+    constexpr int RG = D == 256 ? 1 : kPrefillRowGroups;
+    constexpr int S = D == 256 ? 4 : kPrefillStages;
     constexpr int W = kPrefillLdsWaves;
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
-    hipLaunchKernelGGL((prefill_lds_kernel<RG, kPrefillStages, W, BS>), grid, dim3(64 * W), 0, a.stream,
+    hipLaunchKernelGGL((prefill_lds_kernel<RG, S, W, BS, D>), grid, dim3(64 * W), 0, a.stream,
                        static_cast<const __bf16*>(a.k_cache), static_cast<const __bf16*>(a.v_cache),
                        static_cast<const __bf16*>(a.q), p.q_start, a.block_tables, a.context_lens,
                        a.num_blocks, a.block_stride, p.total_q, a.num_q_heads, a.group, tiles,
@@ -684,13 +692,23 @@ int launch_prefill_lds_bs(const PrefillArgs& p, float sl2, unsigned q_sign) {
     return check_launch("prefill");
 }
 
-int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
+template <int D>
+int launch_prefill_lds_d(const PrefillArgs& p, float sl2, unsigned q_sign) {
     switch (p.d.block_size) {
-        case 8: return launch_prefill_lds_bs<8>(p, sl2, q_sign);
-        case 16: return launch_prefill_lds_bs<16>(p, sl2, q_sign);
-        case 32: return launch_prefill_lds_bs<32>(p, sl2, q_sign);
-        case 64: return launch_prefill_lds_bs<64>(p, sl2, q_sign);
+        case 8: return launch_prefill_lds_bsd<8, D>(p, sl2, q_sign);
+        case 16: return launch_prefill_lds_bsd<16, D>(p, sl2, q_sign);
+        case 32: return launch_prefill_lds_bsd<32, D>(p, sl2, q_sign);
+        case 64: return launch_prefill_lds_bsd<64, D>(p, sl2, q_sign);
         default: return fail(PA_ERR_UNSUPPORTED, "prefill: block size %d", p.d.block_size);
+    }
+}
+
+int launch_prefill_lds(const PrefillArgs& p, float sl2, unsigned q_sign) {
+    switch (p.d.head_dim) {
+        case 64: return launch_prefill_lds_d<64>(p, sl2, q_sign);
+        case 128: return launch_prefill_lds_d<128>(p, sl2, q_sign);
+        case 256: return launch_prefill_lds_d<256>(p, sl2, q_sign);
+        default: return fail(PA_ERR_UNSUPPORTED, "prefill: head_dim %d", p.d.head_dim);
     }
 }
 
@@ -709,12 +727,12 @@ int launch_prefill(const PrefillArgs& p) {
     // group 431 us, 2 groups 273 us, 4 groups 368 us -- 332 VGPRs leave one
     // wave per SIMD; staging the tiles in LDS then took it to 217 us)
     const bool lds = p.max_q_len >= 2 * (FG / a.group);
-    if (!lds && a.block_size != FBS)   // (the host runs such calls as decodes)
-        return fail(PA_ERR_UNSUPPORTED, "prefill: short chunks need blocks of 16");
+    if (!lds && (a.block_size != FBS || a.head_dim != FD))   // (the host runs such calls as decodes)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: short chunks need blocks of 16 and head_dim 128");
     const int st = lds ? launch_prefill_lds(p, sl2, q_sign) : launch_prefill_short(p, sl2, q_sign);
     if (st != PA_OK || a.max_parts <= 1 || p.total_q == 0) return st;
-    return launch_merge(p.ws_len, p.total_q, a.num_q_heads, a.len_clamp, a.part_tokens, a.max_parts,
-                        a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
+    return launch_merge(p.ws_len, p.total_q, a.num_q_heads, a.head_dim, a.len_clamp, a.part_tokens,
+                        a.max_parts, a.ws_acc, a.ws_m, a.ws_l, a.out, a.stream);
 }
 
 // ----------------------------------------------------------------------------

@@ -361,14 +361,14 @@ def add_query_chunks(w: Workload, chunk_lens) -> Workload:
 
 def prefill_chunk(seed: int = 5, device="cpu", poison: bool = True, num_seqs: int = 16,
                   cached_lo: int = 1024, cached_hi: int = 3072, chunk: int = 256,
-                  num_blocks: int = 65536) -> Workload:
+                  num_blocks: int = 65536, head_dim: int = 128) -> Workload:
     """Chunked prefill after a prefix-cache hit: ``num_seqs`` requests, each
     with U[cached_lo, cached_hi] cached positions followed by ``chunk`` new
-    ones whose queries attend causally; 32 q / 8 KV heads, D 128, bs 16,
-    bf16, blocks shuffled from the pool."""
+    ones whose queries attend causally; 32 q / 8 KV heads, D ``head_dim``
+    (128 by default), bs 16, bf16, blocks shuffled from the pool."""
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = (rng.integers(cached_lo, cached_hi, size=num_seqs, endpoint=True) + chunk).tolist()
-    w = paged_random("prefill", num_seqs, 0, cached_hi + chunk, 32, 8, seed=seed,
+    w = paged_random("prefill", num_seqs, 0, cached_hi + chunk, 32, 8, head_dim=head_dim, seed=seed,
                      num_blocks=num_blocks, device=device, poison=poison, lens=lens)
     return add_query_chunks(w, [chunk] * num_seqs)
 

@@ -1007,19 +1007,47 @@ def test_prefill_block_sizes(bs, group, part):
     assert_close(w, out, _oracle_prefill(w), f"prefill short bs={bs} g={group}")
 
 
-@pytest.mark.parametrize("bs", [8, 64])
-def test_prefill_block_sizes_long_history(bs):
-    """Blocks of 8 and 64 and a history of more than 256 blocks (the kernel holds
-    the partition's block entries in LDS 256 at a time and refills them)."""
-    say(f"prefill bs={bs} long history")
+@pytest.mark.parametrize("bs,d", [(8, 128), (64, 128), (8, 64), (16, 256)])
+def test_prefill_block_sizes_long_history(bs, d):
+    """Blocks of 8, 16 and 64 and a history of more than 256 blocks (the kernel
+    holds the partition's block entries in LDS 256 at a time and refills them),
+    at head_dim 64, 128 and 256."""
+    say(f"prefill bs={bs} d={d} long history")
     lens = [20011, 300]
-    w = inputs.paged_random("pfbl", len(lens), 0, max(lens), 8, 2, block_size=bs,
+    w = inputs.paged_random("pfbl", len(lens), 0, max(lens), 8, 2, head_dim=d, block_size=bs,
                             num_blocks=20400 // bs + 8, seed=69, device=DEV, lens=lens)
     poison_tails(w)
     inputs.add_query_chunks(w, [40, 17])
     want = _oracle_prefill(w)
     for part in (1 << 15, 4096):
-        assert_close(w, _run_prefill(w, partition_tokens=part), want, f"prefill bs={bs} long part={part}")
+        assert_close(w, _run_prefill(w, partition_tokens=part), want,
+                     f"prefill bs={bs} d={d} long part={part}")
+
+
+@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("bs", [8, 16, 64])
+@pytest.mark.parametrize("group", [1, 4, 16])
+@pytest.mark.parametrize("part", [0, 2])
+def test_prefill_head_dims(d, bs, group, part):
+    """The MFMA prefill at head_dim 64 (two 32-dim score steps, four PV
+    operands per tile) and 256 (eight and sixteen, one row group per wave, a
+    ring of four stages), whole and split histories (split rows merged by the
+    head_dim-generic merge), positions past a request's length poisoned,
+    against the oracle; then a short chunk (per-row decodes)."""
+    say(f"prefill d={d} bs={bs} g={group} part={part}")
+    hkv = 2
+    lens = [1, 15, 16, 17, 40, 100, 0, 77, 33, 250]
+    w = inputs.paged_random("pfd", len(lens), 0, 250, hkv * group, hkv, head_dim=d, block_size=bs,
+                            num_blocks=120, seed=74, device=DEV, lens=lens)
+    poison_tails(w)
+    inputs.add_query_chunks(w, [1, 15, 3, 17, 40, 9, 2, 0, 35, 120])
+    split = part * max(bs, 16)
+    out = _run_prefill(w, partition_tokens=split)
+    assert_close(w, out, _oracle_prefill(w), f"prefill d={d} bs={bs} g={group} part={part}")
+    short = max(1, 2 * 16 // group - 1)
+    inputs.add_query_chunks(w, [min(short, L) for L in lens])
+    out = _run_prefill(w, partition_tokens=split)
+    assert_close(w, out, _oracle_prefill(w), f"prefill short d={d} bs={bs} g={group}")
 
 
 def test_prefill_validate_rejects_bad_offsets(monkeypatch):
@@ -1037,12 +1065,15 @@ def test_prefill_validate_rejects_bad_offsets(monkeypatch):
 
 # Shapes outside the MFMA prefill kernels: each query row runs as a decode
 # request over a copy of its request's table, cut at the positions it sees.
+# The bf16 shapes with Hq/Hkv dividing 16 take that route only for chunks
+# shorter than two row groups of tokens (32 at Hq/Hkv = 1): theirs are cut
+# to 31.
 ROWS_SHAPES = [
     ("f32", 16, 4, 4),       # generic decode kernel
     ("f32", 128, 16, 8),     # fp32 matrix-core decode
-    ("bf16", 64, 8, 8),
-    ("bf16", 256, 16, 4),
-    ("bf16", 128, 32, 8),
+    ("bf16", 64, 8, 2),      # short chunks
+    ("bf16", 256, 16, 2),
+    ("bf16", 128, 32, 2),
     ("bf16", 128, 16, 6),    # Hq/Hkv = 3 does not divide 16
 ]
 
@@ -1052,7 +1083,11 @@ def _rows_workload(dtype, d, bs, hq, seed=71):
     w = inputs.paged_random("pfr", len(lens), 0, 100, hq, 2, head_dim=d, block_size=bs,
                             dtype=dtype, num_blocks=120, seed=seed, device=DEV, lens=lens)
     poison_tails(w)
-    return inputs.add_query_chunks(w, [1, 15, 3, 17, 40, 9, 2, 0, 35])
+    chunks = [1, 15, 3, 17, 40, 9, 2, 0, 35]
+    g = hq // 2
+    if dtype == "bf16" and 16 % g == 0:
+        chunks = [min(c, 2 * 16 // g - 1) for c in chunks]
+    return inputs.add_query_chunks(w, chunks)
 
 
 @pytest.mark.parametrize("dtype,d,bs,hq", ROWS_SHAPES)
