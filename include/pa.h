@@ -416,9 +416,10 @@ int pa_decode_step_noalloc(const pa_cache_desc_t* c, void* k_cache, void* v_cach
  *   max_q_len     >= every n_i (host); sizes the grid
  *   workspace     >= pa_prefill_workspace_bytes(...) bytes
  *   flags         0
- * MFMA prefill kernels: bf16, head_dim 128, Hq/Hkv dividing 16, and block
- * size 16, or 8, 32 or 64 when max_q_len >= 2 * 16 / (Hq/Hkv) (partition_tokens
- * 0 or a multiple of max(16, block_size) up to 2^20).  Every other
+ * MFMA prefill kernels: bf16, head_dim 64, 128 or 256, Hq/Hkv dividing 16,
+ * block size 8, 16, 32 or 64 when max_q_len >= 2 * 16 / (Hq/Hkv), and any
+ * max_q_len at head_dim 128 with blocks of 16 (partition_tokens 0 or a
+ * multiple of max(16, block_size) up to 2^20).  Every other
  * shape pa_decode accepts runs each query row as a decode request: a small
  * kernel gives row r of request i a copy of i's first ceil(max_context_len /
  * block_size) table entries and its visible length L - n_i + j + 1 (clamped

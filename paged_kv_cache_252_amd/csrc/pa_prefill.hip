@@ -41,7 +41,7 @@ __device__ __forceinline__ void pair_softmax_pv(SoftmaxStateT<D> (&st)[RG], f32x
                 if (tok_base + i >= rvb[u]) sb[u][i] = -INFINITY;
             }
         }
-        if constexpr (RG == 2) {   // the lane's maximum; rows combined below for both groups at once
+        if constexpr (RG % 2 == 0) {   // the lane's maximum; rows combined below two groups at once
             float x = vmax3(sa[u][0], sa[u][1], sa[u][2]);
             x = vmax3(sa[u][3], sb[u][0], x);
             x = vmax3(sb[u][1], sb[u][2], x);
@@ -54,21 +54,24 @@ __device__ __forceinline__ void pair_softmax_pv(SoftmaxStateT<D> (&st)[RG], f32x
         raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
         any = any || raise[u];
     }
-    if constexpr (RG == 2) {
-        // Both groups' row maxima with three row swaps instead of four: the
-        // first swaps group 0's odd rows against group 1's even rows, so the
-        // pairwise maximum holds group 0 in rows 0, 2 and group 1 in rows 1,
-        // 3; the second completes each; the third hands every row both.
-        auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[0]), __float_as_uint(mx[1]),
-                                                  false, false);
-        const float m1 = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
-        auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
-                                                  false);
-        const float m2 = vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
-        auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(m2), __float_as_uint(m2), false,
-                                                  false);
-        mx[0] = __uint_as_float(c[0]) * scale_log2;
-        mx[1] = __uint_as_float(c[1]) * scale_log2;
+    if constexpr (RG % 2 == 0) {
+        // Two groups' row maxima with three row swaps instead of four: the
+        // first swaps group u's odd rows against group u + 1's even rows, so
+        // the pairwise maximum holds group u in rows 0, 2 and group u + 1 in
+        // rows 1, 3; the second completes each; the third hands every row both.
+#pragma unroll
+        for (int u = 0; u < RG; u += 2) {
+            auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx[u]), __float_as_uint(mx[u + 1]),
+                                                      false, false);
+            const float m1 = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+            auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(m1), false,
+                                                      false);
+            const float m2 = vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+            auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(m2), __float_as_uint(m2), false,
+                                                      false);
+            mx[u] = __uint_as_float(c[0]) * scale_log2;
+            mx[u + 1] = __uint_as_float(c[1]) * scale_log2;
+        }
 #pragma unroll
         for (int u = 0; u < RG; ++u) {
             raise[u] = mx[u] > st[u].m + kLazyMaxLog2;
@@ -304,9 +307,30 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #ifndef PA_PREFILL_WAVES_PER_SIMD
 #define PA_PREFILL_WAVES_PER_SIMD 1
 #endif
+// The same at head_dim 64 and 256 (tiles of 4 and 16 KiB).
+#ifndef PA_PREFILL_ROW_GROUPS_D64
+#define PA_PREFILL_ROW_GROUPS_D64 2
+#endif
+#ifndef PA_PREFILL_STAGES_D64
+#define PA_PREFILL_STAGES_D64 6
+#endif
+#ifndef PA_PREFILL_ROW_GROUPS_D256
+#define PA_PREFILL_ROW_GROUPS_D256 1
+#endif
+#ifndef PA_PREFILL_STAGES_D256
+#define PA_PREFILL_STAGES_D256 4
+#endif
 constexpr int kPrefillStages = PA_PREFILL_STAGES;
 constexpr int kPrefillLdsWaves = PA_PREFILL_WAVES;
 constexpr int kPrefillRowGroups = PA_PREFILL_ROW_GROUPS;
+template <int D>
+constexpr int prefill_row_groups() {
+    return D == 64 ? PA_PREFILL_ROW_GROUPS_D64 : (D == 256 ? PA_PREFILL_ROW_GROUPS_D256 : kPrefillRowGroups);
+}
+template <int D>
+constexpr int prefill_stages() {
+    return D == 64 ? PA_PREFILL_STAGES_D64 : (D == 256 ? PA_PREFILL_STAGES_D256 : kPrefillStages);
+}
 
 // Workgroups start in grid order, and a request's workgroups run about as
 // long as its history: when the longest requests come last, their
@@ -676,8 +700,8 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
 template <int BS, int D>
 int launch_prefill_lds_bsd(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
-    constexpr int RG = D == 256 ? 1 : kPrefillRowGroups;
-    constexpr int S = D == 256 ? 4 : kPrefillStages;
+    constexpr int RG = prefill_row_groups<D>();
+    constexpr int S = prefill_stages<D>();
     constexpr int W = kPrefillLdsWaves;
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
