@@ -307,18 +307,29 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #ifndef PA_PREFILL_WAVES_PER_SIMD
 #define PA_PREFILL_WAVES_PER_SIMD 1
 #endif
-// The same at head_dim 64 and 256 (tiles of 4 and 16 KiB).
+// The same at head_dim 64 and 256 (tiles of 4 and 16 KiB).  Measured on the
+// chunked-prefill shape at those head dims (us per call): D 64 with six or
+// eight stages 100 alike, four row groups 114; D 256 with one row group,
+// four waves and four stages 348-360, six stages 521, two row groups 373;
+// eight waves (one workgroup per CU) with four, six or eight stages 352-358,
+// 340-347 and 355-359.
 #ifndef PA_PREFILL_ROW_GROUPS_D64
 #define PA_PREFILL_ROW_GROUPS_D64 2
 #endif
 #ifndef PA_PREFILL_STAGES_D64
 #define PA_PREFILL_STAGES_D64 6
 #endif
+#ifndef PA_PREFILL_WAVES_D64
+#define PA_PREFILL_WAVES_D64 4   // (a 4 KiB tile is four 1 KiB copies: at most four waves)
+#endif
 #ifndef PA_PREFILL_ROW_GROUPS_D256
 #define PA_PREFILL_ROW_GROUPS_D256 1
 #endif
 #ifndef PA_PREFILL_STAGES_D256
-#define PA_PREFILL_STAGES_D256 4
+#define PA_PREFILL_STAGES_D256 6
+#endif
+#ifndef PA_PREFILL_WAVES_D256
+#define PA_PREFILL_WAVES_D256 8
 #endif
 constexpr int kPrefillStages = PA_PREFILL_STAGES;
 constexpr int kPrefillLdsWaves = PA_PREFILL_WAVES;
@@ -693,16 +704,16 @@ int launch_prefill_short(const PrefillArgs& p, float sl2, unsigned q_sign) {
     return check_launch("prefill");
 }
 
-// Longer chunks: kPrefillLdsWaves waves per workgroup sharing each tile
-// through LDS; two row groups per wave at head_dim 64 and 128, one at 256
-// (where a row group alone holds 64 accumulator registers), with a ring of
-// four stages there (16 KiB a tile).
+// Longer chunks: waves of a workgroup sharing each tile through LDS; four
+// waves with two row groups each at head_dim 64 and 128; at 256 (where a row
+// group alone holds 64 accumulator registers) eight waves of one row group
+// and a ring of six 16 KiB stages.
 template <int BS, int D>
 int launch_prefill_lds_bsd(const PrefillArgs& p, float sl2, unsigned q_sign) {
     const DecodeArgs& a = p.d;
     constexpr int RG = prefill_row_groups<D>();
     constexpr int S = prefill_stages<D>();
-    constexpr int W = kPrefillLdsWaves;
+    constexpr int W = D == 256 ? PA_PREFILL_WAVES_D256 : (D == 64 ? PA_PREFILL_WAVES_D64 : kPrefillLdsWaves);
     const int per = W * RG * (FG / a.group);
     const int tiles = (p.max_q_len + per - 1) / per;
     dim3 grid(a.num_kv_heads, a.num_seqs * tiles, a.max_parts);
