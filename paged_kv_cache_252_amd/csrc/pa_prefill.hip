@@ -309,7 +309,7 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #endif
 // The same at head_dim 64 and 256 (tiles of 4 and 16 KiB).  Measured on the
 // chunked-prefill shape at those head dims (us per call): D 64 with six or
-// eight stages 100 alike, four row groups 114; D 256 with one row group,
+// eight stages 100 alike, three or four row groups 113-114, two waves 124; D 256 with one row group,
 // four waves and four stages 348-360, six stages 521, two row groups 373;
 // eight waves (one workgroup per CU) with four, six or eight stages 352-358,
 // 340-347 and 355-359.
