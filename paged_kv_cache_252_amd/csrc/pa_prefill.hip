@@ -280,8 +280,9 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 // ---------------------------------------------------------------------------
 // The same work with the tiles staged in LDS: a workgroup of W waves takes
 // W * RG * 16/g consecutive query tokens of one request and KV head; each tile
-// is copied from memory to LDS once per workgroup by the waves together (8 / W
-// KiB each, global_load_lds: no registers on the way), and every wave reads
+// is copied from memory to LDS once per workgroup by the waves together (a
+// tile is 64 * D bytes of K and V, D / 16 / W KiB per wave, global_load_lds:
+// no registers on the way), and every wave reads
 // its MFMA operands from LDS.  Tiles are consumed in pairs (pair_softmax_pv:
 // one PV MFMA of K 32 for both), S - 2 tiles ahead of the pair being
 // consumed.  One barrier per pair: after it, the pair is in LDS and every
@@ -481,8 +482,8 @@ __attribute__((amdgpu_waves_per_eu(PA_PREFILL_WAVES_PER_SIMD))) void prefill_lds
     const unsigned ring0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(
         (__attribute__((address_space(3))) __bf16*)(&ring[0][0])));
     // tile t (past the end: a block of the walk, so every thread issues the
-    // same number of copies per tile) into stage t % S; the stage's 8 KiB are K
-    // then V, and wave w copies KiB w * kCopies .. (w + 1) * kCopies - 1
+    // same number of copies per tile) into stage t % S; the stage's 2 * KK KiB
+    // are K then V, and wave w copies KiB w * kCopies .. (w + 1) * kCopies - 1
     // V stage layout: 16-byte chunk c of the tile sits at chunk c ^ ((c >> 4) & 1)
     // (the two chunks of a dim swap for dims 8..15 of every 16), so the 8-byte
     // reads of rows r and r + 8, 256 bytes apart, fall in different LDS banks.
