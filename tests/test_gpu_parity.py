@@ -1034,7 +1034,7 @@ def test_prefill_block_sizes_long_history(bs, d):
 
 
 @pytest.mark.parametrize("d", [64, 256])
-@pytest.mark.parametrize("bs", [8, 16, 64])
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
 @pytest.mark.parametrize("group", [1, 4, 16])
 @pytest.mark.parametrize("part", [0, 2])
 def test_prefill_head_dims(d, bs, group, part):
