@@ -945,8 +945,9 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_ke
 //     tile is copied from memory to LDS once (2 KiB per wave, global_load_lds,
 //     S - 1 tiles ahead) and every wave consumes it for its 16 rows (16/g
 //     members x g heads).  The other slots exit.
-//   * Otherwise: wave w of slot s decodes member 4 s + w alone, as the fast
-//     path does (one wave per request, KV head and partition).
+//   * Otherwise: wave w of slot s decodes alone the member whose history is
+//     the (4 s + w)-th longest of the chunk, as the fast path does (one wave
+//     per request, KV head and partition).
 // Both kinds of workgroup run in the same launch, so the shared partitions'
 // matrix work proceeds while the private suffixes stream from HBM.  The
 // arithmetic per row is the fast path's (same tiles in the same order, same
@@ -955,12 +956,13 @@ __global__ __launch_bounds__(WGM ? 64 * kMaxWgParts : 64) void decode_grouped_ke
 // position (the member's history extends past it), so the append, when
 // asked for, is always done by the per-member waves.
 constexpr int kCascadeStages = 4;
-// Three waves per SIMD: the append variant would take 172 VGPRs (two waves);
-// held to 168 it spills 24 bytes per lane and runs the shared-prefix step
-// 2-3 % faster.
+// At least two waves per SIMD: the decode-only variant takes 139 VGPRs
+// (three waves), the append variant 176 (two; held to 168 for three, it
+// spilled 24 to 32 bytes per lane: with the members dealt longest first the
+// shared-prefix step measured 81.3-81.4 us that way against 79.1-79.3).
 
 template <bool NT, bool APPEND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_cascade_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_cascade_kernel(
     const __bf16* __restrict__ k_cache, const __bf16* __restrict__ v_cache,
     const __bf16* __restrict__ q, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int64_t num_blocks, int64_t blk_stride,
@@ -1102,9 +1104,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     }
 
     // One member per wave, as the fast path does (one wave per request, KV
-    // head and partition, block size 16; no copy-on-write here).
-    const int m = slot * 4 + wave;
-    if (m >= nmem) return;
+    // head and partition, block size 16; no copy-on-write here).  Members go
+    // to waves longest history first (slot 0 is dispatched first): the
+    // private suffixes differ in length, and the call ends with its longest
+    // walks, so those start first.  (Ties by position in the chunk; the
+    // order depends on the lengths only, and each member's arithmetic is
+    // the same in any wave.)
+    const int m_slot = slot * 4 + wave;
+    if (m_slot >= nmem) return;
+    int m = m_slot;
+    {
+        const int key = lane < nmem ? clampL(context_lens[seq0 + lane]) : -1;   // nmem <= 64
+        int r = 0;
+        for (int t = 0; t < nmem; ++t) {
+            const int kt = __shfl(key, t);
+            r += (kt > key || (kt == key && t < lane)) ? 1 : 0;
+        }
+        const unsigned long long b = __ballot(lane < nmem && r == m_slot);
+        m = b ? __ffsll(b) - 1 : m_slot;
+    }
     const FastArgs fa{k_cache, v_cache, q, block_tables, context_lens, num_blocks, blk_stride,
                       num_q_heads, group, max_blocks_per_seq, len_clamp, part_tokens, max_parts,
                       scale_log2, out, ws_acc, ws_m, ws_l, k_new, v_new, num_kv_heads, nullptr,
