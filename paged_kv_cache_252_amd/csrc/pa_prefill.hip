@@ -291,11 +291,14 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 // LDS stages (an even number), waves per workgroup sharing them, row groups
 // per wave and the occupancy asked of the compiler.  Measured on the
 // chunked-prefill workload (us per call, with the loop at 189 us): 4, 6 or 8
-// stages 189.0-189.2 alike (at 160 us: 160, 161-162, 161-162); 2 waves 249, 8 waves 201; one row group (134 VGPRs,
-// three waves per SIMD, each tile read from LDS for half as many rows) 223,
-// and at four stages held to 128 VGPRs (four waves) 214; three groups 280
-// (one wave per SIMD) or 197 held to 256 VGPRs; four groups 232.  Two groups
-// at 194 VGPRs leave two waves per SIMD; held to 168 (three) they spill.
+// stages 189.0-189.2 alike; 2 waves 249, 8 waves 201; one row group (134
+// VGPRs, three waves per SIMD, each tile read from LDS for half as many rows)
+// 223, and at four stages held to 128 VGPRs (four waves) 214; three groups
+// 280 (one wave per SIMD) or 197 held to 256 VGPRs; four groups 232.  Two
+// groups at 194 VGPRs leave two waves per SIMD; held to 168 (three) they
+// spill.  With the loop at 159-160 us: 4, 6 or 8 stages 160, 161-162,
+// 161-162; 8 waves 165 (171 with 8 stages); three groups held to 256 VGPRs
+// 182.
 #ifndef PA_PREFILL_STAGES
 #define PA_PREFILL_STAGES 6
 #endif
@@ -310,10 +313,10 @@ __global__ __launch_bounds__(64 * W) void prefill_kernel(
 #endif
 // The same at head_dim 64 and 256 (tiles of 4 and 16 KiB).  Measured on the
 // chunked-prefill shape at those head dims (us per call): D 64 with six or
-// eight stages 100 alike, three or four row groups 113-114, two waves 124; D 256 with one row group,
-// four waves and four stages 348-360, six stages 521, two row groups 373;
-// eight waves (one workgroup per CU) with four, six or eight stages 352-358,
-// 340-347 and 355-359.
+// eight stages 100 alike, three or four row groups 113-114, two waves 124;
+// D 256 with one row group, four waves and four stages 348-360, six stages
+// 521, two row groups 373; eight waves (one workgroup per CU) with four, six
+// or eight stages 352-358, 340-347 and 355-359.
 #ifndef PA_PREFILL_ROW_GROUPS_D64
 #define PA_PREFILL_ROW_GROUPS_D64 2
 #endif
