@@ -73,3 +73,24 @@ def test_replicas_same_bytes():
         assert not set(bt[m].tolist()) & set(bt0[m].tolist())
         for a, b in zip(bt0[m], bt[m]):
             assert torch.equal(w.k_cache[a].view(torch.int16), w.k_cache[b].view(torch.int16))
+
+
+def test_prefill_chunk_structure():
+    """The chunked-prefill workload at a small size and each head_dim: every
+    request's last `chunk` positions are its query rows, lengths in
+    [cached_lo + chunk, cached_hi + chunk], tables cover the lengths, and
+    the same seed gives the same lengths and tables at every head_dim."""
+    ws = [inputs.prefill_chunk(num_seqs=5, cached_lo=20, cached_hi=60, chunk=7, num_blocks=64,
+                               head_dim=d) for d in (64, 128, 256)]
+    for w, d in zip(ws, (64, 128, 256)):
+        assert w.head_dim == d and w.num_q_heads == 32 and w.num_kv_heads == 8
+        assert w.q_chunk.shape == (5 * 7, 32, d)
+        assert w.q_start.tolist() == [7 * i for i in range(6)]
+        lens = w.context_lens.numpy()
+        assert ((lens >= 27) & (lens <= 67)).all()
+        bt = w.block_tables.numpy()
+        for i, L in enumerate(lens):
+            nb = (int(L) + w.block_size - 1) // w.block_size
+            assert (bt[i, :nb] >= 0).all()
+        assert torch.equal(w.context_lens, ws[0].context_lens)
+        assert torch.equal(w.block_tables, ws[0].block_tables)
